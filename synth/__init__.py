@@ -1,0 +1,361 @@
+"""Seeded synthetic inputs for the per-layer Flash-dLLM decode step.
+
+This module only draws inputs: random hidden states, weights and cache contents,
+row layouts and block tables.  It holds none of the method's arithmetic, so both
+the GPU library's tests/benchmark and the CPU oracle can take their inputs from
+it without sharing any computation.
+
+Recipe: every stream is ``numpy.random.default_rng([workload_id, layer, stream])``
+with streams 0 X, 1 W, 2 K cache, 3 V cache, 4 window/tracked positions,
+5 block permutation, 6 lengths, 8 draft tokens, 9 agreement, 10 replacement
+tokens, 11 confidences.  Real values are drawn as standard normals in fp32
+(the weight scaled by 0.02 in fp32) and rounded to bf16 by torch's CPU cast.
+The large 32-layer stack draws its tensors on the GPU with torch's seeded
+generator instead (host generation of ~19 G values would take minutes); those
+tensors are copied back to the host when the oracle needs them.
+
+Shapes follow the pages' LLaDA-8B-class decode settings: hidden 4096, 32 heads x
+128, rotary base 500000, paged cache with block size 32.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+STREAM_X, STREAM_W, STREAM_K, STREAM_V, STREAM_POS, STREAM_PERM, STREAM_LEN = 0, 1, 2, 3, 4, 5, 6
+STREAM_DRAFT, STREAM_AGREE, STREAM_REPL, STREAM_CONF = 8, 9, 10, 11
+
+
+def rng(workload_id: int, layer: int, stream: int) -> np.random.Generator:
+    return np.random.default_rng([int(workload_id), int(layer), int(stream)])
+
+
+def to_bf16_bits(a_f32: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns via torch's CPU cast (round to nearest even)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a_f32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def normal_bf16(workload_id, layer, stream, shape, scale=1.0) -> np.ndarray:
+    g = rng(workload_id, layer, stream)
+    a = g.standard_normal(size=shape, dtype=np.float32)
+    if scale != 1.0:
+        a *= np.float32(scale)
+    return to_bf16_bits(a)
+
+
+@dataclasses.dataclass
+class SeqSpec:
+    """Active rows of one sequence.
+
+    Plain sequence: ``window`` = (w0, W) window rows at positions w0..w0+W-1,
+    then ``tracked`` rows (ascending positions); every row's cache slot equals
+    its position.  Two-view sequence (``draft_start`` = d0 set): W draft rows at
+    positions w0+i writing slots d0+i, then W mask rows at positions w0+i
+    writing slots w0+i, then tracked rows.
+    """
+    kv_len: int
+    window: tuple = (0, 0)
+    tracked: tuple = ()
+    draft_start: Optional[int] = None
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    workload_id: int
+    hid: int
+    num_heads: int
+    head_dim: int
+    block_size: int
+    rope_base: float
+    kv_len: np.ndarray        # int32 [batch]
+    cu_rows: np.ndarray       # int32 [batch+1]
+    positions: np.ndarray     # int32 [R]
+    slots: np.ndarray         # int32 [R]
+    block_table: np.ndarray   # int32 [batch, max_blocks]
+    num_blocks: int
+    views: Optional[np.ndarray]  # int32 [batch, 3] or None
+    topb: int                 # 0: no mass / tracking-set selection
+    layers: int = 1
+    x: Optional[np.ndarray] = None        # bf16 bits [R, hid]
+    w: Optional[np.ndarray] = None        # bf16 bits [3HD, hid]
+    k_cache: Optional[np.ndarray] = None  # bf16 bits [num_blocks, H, bs, D]
+    v_cache: Optional[np.ndarray] = None
+    verify: Optional[dict] = None         # draft, mask, conf (fp32), threshold (fp32)
+
+    @property
+    def batch(self) -> int:
+        return len(self.kv_len)
+
+    @property
+    def rows(self) -> int:
+        return int(self.cu_rows[-1])
+
+    @property
+    def max_blocks(self) -> int:
+        return self.block_table.shape[1]
+
+    @property
+    def max_kv_len(self) -> int:
+        return int(self.kv_len.max()) if len(self.kv_len) else 0
+
+
+def layout(workload_id: int, specs, block_size: int, layer: int = 0):
+    """Row arrays, two-view descriptors and a seeded permuted block table."""
+    batch = len(specs)
+    cu = [0]
+    pos, slots = [], []
+    views = np.zeros((batch, 3), np.int32)
+    any_view = False
+    for b, s in enumerate(specs):
+        w0, wl = s.window
+        if s.draft_start is not None:
+            any_view = True
+            views[b] = (w0, wl, s.draft_start)
+            pos += [w0 + i for i in range(wl)]
+            slots += [s.draft_start + i for i in range(wl)]
+            pos += [w0 + i for i in range(wl)]
+            slots += [w0 + i for i in range(wl)]
+        else:
+            pos += [w0 + i for i in range(wl)]
+            slots += [w0 + i for i in range(wl)]
+        tr = sorted(int(t) for t in s.tracked)
+        pos += tr
+        slots += tr
+        cu.append(len(pos))
+    kv_len = np.array([s.kv_len for s in specs], np.int32)
+    nblk = [-(-int(s.kv_len) // block_size) for s in specs]
+    num_blocks = int(sum(nblk))
+    max_blocks = max(nblk + [1])
+    perm = rng(workload_id, layer, STREAM_PERM).permutation(max(num_blocks, 1))
+    bt = np.zeros((batch, max_blocks), np.int32)  # unused entries: 0 (never read)
+    off = 0
+    for b, n in enumerate(nblk):
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    return (kv_len, np.array(cu, np.int32), np.array(pos, np.int32),
+            np.array(slots, np.int32), bt, max(num_blocks, 1),
+            views if any_view else None)
+
+
+def build(name, workload_id, hid, num_heads, head_dim, block_size, rope_base, specs,
+          topb, layer=0, layers=1, materialize=True) -> Workload:
+    kv_len, cu, pos, slots, bt, nb, views = layout(workload_id, specs, block_size, layer)
+    wl = Workload(name, workload_id, hid, num_heads, head_dim, block_size, rope_base,
+                  kv_len, cu, pos, slots, bt, nb, views, topb, layers)
+    if materialize:
+        fill_layer(wl, layer)
+    return wl
+
+
+def fill_layer(wl: Workload, layer: int) -> Workload:
+    """Draw X, W and the two cache pools of one layer on the host."""
+    r, hd = wl.rows, wl.num_heads * wl.head_dim
+    wid = wl.workload_id
+    wl.x = normal_bf16(wid, layer, STREAM_X, (r, wl.hid))
+    wl.w = normal_bf16(wid, layer, STREAM_W, (3 * hd, wl.hid), scale=0.02)
+    shape = (wl.num_blocks, wl.num_heads, wl.block_size, wl.head_dim)
+    wl.k_cache = normal_bf16(wid, layer, STREAM_K, shape)
+    wl.v_cache = normal_bf16(wid, layer, STREAM_V, shape)
+    return wl
+
+
+def distinct(g: np.random.Generator, lo: int, hi: int, n: int):
+    """n distinct integers from [lo, hi), ascending."""
+    n = min(n, hi - lo)
+    return tuple(sorted(int(v) for v in g.choice(np.arange(lo, hi), size=n, replace=False)))
+
+
+# ---------------------------------------------------------------------------
+# The five decode-step workloads
+# ---------------------------------------------------------------------------
+
+
+def tiny_h256(materialize=True) -> Workload:
+    """hidden 256, 4 heads x 64, one sequence, cache 128 (64 prompt + 64
+    generated), window 64..79, 8 tracked from 0..63, base 1e4, top-8."""
+    g = rng(1, 0, STREAM_POS)
+    spec = SeqSpec(kv_len=128, window=(64, 16), tracked=distinct(g, 0, 64, 8))
+    return build("tiny_h256_l128", 1, 256, 4, 64, 32, 1.0e4, [spec], topb=8,
+                 materialize=materialize)
+
+
+def llada8b_b1(materialize=True) -> Workload:
+    """LLaDA-8B-class layer, batch 1: hidden 4096, 32 x 128, cache 768
+    (256 prompt + 512 generated), window 256..287 + 32 tracked from [0, 256),
+    64 active rows, base 5e5; the tracking set (32) is re-selected."""
+    g = rng(2, 0, STREAM_POS)
+    spec = SeqSpec(kv_len=768, window=(256, 32), tracked=distinct(g, 0, 256, 32))
+    return build("llada8b_b1_l768", 2, 4096, 32, 128, 32, 5.0e5, [spec], topb=32,
+                 materialize=materialize)
+
+
+def llada8b_ragged_b32(materialize=True) -> Workload:
+    """Same layer, batch 32, cache lengths U{512..1024}; even sequences in the
+    refresh stage (block-aligned 32-row window), odd ones in the update stage
+    (window at any offset); 32 tracked rows each; top-32 per sequence."""
+    gl = rng(3, 0, STREAM_LEN)
+    gp = rng(3, 0, STREAM_POS)
+    specs = []
+    for b in range(32):
+        length = int(gl.integers(512, 1025))
+        if b % 2 == 0:
+            w0 = 32 * int(gp.integers(1, length // 32))
+        else:
+            w0 = int(gp.integers(32, length - 32 + 1))
+        specs.append(SeqSpec(kv_len=length, window=(w0, 32),
+                             tracked=distinct(gp, 0, w0, 32)))
+    return build("llada8b_ragged_b32", 3, 4096, 32, 128, 32, 5.0e5, specs, topb=32,
+                 materialize=materialize)
+
+
+def verify_scan_inputs(workload_id: int, batch: int, window: int, crafted=True):
+    """Draft tokens, mask-view argmax tokens (about 70 % agreement) and fp32
+    confidences U(0,1) for the accept scan, threshold 0.9f; plus crafted rows
+    that exercise long prefixes, which the random draws almost never do."""
+    v = 1 << 20
+    draft = rng(workload_id, 0, STREAM_DRAFT).integers(0, v, size=(batch, window)).astype(np.int32)
+    agree = rng(workload_id, 0, STREAM_AGREE).random(size=(batch, window)) < 0.7
+    repl = rng(workload_id, 0, STREAM_REPL).integers(0, v - 1, size=(batch, window))
+    mask = np.where(agree, draft, (draft.astype(np.int64) + 1 + repl) % v).astype(np.int32)
+    conf = rng(workload_id, 0, STREAM_CONF).random(size=(batch, window), dtype=np.float32)
+    thr = np.float32(0.9)
+    if crafted:
+        rows_d, rows_m, rows_c = [], [], []
+        base_d = np.arange(window, dtype=np.int32) * 7 + 11
+        hi = np.full(window, 0.95, np.float32)
+        # all accepted
+        rows_d.append(base_d); rows_m.append(base_d.copy()); rows_c.append(hi.copy())
+        # confidence exactly at the threshold at position 5 (strict comparison stops there)
+        c = hi.copy(); c[min(5, window - 1)] = thr
+        rows_d.append(base_d); rows_m.append(base_d.copy()); rows_c.append(c)
+        # first position disagrees
+        m = base_d.copy(); m[0] += 1
+        rows_d.append(base_d); rows_m.append(m); rows_c.append(hi.copy())
+        # disagreement at the last position
+        m = base_d.copy(); m[-1] += 1
+        rows_d.append(base_d); rows_m.append(m); rows_c.append(hi.copy())
+        # the next float above the threshold passes
+        c = hi.copy(); c[:] = np.nextafter(thr, np.float32(1.0))
+        rows_d.append(base_d); rows_m.append(base_d.copy()); rows_c.append(c)
+        # a NaN confidence fails
+        c = hi.copy(); c[min(9, window - 1)] = np.float32(np.nan)
+        rows_d.append(base_d); rows_m.append(base_d.copy()); rows_c.append(c)
+        draft = np.concatenate([draft, np.stack(rows_d)])
+        mask = np.concatenate([mask, np.stack(rows_m)])
+        conf = np.concatenate([conf, np.stack(rows_c)])
+    return dict(draft=np.ascontiguousarray(draft), mask=np.ascontiguousarray(mask),
+                conf=np.ascontiguousarray(conf), threshold=thr)
+
+
+def llada8b_verify_b8(materialize=True) -> Workload:
+    """Two-view verify step: batch 8, context 1024 plus one draft block
+    (33 blocks per sequence), block-aligned window of 32; 32 draft rows and
+    32 mask rows per sequence at the same positions; then the accept scan."""
+    gp = rng(4, 0, STREAM_POS)
+    specs = []
+    for _ in range(8):
+        w0 = 32 * int(gp.integers(1, 32))
+        specs.append(SeqSpec(kv_len=1024 + 32, window=(w0, 32), draft_start=1024))
+    wl = build("llada8b_verify_b8", 4, 4096, 32, 128, 32, 5.0e5, specs, topb=0,
+               materialize=materialize)
+    wl.verify = verify_scan_inputs(4, 8, 32)
+    return wl
+
+
+def llada8b_stack32_layout() -> Workload:
+    """32-layer stack, batch 16, cache 4096 per sequence: window of 32 at
+    w0 ~ U{32..4064} (shared by all layers) + 32 tracked from [0, w0); top-32
+    re-selected per layer.  Tensors are drawn per layer on the GPU
+    (``stack_layer_tensors``)."""
+    gp = rng(5, 0, STREAM_POS)
+    specs = []
+    for _ in range(16):
+        w0 = int(gp.integers(32, 4064 + 1))
+        specs.append(SeqSpec(kv_len=4096, window=(w0, 32), tracked=distinct(gp, 0, w0, 32)))
+    return build("llada8b_stack32_b16_l4096", 5, 4096, 32, 128, 32, 5.0e5, specs, topb=32,
+                 layers=32, materialize=False)
+
+
+def stack_layer_tensors(wl: Workload, layer: int, device):
+    """Draw one layer's X, W, K and V pools as torch bf16 tensors on ``device``
+    with torch's seeded generator (seed = workload*1e6 + layer*100 + stream)."""
+    import torch
+    hd = wl.num_heads * wl.head_dim
+    shapes = {STREAM_X: ((wl.rows, wl.hid), 1.0), STREAM_W: ((3 * hd, wl.hid), 0.02),
+              STREAM_K: ((wl.num_blocks, wl.num_heads, wl.block_size, wl.head_dim), 1.0),
+              STREAM_V: ((wl.num_blocks, wl.num_heads, wl.block_size, wl.head_dim), 1.0)}
+    out = {}
+    for stream, (shape, scale) in shapes.items():
+        g = torch.Generator(device=device)
+        g.manual_seed(wl.workload_id * 1_000_000 + layer * 100 + stream)
+        t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if scale != 1.0:
+            t.mul_(scale)
+        out[stream] = t.to(torch.bfloat16)
+        del t
+    return out[STREAM_X], out[STREAM_W], out[STREAM_K], out[STREAM_V]
+
+
+# ---------------------------------------------------------------------------
+# Small workloads for element-wise parity: several tiles and ragged tails
+# ---------------------------------------------------------------------------
+
+
+def small_ragged(materialize=True) -> Workload:
+    """hidden 512, 4 x 128, batch 5 with lengths that are not multiples of the
+    block size, refresh and update windows, varying tracked counts, top-8."""
+    g = rng(11, 0, STREAM_POS)
+    lens = [200, 77, 33, 160, 96]
+    specs = []
+    for b, length in enumerate(lens):
+        if b % 2 == 0:
+            w0 = 32 * int(g.integers(0, max(1, length // 32)))
+            wl = min(32, length - w0)
+        else:
+            w0 = int(g.integers(0, length - 16 + 1))
+            wl = 16
+        nt = int(g.integers(0, 13))
+        pool = [p for p in range(length) if not (w0 <= p < w0 + wl)]
+        tr = tuple(sorted(int(p) for p in g.choice(pool, size=min(nt, len(pool)), replace=False)))
+        specs.append(SeqSpec(kv_len=length, window=(w0, wl), tracked=tr))
+    return build("small_ragged_b5", 11, 512, 4, 128, 32, 5.0e5, specs, topb=8,
+                 materialize=materialize)
+
+
+def small_verify(materialize=True) -> Workload:
+    """Two-view step at small size: hidden 256, 2 x 64, batch 3, contexts of
+    different lengths, windows of 16 at block- and non-block-aligned offsets."""
+    specs = [SeqSpec(kv_len=96 + 16, window=(32, 16), draft_start=96),
+             SeqSpec(kv_len=150 + 16, window=(70, 16), draft_start=150),
+             SeqSpec(kv_len=64 + 16, window=(0, 16), draft_start=64)]
+    wl = build("small_verify_b3", 12, 256, 2, 64, 32, 1.0e4, specs, topb=8,
+               materialize=materialize)
+    wl.verify = verify_scan_inputs(12, 3, 16)
+    return wl
+
+
+def small_d64_many_rows(materialize=True) -> Workload:
+    """head_dim 64, batch 2, one sequence with 150 active rows (more than one row
+    tile) and a long cache, one with 1 row; hidden 384."""
+    g = rng(13, 0, STREAM_POS)
+    specs = [SeqSpec(kv_len=300, window=(100, 64), tracked=distinct(g, 0, 100, 86)),
+             SeqSpec(kv_len=45, window=(44, 1))]
+    return build("small_d64_rows150", 13, 384, 6, 64, 32, 1.0e4, specs, topb=16,
+                 materialize=materialize)
+
+
+WORKLOADS = {
+    "tiny_h256_l128": tiny_h256,
+    "llada8b_b1_l768": llada8b_b1,
+    "llada8b_ragged_b32": llada8b_ragged_b32,
+    "llada8b_verify_b8": llada8b_verify_b8,
+    "small_ragged_b5": small_ragged,
+    "small_verify_b3": small_verify,
+    "small_d64_rows150": small_d64_many_rows,
+}

@@ -1,0 +1,377 @@
+"""Pins of the CPU oracle: checks against closed forms, invariants, hand-worked
+fixtures and brute force.  Each pin returns None or raises AssertionError, so the
+mutation test can plant a mistake in the oracle and show that some pin fails.
+
+Page key: [P4] "Flash-dLLM: I/O-Aware KV Caching and Parallel Decoding for Fast,
+Memory-Efficient Diffusion LLMs" (ai4snews.wisdomeyes.cn summary), paragraphs 1-5.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def bits(x):
+    """Exact fp64 -> bf16 bits for values known to be representable (test helper)."""
+    b = (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(O.bf16_bits_to_f64(b), np.asarray(x, np.float64)), "not bf16-exact"
+    return b
+
+
+# --- bf16 codec -------------------------------------------------------------
+
+def pin_bf16_midpoints():
+    """Round-to-nearest-even at exact halfway points (storage format of the cache)."""
+    one = 1.0
+    cases = {one + 2.0 ** -8: 1.0,                      # halfway, even neighbour below
+             one + 3 * 2.0 ** -8: one + 2.0 ** -6,      # halfway, even neighbour above
+             one + 2.0 ** -8 + 2.0 ** -30: one + 2.0 ** -7,  # just above halfway
+             -(one + 2.0 ** -8): -1.0,
+             0.0: 0.0,
+             3.0: 3.0}
+    for x, want in cases.items():
+        got = O.bf16_bits_to_f64(O.f64_to_bf16_bits(np.array([x])))[0]
+        assert got == want, (x, got, want)
+    big = O.f64_to_bf16_bits(np.array([3.5e38, -3.5e38]))
+    assert np.all(np.isinf(O.bf16_bits_to_f64(big)))
+
+
+def pin_bf16_vs_torch(n=20000, seed=0):
+    """fp32 inputs: direct fp64->bf16 rounding equals torch's fp32->bf16 cast (RNE)."""
+    import torch
+    g = np.random.default_rng(seed)
+    a = np.concatenate([g.standard_normal(n).astype(np.float32) * np.float32(10.0) ** g.integers(-30, 30, n).astype(np.float32),
+                        np.array([1e-40, -1e-40, 1.1754944e-38, 3.3e38, 0.0, -0.0, 1.0], np.float32)])
+    a = a[np.isfinite(a)]
+    want = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = O.f64_to_bf16_bits(a.astype(np.float64))
+    assert np.array_equal(got, want), np.flatnonzero(got != want)[:5]
+
+
+# --- QKV projection ---------------------------------------------------------
+
+def pin_gemm_integer_exact(seed=1):
+    """Small-integer inputs: the product is exact; compare with a Python-int triple loop."""
+    g = np.random.default_rng(seed)
+    r, hid, n = 5, 12, 9
+    xi = g.integers(-2, 3, (r, hid))
+    wi = g.integers(-2, 3, (n, hid))
+    y = O.qkv_projection(bits(xi.astype(np.float64)), bits(wi.astype(np.float64)))
+    for i in range(r):
+        for j in range(n):
+            acc = 0
+            for k in range(hid):
+                acc += int(xi[i, k]) * int(wi[j, k])
+            assert y[i, j] == acc, (i, j, y[i, j], acc)
+
+
+# --- rotary embedding --------------------------------------------------------
+
+def pin_rope_closed_form():
+    """D=4, base b: e0 at position p -> (cos p, 0, sin p, 0) and
+    e1 -> (0, cos(p b^-1/2), 0, sin(p b^-1/2)) (half-split pairs; an interleaved
+    convention would give (cos p, sin p, 0, 0))."""
+    base = 10000.0
+    for p in (0, 1, 7, 1000):
+        e = np.zeros((2, 1, 4))
+        e[0, 0, 0] = 1.0
+        e[1, 0, 1] = 1.0
+        out = O.rope_rotate(e, np.array([p, p]), base)
+        a1 = p * base ** -0.5
+        assert np.allclose(out[0, 0], [math.cos(p), 0, math.sin(p), 0], atol=1e-12), out[0, 0]
+        assert np.allclose(out[1, 0], [0, math.cos(a1), 0, math.sin(a1)], atol=1e-12), out[1, 0]
+
+
+def pin_rope_invariants(seed=2):
+    """Per-pair norms preserved; <R_m q, R_n k> depends only on m - n; p = 0 is the identity."""
+    g = np.random.default_rng(seed)
+    d = 128
+    q = g.standard_normal((1, 1, d))
+    k = g.standard_normal((1, 1, d))
+    for base in (1e4, 5e5):
+        r = O.rope_rotate(q, np.array([3]), base)
+        half = d // 2
+        n0 = q[..., :half] ** 2 + q[..., half:] ** 2
+        n1 = r[..., :half] ** 2 + r[..., half:] ** 2
+        assert np.allclose(n0, n1, rtol=1e-12, atol=1e-12)
+        m, n = 37, 5
+        ref = np.sum(O.rope_rotate(q, np.array([m]), base) * O.rope_rotate(k, np.array([n]), base))
+        for t in (1, 100, 3000):
+            sh = np.sum(O.rope_rotate(q, np.array([m + t]), base) * O.rope_rotate(k, np.array([n + t]), base))
+            assert abs(sh - ref) < 1e-9 * (1 + abs(ref)), (t, sh, ref)
+        assert np.array_equal(O.rope_rotate(q, np.array([0]), base), q)
+
+
+# --- cache write ---------------------------------------------------------------
+
+def pin_slot_map_hand():
+    gd = golden("slot_map.json")
+    ps = O.physical_slots(np.array(gd["cu_rows"]), np.array(gd["slots"]),
+                          np.array(gd["block_table"]), gd["block_size"])
+    assert list(ps) == gd["expect_physical"], ps
+
+
+def _tiny_step(seed, h=2, d=8, hid=16, bs=4, lens=(10, 7), perm=None, rows=None):
+    g = np.random.default_rng(seed)
+    nblk = [-(-L // bs) for L in lens]
+    nb = sum(nblk)
+    perm = np.arange(nb) if perm is None else np.asarray(perm)
+    bt = np.zeros((len(lens), max(nblk)), np.int32)
+    off = 0
+    for b, n in enumerate(nblk):
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    rows = rows or [[2, 3, 0], [6]]
+    cu = np.cumsum([0] + [len(r) for r in rows]).astype(np.int32)
+    slots = np.array([s for r in rows for s in r], np.int32)
+    pos = slots.copy()
+    x = bits(np.round(g.standard_normal((len(slots), hid)) * 4) / 4)
+    w = bits(np.round(g.standard_normal((3 * h * d, hid)) * 8) / 64)
+    kc = bits(np.round(g.standard_normal((nb, h, bs, d)) * 4) / 4)
+    vc = bits(np.round(g.standard_normal((nb, h, bs, d)) * 4) / 4)
+    return dict(x=x, w=w, h=h, d=d, pos=pos, cu=cu, slots=slots, bt=bt, bs=bs, kc=kc, vc=vc,
+                kv_len=np.array(lens, np.int32))
+
+
+def pin_cache_write_invariants():
+    """Only the active slots change; written V equals the unrotated projection
+    rounded to bf16; logical results do not depend on the physical block order."""
+    t = _tiny_step(3)
+    q, kc, vc, ps = O.flash_cache_step(t["x"], t["w"], t["h"], t["d"], t["pos"], 1e4, t["cu"],
+                                       t["slots"], t["bt"], t["bs"], t["kc"], t["vc"])
+    hd = t["h"] * t["d"]
+    flat_old = t["kc"].transpose(0, 2, 1, 3).reshape(-1, hd)
+    flat_new = kc.transpose(0, 2, 1, 3).reshape(-1, hd)
+    untouched = np.setdiff1d(np.arange(flat_old.shape[0]), ps)
+    assert np.array_equal(flat_old[untouched], flat_new[untouched])
+    vflat = vc.transpose(0, 2, 1, 3).reshape(-1, hd)
+    y = O.bf16_bits_to_f64(t["x"]) @ O.bf16_bits_to_f64(t["w"]).T
+    assert np.array_equal(vflat[ps], O.f64_to_bf16_bits(y[:, 2 * hd:]))  # V is stored unrotated
+    kflat = flat_new[ps]
+    moved = t["pos"] != 0
+    assert not np.array_equal(kflat[moved], O.f64_to_bf16_bits(y[moved, hd:2 * hd]))  # K is rotated
+    # block permutation invariance of everything logical
+    t2 = _tiny_step(3, perm=[4, 2, 0, 3, 1])
+    blocks_old = t["bt"]
+    kc2 = np.zeros_like(t2["kc"])
+    vc2 = np.zeros_like(t2["vc"])
+    for b in range(2):
+        for i in range(-(-int(t["kv_len"][b]) // t["bs"])):
+            kc2[t2["bt"][b, i]] = t["kc"][blocks_old[b, i]]
+            vc2[t2["bt"][b, i]] = t["vc"][blocks_old[b, i]]
+    r1 = O.decode_step(t["x"], t["w"], t["h"], t["d"], t["pos"], 1e4, t["cu"], t["slots"], t["bt"],
+                       t["bs"], t["kc"], t["vc"], t["kv_len"], topb=3)
+    r2 = O.decode_step(t["x"], t["w"], t["h"], t["d"], t["pos"], 1e4, t["cu"], t["slots"], t2["bt"],
+                       t["bs"], kc2, vc2, t["kv_len"], topb=3)
+    assert np.array_equal(r1["out"], r2["out"]) and np.array_equal(r1["topb"], r2["topb"])
+    assert np.array_equal(r1["mass"], r2["mass"]) and np.array_equal(r1["q"], r2["q"])
+
+
+# --- attention -------------------------------------------------------------------
+
+def _one_seq_cache(kmat, vmat, bs=4):
+    """Pack [L, D] keys/values of one head into a 1-head paged cache with identity table."""
+    L, d = kmat.shape
+    nb = -(-L // bs)
+    kc = np.zeros((nb, 1, bs, d), np.uint16)
+    vc = np.zeros((nb, 1, bs, d), np.uint16)
+    kp = np.zeros((nb * bs, d))
+    vp = np.zeros((nb * bs, d))
+    kp[:L] = kmat
+    vp[:L] = vmat
+    kc[:, 0] = bits(kp).reshape(nb, bs, d)
+    vc[:, 0] = bits(vp).reshape(nb, bs, d)
+    return kc, vc, np.arange(nb, dtype=np.int32)[None]
+
+
+def pin_attention_closed_forms(seed=4):
+    g = np.random.default_rng(seed)
+    d, L = 4, 7
+    kmat = np.round(g.standard_normal((L, d)) * 8) / 8
+    vmat = np.round(g.standard_normal((L, d)) * 8) / 8
+    kc, vc, bt = _one_seq_cache(kmat, vmat)
+    # q = 0: uniform weights -> O = mean of V
+    q = np.zeros((1, 1, d), np.uint16)
+    o = O.attention(q, kc, vc, bt, 4, np.array([0, 1]), np.array([L]))
+    assert np.allclose(o[0, 0], vmat.mean(0), atol=1e-15)
+    # single visible key -> O = v_0
+    o = O.attention(bits(np.ones((1, 1, d))), kc, vc, bt, 4, np.array([0, 1]), np.array([1]))
+    assert np.array_equal(o[0, 0], vmat[0])
+    # two keys whose scaled scores differ by ln 3 -> weights 3/4 and 1/4
+    s = math.log(3.0)
+    k2 = np.zeros((2, d))
+    k2[0, 0] = 1.0
+    v2 = np.zeros((2, d))
+    v2[0, 1] = 1.0
+    v2[1, 2] = 1.0
+    kc2, vc2, bt2 = _one_seq_cache(k2, v2)
+    qv = np.zeros((1, 1, d))
+    qv[0, 0, 0] = 2.0  # q.k0 = 2, q.k1 = 0; scale = s/2 makes the gap ln 3
+    o = O.attention(bits(qv), kc2, vc2, bt2, 4, np.array([0, 1]), np.array([2]), scale=s / 2)
+    assert abs(o[0, 0, 1] - 0.75) < 1e-14 and abs(o[0, 0, 2] - 0.25) < 1e-14, o
+    # default scale is 1/sqrt(D): q.k gap of ln(3)*sqrt(D) gives 3/4 too
+    qd = np.zeros((1, 1, d))
+    qd[0, 0, 0] = 2.0
+    o = O.attention(bits(qd), kc2, vc2, bt2, 4, np.array([0, 1]), np.array([2]))
+    w0 = 1.0 / (1.0 + math.exp(-2.0 / math.sqrt(d)))
+    assert abs(o[0, 0, 1] - w0) < 1e-14, (o, w0)
+
+
+def pin_softmax_rows_sum_to_one(seed=5):
+    t = _tiny_step(seed)
+    q, kc, vc, _ = O.flash_cache_step(t["x"], t["w"], t["h"], t["d"], t["pos"], 1e4, t["cu"],
+                                      t["slots"], t["bt"], t["bs"], t["kc"], t["vc"])
+    _, probs = O.attention(q, kc, vc, t["bt"], t["bs"], t["cu"], t["kv_len"], want_probs=True)
+    for p in probs:
+        assert np.allclose(p.sum(-1), 1.0, rtol=0, atol=1e-12)
+        assert np.all(p >= 0)
+
+
+def pin_attention_brute_force(seed=6):
+    """Pure-Python loops over an explicit mask matrix on a tiny two-view case."""
+    g = np.random.default_rng(seed)
+    d, h, bs = 4, 2, 4
+    view = (1, 2, 4)
+    L = 6
+    nb = 2
+    kc = bits(np.round(g.standard_normal((nb, h, bs, d)) * 4) / 4)
+    vc = bits(np.round(g.standard_normal((nb, h, bs, d)) * 4) / 4)
+    bt = np.array([[1, 0]], np.int32)
+    q = bits(np.round(g.standard_normal((4, h, d)) * 4) / 4)
+    o = O.attention(q, kc, vc, bt, bs, np.array([0, 4]), np.array([L]), views=np.array([view]))
+    vis = golden("two_view_mask.json")["expect"]
+    qf, kf, vf = (O.bf16_bits_to_f64(a) for a in (q, kc, vc))
+    for hh in range(h):
+        for r in range(4):
+            sc, vals = [], []
+            for j in range(L):
+                if not vis[r][j]:
+                    continue
+                blk, off = int(bt[0, j // bs]), j % bs
+                sc.append(sum(qf[r, hh, c] * kf[blk, hh, off, c] for c in range(d)) / math.sqrt(d))
+                vals.append([vf[blk, hh, off, c] for c in range(d)])
+            mx = max(sc)
+            ws = [math.exp(s - mx) for s in sc]
+            z = sum(ws)
+            want = [sum(ws[i] * vals[i][c] for i in range(len(ws))) / z for c in range(d)]
+            assert np.allclose(o[r, hh], want, rtol=1e-12, atol=1e-12), (hh, r)
+
+
+def pin_two_view_mask_hand():
+    gd = golden("two_view_mask.json")
+    vis = O.visibility_mask(gd["rows"], gd["kv_len"], gd["view"])
+    assert np.array_equal(vis.astype(int), np.array(gd["expect"])), vis.astype(int)
+
+
+def pin_two_view_closed_forms(seed=7):
+    """q = 0: draft row i -> (sum_ctx v + sum_{i'<=i} v_draft)/(|ctx|+i+1);
+    mask row i -> (sum_ctx v + sum_window v)/(|ctx|+W).  Perturbing one view's
+    keys/values leaves the other view's outputs bit-identical; perturbing draft
+    key j leaves draft rows i < j bit-identical."""
+    g = np.random.default_rng(seed)
+    d, w0, wl, d0 = 4, 3, 3, 8
+    L = d0 + wl
+    vmat = np.round(g.standard_normal((L, d)) * 8) / 8
+    kmat = np.round(g.standard_normal((L, d)) * 8) / 8
+    kc, vc, bt = _one_seq_cache(kmat, vmat)
+    view = np.array([[w0, wl, d0]])
+    cu = np.array([0, 2 * wl])
+    q0 = np.zeros((2 * wl, 1, d), np.uint16)
+    o = O.attention(q0, kc, vc, bt, 4, cu, np.array([L]), views=view)
+    ctx = [j for j in range(d0) if not (w0 <= j < w0 + wl)]
+    for i in range(wl):
+        want = (vmat[ctx].sum(0) + vmat[d0:d0 + i + 1].sum(0)) / (len(ctx) + i + 1)
+        assert np.allclose(o[i, 0], want, atol=1e-14), i
+        want = (vmat[ctx].sum(0) + vmat[w0:w0 + wl].sum(0)) / (len(ctx) + wl)
+        assert np.allclose(o[wl + i, 0], want, atol=1e-14), i
+    q = bits(np.round(g.standard_normal((2 * wl, 1, d)) * 4) / 4)
+    base = O.attention(q, kc, vc, bt, 4, cu, np.array([L]), views=view)
+    k2, v2 = kmat.copy(), vmat.copy()
+    k2[d0:] += 1.0
+    v2[d0:] -= 2.0
+    kcp, vcp, _ = _one_seq_cache(k2, v2)
+    pert = O.attention(q, kcp, vcp, bt, 4, cu, np.array([L]), views=view)
+    assert np.array_equal(pert[wl:], base[wl:])       # mask view blind to draft keys
+    assert not np.array_equal(pert[:wl], base[:wl])
+    k3, v3 = kmat.copy(), vmat.copy()
+    k3[w0:w0 + wl] += 1.0
+    v3[w0:w0 + wl] -= 2.0
+    kcp, vcp, _ = _one_seq_cache(k3, v3)
+    pert = O.attention(q, kcp, vcp, bt, 4, cu, np.array([L]), views=view)
+    assert np.array_equal(pert[:wl], base[:wl])       # draft view blind to window (mask-view) keys
+    k4, v4 = kmat.copy(), vmat.copy()
+    k4[d0 + 2] += 1.0
+    v4[d0 + 2] -= 2.0
+    kcp, vcp, _ = _one_seq_cache(k4, v4)
+    pert = O.attention(q, kcp, vcp, bt, 4, cu, np.array([L]), views=view)
+    assert np.array_equal(pert[:2], base[:2])         # causal inside the draft view
+    assert not np.array_equal(pert[2], base[2])
+
+
+# --- attention mass and top-B -----------------------------------------------
+
+def pin_mass_sum_and_uniform(seed=8):
+    """sum_j m_b[j] = H * R_b; with q = 0 every visible key has equal mass, so the
+    tie rule makes top-B = {0..B-1}."""
+    t = _tiny_step(seed, h=3)
+    q, kc, vc, _ = O.flash_cache_step(t["x"], t["w"], t["h"], t["d"], t["pos"], 1e4, t["cu"],
+                                      t["slots"], t["bt"], t["bs"], t["kc"], t["vc"])
+    _, probs = O.attention(q, kc, vc, t["bt"], t["bs"], t["cu"], t["kv_len"], want_probs=True)
+    mass = O.attention_mass(probs)
+    for b in range(2):
+        rb = t["cu"][b + 1] - t["cu"][b]
+        assert abs(mass[b].sum() - 3 * rb) < 1e-12 * 3 * rb
+    q0 = np.zeros_like(q)
+    _, probs = O.attention(q0, kc, vc, t["bt"], t["bs"], t["cu"], t["kv_len"], want_probs=True)
+    mass = O.attention_mass(probs)
+    for b in range(2):
+        L = int(t["kv_len"][b])
+        assert np.all(mass[b, :L] == mass[b, 0])
+        assert list(O.top_b(mass[b], L, 4)) == [0, 1, 2, 3]
+
+
+def pin_top_b_crafted():
+    m = np.array([0.5, 2.0, 2.0, 0.1, 3.0, 2.0, 0.0])
+    assert list(O.top_b(m, 7, 3)) == [1, 2, 4]          # ties at 2.0 -> lower indices win
+    assert list(O.top_b(m, 7, 1)) == [4]
+    assert list(O.top_b(m, 7, 7)) == [0, 1, 2, 3, 4, 5, 6]
+    assert list(O.top_b(m, 3, 5)) == [0, 1, 2, -1, -1]   # kv_len < B pads with -1
+    assert list(O.top_b(m, 6, 4)) == [1, 2, 4, 5]
+    assert list(O.top_b(np.array([1.0, 0.0, 5.0]), 2, 1)) == [0]  # keys past kv_len never count
+    assert list(O.top_b(np.zeros(5), 5, 2)) == [0, 1]
+
+
+def pin_top_b_brute(seed=9):
+    g = np.random.default_rng(seed)
+    for _ in range(50):
+        n = int(g.integers(1, 40))
+        b = int(g.integers(1, 12))
+        m = g.integers(0, 5, n).astype(np.float64) / 4  # many ties
+        best = sorted(range(n), key=lambda j: (-m[j], j))[:b]
+        want = sorted(best) + [-1] * (b - len(best))
+        assert list(O.top_b(m, n, b)) == want
+
+
+# --- accept scan -----------------------------------------------------------------
+
+def pin_accept_hand():
+    gd = golden("accept_hand.json")
+    thr = np.float32(gd["threshold"])
+    for c in gd["cases"]:
+        conf = [thr if v == "0.9f" else np.float32(v) for v in c["conf"]]
+        got = O.accept_length(c["draft"], c["mask"], conf, thr)
+        assert got == c["expect"], (c, got)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,160 @@
+"""Plant plausible mistakes in the CPU oracle and check that at least one pin
+catches each.  The mistakes live only in this process (monkeypatched), on the CPU."""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.reference as R
+from tests import pins
+
+_orig = {name: getattr(R, name) for name in dir(R) if callable(getattr(R, name))}
+
+
+def _truncating_bf16(x):
+    x = np.asarray(x, dtype=np.float64)
+    return (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _gemm_dropped_term(x_bits, w_bits):
+    x = R.bf16_bits_to_f64(x_bits)
+    w = R.bf16_bits_to_f64(w_bits)
+    return x[:, :-1] @ w[:, :-1].T
+
+
+def _rope_variant(kind):
+    def rope(x, positions, base):
+        x = np.asarray(x, dtype=np.float64)
+        d = x.shape[-1]
+        half = d // 2
+        i = np.arange(half, dtype=np.float64)
+        theta = float(base) ** ((-1.0 if kind == "theta" else -2.0) * i / d)
+        ang = np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]
+        c = np.cos(ang)[:, None, :]
+        s = np.sin(ang)[:, None, :]
+        if kind == "interleaved":
+            x1, x2 = x[..., 0::2], x[..., 1::2]
+            out = np.empty_like(x)
+            out[..., 0::2] = x1 * c - x2 * s
+            out[..., 1::2] = x2 * c + x1 * s
+            return out
+        x1, x2 = x[..., :half], x[..., half:]
+        sign = -1.0 if kind == "sign" else 1.0
+        return np.concatenate([x1 * c - sign * x2 * s, x2 * c + sign * x1 * s], axis=-1)
+    return rope
+
+
+def _slots_wrong_offset(cu_rows, slots, block_table, block_size):
+    seq = R.row_sequence(cu_rows)
+    s = np.asarray(slots, dtype=np.int64)
+    bt = np.asarray(block_table, dtype=np.int64)
+    return bt[seq, s // block_size] * block_size + s // block_size
+
+
+def _attention_no_scale(*a, **k):
+    k["scale"] = 1.0 if k.get("scale") is None else k["scale"]
+    return _orig["attention"](*a, **k)
+
+
+def _vis_variant(kind):
+    def vis(n_rows, kv_len, view=None):
+        m = _orig["visibility_mask"](n_rows, kv_len, view)
+        if view is None or int(view[1]) == 0:
+            return m
+        w0, wl, d0 = (int(v) for v in view)
+        j = np.arange(kv_len)
+        for t in range(min(wl, n_rows)):
+            if kind == "leak":
+                m[t] |= (j >= w0) & (j < w0 + wl)
+            elif kind == "noncausal":
+                m[t] |= (j >= d0) & (j < d0 + wl)
+        return m
+    return vis
+
+
+def _mass_mean(probs, mass_stride=None):
+    m = _orig["attention_mass"](probs, mass_stride)
+    for b, p in enumerate(probs):
+        if p.shape[1]:
+            m[b] /= p.shape[0] * p.shape[1]
+    return m
+
+
+def _topb_variant(kind):
+    def topb(mass_row, kv_len, b):
+        n = int(kv_len)
+        m = np.asarray(mass_row, dtype=np.float64)[:n]
+        idx = np.arange(n)
+        if kind == "hi_ties":
+            order = np.lexsort((-idx, -m))
+            chosen = np.sort(order[:b])
+        else:  # kept in mass order
+            order = np.lexsort((idx, -m))
+            chosen = order[:b]
+        out = np.full(b, -1, dtype=np.int32)
+        out[:len(chosen)] = chosen
+        return out
+    return topb
+
+
+def _accept_variant(kind):
+    def acc(draft, mask, conf, thr):
+        if kind == "ge":
+            k = 0
+            while k < len(draft) and int(draft[k]) == int(mask[k]) and float(conf[k]) >= float(thr):
+                k += 1
+            return k
+        return sum(1 for k in range(len(draft))
+                   if int(draft[k]) == int(mask[k]) and float(conf[k]) > float(thr))
+    return acc
+
+
+def _fcs_rotating_v(x_bits, w_bits, num_heads, head_dim, positions, rope_base, cu_rows, slots,
+                    block_table, block_size, k_cache_bits, v_cache_bits):
+    h, d = int(num_heads), int(head_dim)
+    hd = h * d
+    y = R.qkv_projection(x_bits, w_bits)
+    r = y.shape[0]
+    q = R.rope_rotate(y[:, :hd].reshape(r, h, d), positions, rope_base)
+    k = R.rope_rotate(y[:, hd:2 * hd].reshape(r, h, d), positions, rope_base)
+    v = R.rope_rotate(y[:, 2 * hd:].reshape(r, h, d), positions, rope_base)
+    ps = R.physical_slots(cu_rows, slots, block_table, block_size)
+    kc = np.array(k_cache_bits, copy=True)
+    vc = np.array(v_cache_bits, copy=True)
+    kc[ps // block_size, :, ps % block_size, :] = R.f64_to_bf16_bits(k)
+    vc[ps // block_size, :, ps % block_size, :] = R.f64_to_bf16_bits(v)
+    return R.f64_to_bf16_bits(q), kc, vc, ps
+
+
+MUTANTS = {
+    "bf16_truncates": ("f64_to_bf16_bits", _truncating_bf16),
+    "gemm_drops_term": ("qkv_projection", _gemm_dropped_term),
+    "rope_sign": ("rope_rotate", _rope_variant("sign")),
+    "rope_interleaved": ("rope_rotate", _rope_variant("interleaved")),
+    "rope_theta": ("rope_rotate", _rope_variant("theta")),
+    "slot_offset": ("physical_slots", _slots_wrong_offset),
+    "attention_unscaled": ("attention", _attention_no_scale),
+    "view_leak": ("visibility_mask", _vis_variant("leak")),
+    "view_noncausal": ("visibility_mask", _vis_variant("noncausal")),
+    "mass_mean": ("attention_mass", _mass_mean),
+    "topb_high_ties": ("top_b", _topb_variant("hi_ties")),
+    "topb_mass_order": ("top_b", _topb_variant("order")),
+    "accept_ge": ("accept_length", _accept_variant("ge")),
+    "accept_no_stop": ("accept_length", _accept_variant("nostop")),
+    "v_rotated": ("flash_cache_step", _fcs_rotating_v),
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_some_pin_catches(mutant, monkeypatch):
+    name, fn = MUTANTS[mutant]
+    monkeypatch.setattr(R, name, fn)
+    if hasattr(oracle, name):
+        monkeypatch.setattr(oracle, name, fn)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutant {mutant}"
