@@ -1,0 +1,174 @@
+/*
+ * fdllm.h -- C ABI of the MI355X (gfx950) library for the per-layer hot path of
+ * one Flash-dLLM decoding step.
+ *
+ * Pages cited (public summaries of one preprint):
+ *   [P4] "Flash-dLLM: I/O-Aware KV Caching and Parallel Decoding for Fast,
+ *        Memory-Efficient Diffusion LLMs", ai4snews.wisdomeyes.cn summary,
+ *        paragraphs 1-5.
+ *   [P2] arXiv abstract page of the same preprint.
+ *
+ * Conventions for every entry point
+ *   - Buffer arguments are DEVICE pointers owned by the caller (for example
+ *     torch.Tensor.data_ptr()).  The library never allocates, frees or keeps
+ *     caller memory; scratch space comes from the caller's `workspace`.
+ *   - Struct arguments (fdl_kv_cache) are HOST structs read during the call only.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls are
+ *     asynchronous and ordered on that stream; nothing synchronises the host.
+ *     Inputs must stay alive, and outputs are valid, once the stream reaches
+ *     the end of the call.
+ *   - Calls on different streams must use different output/workspace buffers.
+ *   - bf16 = IEEE bfloat16 bit patterns, round-to-nearest-even when produced.
+ *   - Return value: FDL_OK, or an error code.  Size, pointer and shape checks
+ *     happen on the host before any launch; on error nothing is launched.
+ *     Index contents of device arrays (positions, slots, block ids, lengths)
+ *     are not read by the host: values out of range are undefined behaviour,
+ *     as for any paged-attention kernel; the caller validates them.
+ *
+ * Supported shapes: head_dim in {64, 128}; block_size in {32, 64, 128, 256};
+ * hidden a multiple of 128 and at most 32768; num_heads * head_dim <= 16384.
+ */
+#ifndef FDLLM_H
+#define FDLLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  FDL_OK = 0,
+  FDL_EINVAL = 1,       /* null pointer, negative or inconsistent size */
+  FDL_EUNSUPPORTED = 2, /* shape outside the supported set above */
+  FDL_EWORKSPACE = 3,   /* workspace smaller than fdl_attention_workspace_bytes() */
+  FDL_EHIP = 4          /* a HIP launch failed; see fdl_last_hip_error() */
+};
+
+/* Paged KV cache of one layer [P4 para 1: keys and values written directly into
+ * the KV cache; a block table maps each sequence's logical blocks].
+ * Pools are bf16 [num_blocks][num_heads][block_size][head_dim]: the keys of one
+ * head inside one page are contiguous (block_size * head_dim elements).
+ * Logical slot s of sequence b is physical block block_table[b*max_blocks_per_seq
+ * + s / block_size], offset s % block_size; its "physical slot" number is
+ * block * block_size + offset.  Entries past ceil(kv_len / block_size) of a
+ * sequence are never read. */
+typedef struct fdl_kv_cache {
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  void *k_cache;              /* device bf16 pool (written by flash_cache_step) */
+  void *v_cache;              /* device bf16 pool */
+  const int32_t *block_table; /* device int32 [batch][max_blocks_per_seq] */
+} fdl_kv_cache;
+
+/* Two-view (Flash-Verify) descriptor of one sequence [P4 para 3].
+ * window_len == 0: plain sequence; every row attends to every slot < kv_len.
+ * Otherwise the window's own slots window_start .. window_start+window_len-1
+ * hold the MASK view, the DRAFT view's keys sit at slots draft_slot_start ..
+ * draft_slot_start+window_len-1 (same rotary positions), and the sequence's
+ * rows are window_len draft rows followed by mask rows.  Draft row i sees the
+ * context (slots < draft_slot_start outside the window) and draft slots
+ * draft_slot_start .. draft_slot_start+i; every later row (mask view) sees all
+ * slots < draft_slot_start.  Requires window_start + window_len <=
+ * draft_slot_start and draft_slot_start + window_len <= kv_len. */
+typedef struct fdl_two_view {
+  int32_t window_start;
+  int32_t window_len;
+  int32_t draft_slot_start;
+} fdl_two_view;
+
+/* Flash-Cache [P4 para 1; P4 para 2 for which rows are active]: for the
+ * num_rows active rows (sliding unmasking window plus tracked rows of every
+ * sequence), Y = X . W_qkv in fp32, rotary embedding of the Q and K parts at
+ * each row's position, rounding to bf16, K and V rows written straight into the
+ * paged cache at the row's slot, Q written to q_out.  One fused launch: the
+ * projections never make an HBM round trip.
+ *   x          device bf16 [num_rows][hidden]
+ *   w_qkv      device bf16 [3*H*D][hidden]: output feature n is row n (the
+ *              nn.Linear weight layout); features [0,HD) are Q, [HD,2HD) K,
+ *              [2HD,3HD) V; head h owns features h*D .. h*D+D-1 of each part.
+ *   cu_rows    device int32 [batch+1]; rows of sequence b are cu_rows[b] ..
+ *              cu_rows[b+1]-1 (non-decreasing, cu_rows[batch] == num_rows).
+ *   positions  device int32 [num_rows], rotary position (0-based) of each row.
+ *   slots      device int32 [num_rows], logical cache slot of each row; slots
+ *              of one call must map to distinct physical slots.
+ *   rope_base  rotary base; pairs (i, i + D/2), angle position*base^(-2i/D).
+ *   q_out      device bf16 [num_rows][H][D]
+ *   slot_mapping_out  device int64 [num_rows] physical slot of each row, or NULL.
+ * num_rows == 0 or batch == 0 is a no-op. */
+int flash_cache_step(const fdl_kv_cache *cache, const void *x, int32_t hidden,
+                     const void *w_qkv, int32_t batch, int32_t num_rows,
+                     const int32_t *cu_rows, const int32_t *positions,
+                     const int32_t *slots, float rope_base, void *q_out,
+                     int64_t *slot_mapping_out, void *stream);
+
+/* Scheduled attention [P4 para 1: block-table scheduling over the ragged
+ * lengths of a batch; P4 para 3: two-view mask] plus, when `mass` is not NULL,
+ * the attention mass that ranks the most-attended keys [P4 para 2].
+ * For sequence b, head h and row r: P = softmax(scale * q_r . k_j) over the
+ * visible slots j < kv_len[b] (see fdl_two_view), out_r = sum_j P_j v_j.
+ *   q          device bf16 [num_rows][H][D] (as written by flash_cache_step)
+ *   kv_len     device int32 [batch]; max_kv_len >= every kv_len[b] (host bound).
+ *   max_rows_per_seq  host upper bound on cu_rows[b+1]-cu_rows[b].
+ *   views      device fdl_two_view [batch], or NULL (all sequences plain).
+ *   softmax_scale  0 selects 1/sqrt(D).
+ *   out        device fp32 [num_rows][H][D]; a row that sees no key gets 0.
+ *   mass       device fp32 [batch][mass_stride] or NULL:
+ *              mass[b][j] = sum over heads and rows of P, for j < kv_len[b];
+ *              entries kv_len[b] <= j < mass_stride are set to 0.  The sum runs
+ *              in a fixed order: results are bitwise reproducible.
+ *   mass_stride >= max_kv_len when mass is given.
+ *   workspace  device scratch of at least fdl_attention_workspace_bytes(...)
+ *              bytes (same arguments); contents need no initialisation. */
+int scheduled_attention(const fdl_kv_cache *cache, const void *q, int32_t batch,
+                        int32_t num_rows, const int32_t *cu_rows,
+                        const int32_t *kv_len, int32_t max_kv_len,
+                        int32_t max_rows_per_seq, const fdl_two_view *views,
+                        float softmax_scale, float *out, float *mass,
+                        int32_t mass_stride, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* Workspace bytes scheduled_attention needs for these sizes (mass_stride 0 =
+ * no mass).  Returns 0 for invalid sizes. */
+size_t fdl_attention_workspace_bytes(int32_t batch, int32_t num_rows,
+                                     int32_t num_heads, int32_t head_dim,
+                                     int32_t max_kv_len, int32_t max_rows_per_seq,
+                                     int32_t mass_stride);
+
+/* Next tracking set [P4 para 2: a fixed budget of most-attended tokens]:
+ * per sequence the topb keys j < kv_len[b] with the largest mass[b][j]; equal
+ * masses go to the lower index.  Written as a set in ascending index order to
+ * idx_out (device int32 [batch][topb]); when kv_len[b] < topb the tail is -1.
+ * mass values must be non-negative and not NaN (attention masses are). */
+int track_topb(const float *mass, int32_t mass_stride, const int32_t *kv_len,
+               int32_t batch, int32_t topb, int32_t *idx_out, void *stream);
+
+/* Flash-Verify acceptance [P4 para 3]: per sequence, the length of the longest
+ * prefix of positions k = 0, 1, ... where draft_tok == mask_tok and conf is
+ * strictly greater than threshold; the scan stops at the first failure.
+ *   draft_tok, mask_tok  device int32 [batch][window]
+ *   conf                 device fp32 [batch][window] (NaN fails)
+ *   accept_len_out       device int32 [batch]
+ * window == 0 gives 0 for every sequence. */
+int verify_accept(const int32_t *draft_tok, const int32_t *mask_tok,
+                  const float *conf, int32_t batch, int32_t window,
+                  float threshold, int32_t *accept_len_out, void *stream);
+
+/* Text for a status code (static storage). */
+const char *fdl_status_string(int status);
+
+/* hipError_t of the most recent FDL_EHIP on this host thread (0 if none). */
+int fdl_last_hip_error(void);
+
+/* Library version string. */
+const char *fdl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FDLLM_H */

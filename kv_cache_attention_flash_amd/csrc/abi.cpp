@@ -1,0 +1,166 @@
+// C ABI of libfdllm: host-side argument validation and kernel dispatch.  The
+// declarations, with the page passages each call implements, are in
+// include/fdllm.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "../../include/fdllm.h"
+#include "internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return FDL_OK;
+  g_last_hip_error = (int)e;
+  return FDL_EHIP;
+}
+
+bool block_size_ok(int bs) { return bs == 32 || bs == 64 || bs == 128 || bs == 256; }
+
+int check_cache(const fdl_kv_cache *c, bool need_pools) {
+  if (!c) return FDL_EINVAL;
+  if (c->num_heads <= 0 || c->head_dim <= 0 || c->block_size <= 0 || c->num_blocks <= 0 ||
+      c->max_blocks_per_seq <= 0)
+    return FDL_EINVAL;
+  if (!c->block_table) return FDL_EINVAL;
+  if (need_pools && (!c->k_cache || !c->v_cache)) return FDL_EINVAL;
+  if (c->head_dim != 64 && c->head_dim != 128) return FDL_EUNSUPPORTED;
+  if (!block_size_ok(c->block_size)) return FDL_EUNSUPPORTED;
+  if ((long)c->num_heads * c->head_dim > 16384) return FDL_EUNSUPPORTED;
+  return FDL_OK;
+}
+
+fdl::CacheView view_of(const fdl_kv_cache *c) {
+  fdl::CacheView v;
+  v.H = c->num_heads;
+  v.D = c->head_dim;
+  v.bs = c->block_size;
+  v.num_blocks = c->num_blocks;
+  v.max_blocks = c->max_blocks_per_seq;
+  v.k = static_cast<uint16_t *>(c->k_cache);
+  v.v = static_cast<uint16_t *>(c->v_cache);
+  v.block_table = c->block_table;
+  return v;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *fdl_status_string(int status) {
+  switch (status) {
+    case FDL_OK: return "ok";
+    case FDL_EINVAL: return "invalid argument (null pointer or inconsistent size)";
+    case FDL_EUNSUPPORTED: return "unsupported shape (head_dim, block_size or hidden)";
+    case FDL_EWORKSPACE: return "workspace too small";
+    case FDL_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int fdl_last_hip_error(void) { return g_last_hip_error; }
+
+const char *fdl_version(void) { return "fdllm 0.1 gfx950"; }
+
+int flash_cache_step(const fdl_kv_cache *cache, const void *x, int32_t hidden, const void *w_qkv,
+                     int32_t batch, int32_t num_rows, const int32_t *cu_rows,
+                     const int32_t *positions, const int32_t *slots, float rope_base,
+                     void *q_out, int64_t *slot_mapping_out, void *stream) {
+  int st = check_cache(cache, true);
+  if (st) return st;
+  if (batch < 0 || num_rows < 0 || hidden <= 0) return FDL_EINVAL;
+  if (!(rope_base > 0.f) || !std::isfinite(rope_base)) return FDL_EINVAL;
+  if (hidden % 128 != 0 || hidden > 32768) return FDL_EUNSUPPORTED;
+  if (batch == 0 || num_rows == 0) return FDL_OK;
+  if (!x || !w_qkv || !cu_rows || !positions || !slots || !q_out) return FDL_EINVAL;
+  fdl::FlashCacheArgs a;
+  a.c = view_of(cache);
+  a.x = static_cast<const uint16_t *>(x);
+  a.w = static_cast<const uint16_t *>(w_qkv);
+  a.hidden = hidden;
+  a.batch = batch;
+  a.rows = num_rows;
+  a.cu_rows = cu_rows;
+  a.positions = positions;
+  a.slots = slots;
+  a.log2_base = std::log2((double)rope_base);
+  a.q_out = static_cast<uint16_t *>(q_out);
+  a.slot_mapping = slot_mapping_out;
+  return hip_status(fdl::launch_flash_cache(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t fdl_attention_workspace_bytes(int32_t batch, int32_t num_rows, int32_t num_heads,
+                                     int32_t head_dim, int32_t max_kv_len,
+                                     int32_t max_rows_per_seq, int32_t mass_stride) {
+  if (batch < 0 || num_rows < 0 || num_heads <= 0 || head_dim <= 0 || max_kv_len < 0 ||
+      max_rows_per_seq < 0 || mass_stride < 0)
+    return 0;
+  return fdl::plan_attention(batch, num_rows, num_heads, head_dim, max_kv_len, max_rows_per_seq,
+                             mass_stride)
+      .bytes;
+}
+
+int scheduled_attention(const fdl_kv_cache *cache, const void *q, int32_t batch,
+                        int32_t num_rows, const int32_t *cu_rows, const int32_t *kv_len,
+                        int32_t max_kv_len, int32_t max_rows_per_seq, const fdl_two_view *views,
+                        float softmax_scale, float *out, float *mass, int32_t mass_stride,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_cache(cache, true);
+  if (st) return st;
+  if (batch < 0 || num_rows < 0 || max_kv_len < 0 || max_rows_per_seq < 0) return FDL_EINVAL;
+  if (!(softmax_scale >= 0.f) || !std::isfinite(softmax_scale)) return FDL_EINVAL;
+  if ((long)max_kv_len > (long)cache->max_blocks_per_seq * cache->block_size) return FDL_EINVAL;
+  if (mass && mass_stride < max_kv_len) return FDL_EINVAL;
+  if (mass && mass_stride <= 0) return FDL_EINVAL;
+  if (batch == 0) return FDL_OK;
+  if (!cu_rows || !kv_len) return FDL_EINVAL;
+  if (num_rows > 0 && (!q || !out)) return FDL_EINVAL;
+  if (num_rows > 0 && max_rows_per_seq == 0) return FDL_EINVAL;
+  const int ms = mass ? mass_stride : 0;
+  fdl::AttnPlan plan = fdl::plan_attention(batch, num_rows, cache->num_heads, cache->head_dim,
+                                           max_kv_len, max_rows_per_seq, ms);
+  if (plan.bytes > workspace_bytes) return FDL_EWORKSPACE;
+  if (plan.bytes && !workspace) return FDL_EWORKSPACE;
+  if (num_rows == 0 && !mass) return FDL_OK;
+  fdl::AttnArgs a;
+  a.c = view_of(cache);
+  a.q = static_cast<const uint16_t *>(q);
+  a.batch = batch;
+  a.rows = num_rows;
+  a.cu_rows = cu_rows;
+  a.kv_len = kv_len;
+  a.views = reinterpret_cast<const int32_t *>(views);
+  const double scale = softmax_scale > 0.f ? (double)softmax_scale
+                                            : 1.0 / std::sqrt((double)cache->head_dim);
+  a.scale_log2 = (float)(scale * 1.4426950408889634073599246810019);
+  a.out = out;
+  a.mass = mass;
+  a.mass_stride = ms;
+  a.ws = static_cast<char *>(workspace);
+  return hip_status(fdl::launch_attention(a, plan, static_cast<hipStream_t>(stream)));
+}
+
+int track_topb(const float *mass, int32_t mass_stride, const int32_t *kv_len, int32_t batch,
+               int32_t topb, int32_t *idx_out, void *stream) {
+  if (batch < 0 || topb <= 0 || mass_stride <= 0) return FDL_EINVAL;
+  if (batch == 0) return FDL_OK;
+  if (!mass || !kv_len || !idx_out) return FDL_EINVAL;
+  return hip_status(
+      fdl::launch_topb(mass, mass_stride, kv_len, batch, topb, idx_out, static_cast<hipStream_t>(stream)));
+}
+
+int verify_accept(const int32_t *draft_tok, const int32_t *mask_tok, const float *conf,
+                  int32_t batch, int32_t window, float threshold, int32_t *accept_len_out,
+                  void *stream) {
+  if (batch < 0 || window < 0) return FDL_EINVAL;
+  if (batch == 0) return FDL_OK;
+  if (!accept_len_out) return FDL_EINVAL;
+  if (window > 0 && (!draft_tok || !mask_tok || !conf)) return FDL_EINVAL;
+  return hip_status(fdl::launch_verify(draft_tok, mask_tok, conf, batch, window, threshold,
+                                       accept_len_out, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Host-side launch interfaces between the C ABI (abi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fdl {
+
+struct CacheView {
+  int H, D, bs, num_blocks, max_blocks;
+  uint16_t *k, *v;
+  const int32_t *block_table;
+};
+
+struct FlashCacheArgs {
+  CacheView c;
+  const uint16_t *x;
+  const uint16_t *w;
+  int hidden, batch, rows;
+  const int32_t *cu_rows, *positions, *slots;
+  double log2_base;
+  uint16_t *q_out;
+  int64_t *slot_mapping;
+};
+
+hipError_t launch_flash_cache(const FlashCacheArgs &a, hipStream_t s);
+
+struct AttnPlan {
+  int row_tiles;      // ceil(max_rows_per_seq / 64)
+  int splits;         // KV splits of the first pass
+  int mass_splits;    // KV chunks of the mass pass (0: no mass)
+  size_t off_part_o, off_part_ml, off_lse, off_mass_part, bytes;
+};
+
+AttnPlan plan_attention(int batch, int rows, int H, int D, int max_kv_len,
+                        int max_rows_per_seq, int mass_stride);
+
+struct AttnArgs {
+  CacheView c;
+  const uint16_t *q;
+  int batch, rows;
+  const int32_t *cu_rows, *kv_len, *views;
+  float scale_log2;
+  float *out, *mass;
+  int mass_stride;
+  char *ws;
+};
+
+hipError_t launch_attention(const AttnArgs &a, const AttnPlan &p, hipStream_t s);
+
+hipError_t launch_topb(const float *mass, int stride, const int32_t *kv_len, int batch,
+                       int topb, int32_t *out, hipStream_t s);
+
+hipError_t launch_verify(const int32_t *draft, const int32_t *mask, const float *conf,
+                         int batch, int window, float thr, int32_t *out, hipStream_t s);
+
+}  // namespace fdl

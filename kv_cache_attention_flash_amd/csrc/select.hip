@@ -1,0 +1,140 @@
+// Tracking-set selection (top-B most-attended keys) and the Flash-Verify accept
+// scan, for gfx950.
+//
+// Sources: [P4] "Flash-dLLM: I/O-Aware KV Caching and Parallel Decoding for
+// Fast, Memory-Efficient Diffusion LLMs" (ai4snews.wisdomeyes.cn summary),
+// para 2 (a fixed budget of the most-attended tokens is kept and updated),
+// para 3 (accept while both views agree and the mask-view confidence exceeds
+// the threshold, in causal order, stopping at the first mismatch).
+#include "device_common.h"
+#include "internal.h"
+
+namespace fdl {
+
+namespace {
+
+// Exclusive prefix count of `flag` over the block (in thread order) and the
+// block total.  256 threads = 4 waves.
+__device__ __forceinline__ int block_excl_count(bool flag, int &total, int *sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned long long bal = __ballot(flag);
+  const int in_wave = __popcll(bal & ((1ull << lane) - 1ull));
+  if (lane == 0) sh[wave] = __popcll(bal);
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int c = sh[w];
+    before += w < wave ? c : 0;
+    total += c;
+  }
+  __syncthreads();
+  return before + in_wave;
+}
+
+// One workgroup (256 threads) per sequence.  Masses are non-negative, so their
+// fp32 bit patterns order like the values: a 4-pass radix select over 8-bit
+// digits finds the bit pattern T of the B-th largest mass; every key above T is
+// taken, and keys equal to T are taken in index order until B are chosen.  A
+// final in-order scan writes the chosen indices ascending.
+__global__ __launch_bounds__(256) void topb_kernel(const float *mass, int stride,
+                                                   const int32_t *kv_len, int topb,
+                                                   int32_t *out) {
+  __shared__ unsigned hist[256];
+  __shared__ unsigned s_digit, s_remaining;
+  __shared__ int sh[4];
+  const int b = blockIdx.x;
+  const int L = kv_len[b];
+  const uint32_t *mb = reinterpret_cast<const uint32_t *>(mass + (size_t)b * stride);
+  int32_t *ob = out + (size_t)b * topb;
+
+  if (L <= topb) {
+    for (int k = threadIdx.x; k < topb; k += blockDim.x) ob[k] = k < L ? k : -1;
+    return;
+  }
+
+  uint32_t prefix = 0, pmask = 0;
+  unsigned remaining = (unsigned)topb;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    hist[threadIdx.x] = 0;
+    __syncthreads();
+    for (int k = threadIdx.x; k < L; k += blockDim.x) {
+      const uint32_t u = mb[k];
+      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned cum = 0;
+      int d = 255;
+      for (; d > 0; --d) {
+        if (cum + hist[d] >= remaining) break;
+        cum += hist[d];
+      }
+      s_digit = (unsigned)d;
+      s_remaining = remaining - cum;
+    }
+    __syncthreads();
+    prefix |= s_digit << shift;
+    pmask |= 255u << shift;
+    remaining = s_remaining;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  // `remaining` keys equal to T are needed (after all keys above T).
+  int base_sel = 0, base_eq = 0;
+  for (int c0 = 0; c0 < L; c0 += blockDim.x) {
+    const int k = c0 + threadIdx.x;
+    const uint32_t u = k < L ? mb[k] : 0u;
+    const bool gt = k < L && u > T;
+    const bool eq = k < L && u == T;
+    int eq_total, sel_total;
+    const int eq_rank = base_eq + block_excl_count(eq, eq_total, sh);
+    const bool sel = gt || (eq && eq_rank < (int)remaining);
+    const int pos = base_sel + block_excl_count(sel, sel_total, sh);
+    if (sel && pos < topb) ob[pos] = k;
+    base_eq += eq_total;
+    base_sel += sel_total;
+  }
+}
+
+// One wave per sequence: ballot the pass/fail flags 64 positions at a time and
+// stop at the first failure.
+__global__ __launch_bounds__(256) void verify_kernel(const int32_t *draft, const int32_t *mask,
+                                                     const float *conf, int batch, int window,
+                                                     float thr, int32_t *out) {
+  const int lane = threadIdx.x & 63;
+  const int seq = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (seq >= batch) return;
+  const size_t row = (size_t)seq * window;
+  int len = window;
+  for (int base = 0; base < window; base += 64) {
+    const int k = base + lane;
+    bool ok = true;
+    if (k < window) ok = draft[row + k] == mask[row + k] && conf[row + k] > thr;
+    const unsigned long long fails = ~__ballot(ok);
+    if (fails) {
+      len = base + __ffsll((long long)fails) - 1;
+      break;
+    }
+  }
+  if (lane == 0) out[seq] = len;
+}
+
+}  // namespace
+
+hipError_t launch_topb(const float *mass, int stride, const int32_t *kv_len, int batch,
+                       int topb, int32_t *out, hipStream_t s) {
+  hipLaunchKernelGGL(topb_kernel, dim3(batch), dim3(256), 0, s, mass, stride, kv_len, topb, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(const int32_t *draft, const int32_t *mask, const float *conf,
+                         int batch, int window, float thr, int32_t *out, hipStream_t s) {
+  hipLaunchKernelGGL(verify_kernel, dim3((batch + 3) / 4), dim3(256), 0, s, draft, mask, conf,
+                     batch, window, thr, out);
+  return hipGetLastError();
+}
+
+}  // namespace fdl

@@ -1,0 +1,108 @@
+"""The C-ABI library loads on a machine without a GPU, exports every function
+include/fdllm.h declares, and rejects bad arguments on the host before any HIP
+call.  No GPU is touched here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_attention_flash_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "fdllm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in {"defined"}))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_lists_the_four_calls():
+    names = declared_functions()
+    for n in ("flash_cache_step", "scheduled_attention", "track_topb", "verify_accept",
+              "fdl_attention_workspace_bytes", "fdl_status_string", "fdl_last_hip_error",
+              "fdl_version"):
+        assert n in names, names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(declared_functions()) == set(_lib.EXPORTS)
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        s = lib.fdl_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.fdl_status_string(99).decode() == "unknown status"
+    assert b"gfx950" in lib.fdl_version()
+
+
+def _cache(h=4, d=64, bs=32, nb=4, mb=4, k=0x1000, v=0x2000, bt=0x3000):
+    return _lib.KVCacheStruct(h, d, bs, nb, mb, k, v, bt)
+
+
+def test_flash_cache_step_validation(lib):
+    fake = 0x10000
+    args = lambda c, hid=256, batch=1, rows=4, base=1e4: lib.flash_cache_step(
+        ctypes.byref(c), fake, hid, fake, batch, rows, fake, fake, fake, base, fake, None, None)
+    assert args(_cache(d=96)) == _lib.FDL_EUNSUPPORTED
+    assert args(_cache(bs=48)) == _lib.FDL_EUNSUPPORTED
+    assert args(_cache(), hid=200) == _lib.FDL_EUNSUPPORTED
+    assert args(_cache(), hid=-128) == _lib.FDL_EINVAL
+    assert args(_cache(), base=0.0) == _lib.FDL_EINVAL
+    assert args(_cache(), base=float("nan")) == _lib.FDL_EINVAL
+    assert args(_cache(h=0)) == _lib.FDL_EINVAL
+    assert args(_cache(bt=0)) == _lib.FDL_EINVAL
+    assert args(_cache(k=0)) == _lib.FDL_EINVAL
+    assert args(_cache(), rows=-1) == _lib.FDL_EINVAL
+    # empty calls are no-ops and touch nothing
+    assert args(_cache(), rows=0) == _lib.FDL_OK
+    assert args(_cache(), batch=0) == _lib.FDL_OK
+    assert lib.flash_cache_step(ctypes.byref(_cache()), None, 256, fake, 1, 3, fake, fake, fake,
+                                1e4, fake, None, None) == _lib.FDL_EINVAL
+    assert lib.flash_cache_step(None, fake, 256, fake, 1, 3, fake, fake, fake, 1e4, fake, None,
+                                None) == _lib.FDL_EINVAL
+
+
+def test_attention_validation_and_workspace(lib):
+    fake = 0x10000
+    ws = lib.fdl_attention_workspace_bytes(1, 64, 32, 128, 768, 64, 768)
+    assert ws > 0
+    assert lib.fdl_attention_workspace_bytes(1, 64, 32, 128, 768, 64, 0) < ws
+    assert lib.fdl_attention_workspace_bytes(-1, 64, 32, 128, 768, 64, 0) == 0
+    c = _cache(h=32, d=128, nb=24, mb=24)
+    call = lambda **kw: lib.scheduled_attention(
+        ctypes.byref(kw.get("c", c)), fake, kw.get("batch", 1), kw.get("rows", 64), fake, fake,
+        kw.get("max_kv", 768), kw.get("max_rows", 64), None, kw.get("scale", 0.0), fake,
+        kw.get("mass", fake), kw.get("stride", 768), kw.get("ws", fake), kw.get("wsb", ws), None)
+    assert call(wsb=ws - 1) == _lib.FDL_EWORKSPACE
+    assert call(ws=None) == _lib.FDL_EWORKSPACE
+    assert call(stride=700) == _lib.FDL_EINVAL         # mass stride below max_kv_len
+    assert call(max_kv=24 * 32 + 1) == _lib.FDL_EINVAL  # exceeds what the block table can map
+    assert call(scale=-1.0) == _lib.FDL_EINVAL
+    assert call(max_rows=0) == _lib.FDL_EINVAL
+    assert call(c=_cache(h=32, d=80)) == _lib.FDL_EUNSUPPORTED
+    assert call(batch=0) == _lib.FDL_OK
+
+
+def test_topb_and_verify_validation(lib):
+    fake = 0x10000
+    assert lib.track_topb(fake, 128, fake, 1, 0, fake, None) == _lib.FDL_EINVAL
+    assert lib.track_topb(fake, 0, fake, 1, 8, fake, None) == _lib.FDL_EINVAL
+    assert lib.track_topb(None, 128, fake, 1, 8, fake, None) == _lib.FDL_EINVAL
+    assert lib.track_topb(fake, 128, fake, 0, 8, fake, None) == _lib.FDL_OK
+    assert lib.verify_accept(fake, fake, fake, -1, 4, 0.9, fake, None) == _lib.FDL_EINVAL
+    assert lib.verify_accept(None, fake, fake, 2, 4, 0.9, fake, None) == _lib.FDL_EINVAL
+    assert lib.verify_accept(fake, fake, fake, 2, 4, 0.9, None, None) == _lib.FDL_EINVAL
+    assert lib.verify_accept(fake, fake, fake, 0, 4, 0.9, fake, None) == _lib.FDL_OK

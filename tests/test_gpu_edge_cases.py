@@ -1,0 +1,169 @@
+"""GPU edge cases, reproducibility and structural invariants of the HIP path."""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from synth import SeqSpec
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+from tests import gpu_util as G  # noqa: E402
+from tests.test_parity_gpu import full_check, _banner  # noqa: E402
+
+
+def _fd():
+    import kv_cache_attention_flash_amd as fd
+    fd.load()
+    return fd
+
+
+def test_ragged_edges():
+    """A sequence with no active rows, one with a single cached slot, one shorter
+    than the tracking budget, one not a multiple of the block size."""
+    _banner("edges: empty sequence, kv_len 1, kv_len < B, ragged tail")
+    specs = [SeqSpec(kv_len=40), SeqSpec(kv_len=1, window=(0, 1)),
+             SeqSpec(kv_len=5, window=(3, 2)), SeqSpec(kv_len=70, window=(33, 16), tracked=(1, 2, 60))]
+    wl = synth.build("edges", 21, 128, 2, 64, 32, 1.0e4, specs, topb=8)
+    run, _ = full_check(wl)
+    idx = run.idx.cpu().numpy()
+    assert list(idx[1]) == [0] + [-1] * 7
+    assert list(idx[2]) == [0, 1, 2, 3, 4, -1, -1, -1]
+    assert np.all(run.mass.cpu().numpy()[0] == 0.0)  # no rows: no mass
+
+
+def test_block_size_64_and_d128():
+    _banner("block size 64, head_dim 128")
+    g = np.random.default_rng(5)
+    specs = [SeqSpec(kv_len=130, window=(64, 32), tracked=(0, 5, 9)),
+             SeqSpec(kv_len=64, window=(7, 20)),
+             SeqSpec(kv_len=200, window=(128, 32), tracked=tuple(sorted(g.choice(128, 30, replace=False))))]
+    wl = synth.build("bs64", 22, 256, 3, 128, 64, 5.0e5, specs, topb=16)
+    full_check(wl)
+
+
+def test_empty_calls():
+    fd = _fd()
+    dev = "cuda:0"
+    wl = synth.tiny_h256()
+    run = G.GpuRun(wl, dev)
+    x0 = run.x[:0]
+    q, sm = fd.flash_cache_step(run.cache, x0, run.w, G.i32([0, 0], dev), G.i32([], dev),
+                                G.i32([], dev), 1e4)
+    assert q.shape[0] == 0
+    # rows = 0 with mass requested: mass is all zeros
+    mass = torch.full((1, 128), 7.0, device=dev)
+    out, m = fd.scheduled_attention(run.cache, q, G.i32([0, 0], dev), run.kv_len, 128, 0, mass=mass)
+    torch.cuda.synchronize()
+    assert torch.all(m == 0)
+
+
+def test_deterministic_reruns():
+    _banner("bitwise reruns")
+    wl = synth.llada8b_b1()
+    a = G.GpuRun(wl).step()
+    b = G.GpuRun(wl).step()
+    for f in ("q", "out", "mass", "idx", "slot_mapping"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+    assert torch.equal(a.cache.k_cache, b.cache.k_cache)
+
+
+def test_block_permutation_invariance():
+    _banner("block-table permutation invariance")
+    wl = synth.small_ragged()
+    perm = np.random.default_rng(99).permutation(wl.num_blocks)
+    bt2 = np.zeros_like(wl.block_table)
+    k2 = np.zeros_like(wl.k_cache)
+    v2 = np.zeros_like(wl.v_cache)
+    off = 0
+    for b in range(wl.batch):
+        n = -(-int(wl.kv_len[b]) // wl.block_size)
+        bt2[b, :n] = perm[off:off + n]
+        off += n
+        k2[bt2[b, :n]] = wl.k_cache[wl.block_table[b, :n]]
+        v2[bt2[b, :n]] = wl.v_cache[wl.block_table[b, :n]]
+    a = G.GpuRun(wl).step()
+    b = G.GpuRun(wl, k=G.bf16_tensor(k2, "cuda:0"), v=G.bf16_tensor(v2, "cuda:0"),
+                 block_table=bt2).step()
+    for f in ("q", "out", "mass", "idx"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+
+
+def test_uniform_attention_ties():
+    """All hidden states zero: every score is 0, every visible key gets exactly
+    the same mass, so the lower-index tie rule gives top-B = {0..B-1}."""
+    _banner("exact ties")
+    wl = synth.llada8b_b1()
+    wl.x = np.zeros_like(wl.x)
+    run = G.GpuRun(wl).step()
+    m = run.mass.cpu().numpy()[0]
+    assert np.all(m[:768] == m[0])
+    assert list(run.idx.cpu().numpy()[0]) == list(range(32))
+
+
+def test_two_view_isolation_and_causality():
+    """Changing the draft rows' inputs leaves the mask rows' outputs bit-identical
+    and vice versa; changing draft row j leaves draft rows i < j bit-identical."""
+    _banner("two-view isolation")
+    wl = synth.small_verify()
+    base = G.GpuRun(wl).step()
+    out0 = base.out.cpu().numpy()
+    wlen = int(wl.views[0, 1])
+    r0 = int(wl.cu_rows[0])
+    # perturb all draft rows of sequence 0
+    x = wl.x.copy()
+    x[r0:r0 + wlen] = synth.normal_bf16(77, 0, 0, (wlen, wl.hid))
+    run = G.GpuRun(wl, x=G.bf16_tensor(x, "cuda:0")).step()
+    o = run.out.cpu().numpy()
+    assert np.array_equal(o[r0 + wlen:r0 + 2 * wlen], out0[r0 + wlen:r0 + 2 * wlen])
+    assert not np.array_equal(o[r0:r0 + wlen], out0[r0:r0 + wlen])
+    # perturb mask rows of sequence 0
+    x = wl.x.copy()
+    x[r0 + wlen:r0 + 2 * wlen] = synth.normal_bf16(78, 0, 0, (wlen, wl.hid))
+    run = G.GpuRun(wl, x=G.bf16_tensor(x, "cuda:0")).step()
+    o = run.out.cpu().numpy()
+    assert np.array_equal(o[r0:r0 + wlen], out0[r0:r0 + wlen])
+    # perturb draft row 5 only
+    x = wl.x.copy()
+    x[r0 + 5] = synth.normal_bf16(79, 0, 0, (1, wl.hid))[0]
+    run = G.GpuRun(wl, x=G.bf16_tensor(x, "cuda:0")).step()
+    o = run.out.cpu().numpy()
+    assert np.array_equal(o[r0:r0 + 5], out0[r0:r0 + 5])
+    assert not np.array_equal(o[r0 + 5:r0 + wlen], out0[r0 + 5:r0 + wlen])
+
+
+def test_topb_crafted_masses():
+    """track_topb alone on crafted masses (ties, zeros, kv_len < B, long rows)."""
+    fd = _fd()
+    dev = "cuda:0"
+    rng = np.random.default_rng(3)
+    rows = [np.array([0.5, 2.0, 2.0, 0.1, 3.0, 2.0, 0.0] + [0.0] * 4089, np.float32),
+            rng.integers(0, 4, 4096).astype(np.float32) / 8,
+            rng.random(4096, dtype=np.float32),
+            np.zeros(4096, np.float32)]
+    lens = [7, 4096, 3000, 10]
+    mass = torch.from_numpy(np.stack(rows)).to(dev)
+    kv = G.i32(lens, dev)
+    for b_ in (1, 3, 8, 32, 100):
+        got = fd.track_topb(mass, kv, b_).cpu().numpy()
+        for i, L in enumerate(lens):
+            assert np.array_equal(got[i], O.top_b(rows[i].astype(np.float64), L, b_)), (b_, i)
+
+
+def test_verify_long_window():
+    """Windows longer than one wavefront; crafted prefixes."""
+    fd = _fd()
+    dev = "cuda:0"
+    v = synth.verify_scan_inputs(31, 5, 150)
+    d, m, c = v["draft"].copy(), v["mask"].copy(), v["conf"].copy()
+    d[:3] = np.arange(150)
+    m[:3] = np.arange(150)
+    c[:3] = 0.99
+    m[1, 97] += 1
+    c[2, 64] = 0.9
+    got = fd.verify_accept(*(torch.from_numpy(a).to(dev) for a in (d, m, c)), 0.9).cpu().numpy()
+    want = [O.accept_length(d[i], m[i], c[i], v["threshold"]) for i in range(len(d))]
+    assert list(got) == want
+    assert want[:3] == [150, 97, 64]
