@@ -48,7 +48,7 @@ __device__ __forceinline__ void rope_cs(int pos, int i, int D, double log2_base,
   sincosf((float)red, &s, &c);
 }
 
-template <int MT, int NT, int NW>
+template <int MT, int NT, int NW, int DEPTH>
 __global__ __launch_bounds__(NW * 64) void qkv_rope_write_kernel(FlashCacheArgs a) {
   constexpr int ROWS = 16 * MT;
   constexpr int COLS = 16 * NT;
@@ -112,19 +112,47 @@ __global__ __launch_bounds__(NW * 64) void qkv_rope_write_kernel(FlashCacheArgs 
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll 4
-  for (int st = s_begin; st < s_end; ++st) {
-    const int k = st * 32;
-    u32x4 av[MT], bv[NT];
+  // Register ring of DEPTH reduction steps in flight per wave: the loads of
+  // step st + DEPTH are issued as soon as step st's operands are consumed, so
+  // every wave keeps DEPTH * (MT + NT) KiB of loads outstanding.
+  // Loads are unconditional (addresses clamped to the last valid step) so the
+  // compiler can count outstanding loads exactly across the unrolled ring.
+  u32x4 abuf[DEPTH][MT], bbuf[DEPTH][NT];
+  const int nsteps = max(0, s_end - s_begin);
+  const int nfull = nsteps / DEPTH * DEPTH;
+  // Workgroups start their step loop at different offsets (rotation by the
+  // workgroup's index within its XCD) so that the many workgroups sharing an
+  // L2 do not all read the same activation lines at the same moment.
+#ifndef FDL_FC_ROTATE
+#define FDL_FC_ROTATE 1
+#endif
+  const int rot = FDL_FC_ROTATE ? (int)(blockIdx.x >> 3) : 0;
+  auto issue = [&](int d, int st) {
+    const int rel = min(st, s_end - 1) - s_begin;
+    const int k = (nsteps > 0 ? s_begin + (rel + rot) % nsteps : 0) * 32;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) bv[t] = ld16(wrow[t] + k);
+    for (int t = 0; t < NT; ++t) bbuf[d][t] = ld16(wrow[t] + k);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) av[mt] = ld16(xrow[mt] + k);
+    for (int mt = 0; mt < MT; ++mt) abuf[d][mt] = ld16(xrow[mt] + k);
+  };
+  auto consume = [&](int d) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[mt][t] = mfma16(av[mt], bv[t], acc[mt][t]);
+      for (int t = 0; t < NT; ++t) acc[mt][t] = mfma16(abuf[d][mt], bbuf[d][t], acc[mt][t]);
+  };
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) issue(d, s_begin + d);
+  for (int st0 = 0; st0 < nfull; st0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      consume(d);
+      issue(d, s_begin + st0 + d + DEPTH);
+    }
   }
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (d < nsteps - nfull) consume(d);
 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -175,11 +203,23 @@ __global__ __launch_bounds__(NW * 64) void qkv_rope_write_kernel(FlashCacheArgs 
 
 }  // namespace
 
+// Tile shape of the skinny (few active rows) projection: 16*MT rows, 8*NT
+// rotary pairs and NW waves per workgroup, DEPTH reduction steps in flight.
+#ifndef FDL_FC_NT
+#define FDL_FC_NT 3
+#endif
+#ifndef FDL_FC_NW
+#define FDL_FC_NW 8
+#endif
+#ifndef FDL_FC_DEPTH
+#define FDL_FC_DEPTH 4
+#endif
+
 hipError_t launch_flash_cache(const FlashCacheArgs &a, hipStream_t s) {
-  constexpr int MT = 4, NT = 3, NW = 8;
+  constexpr int MT = 4, NT = FDL_FC_NT, NW = FDL_FC_NW, DEPTH = FDL_FC_DEPTH;
   const int total_pairs = 3 * a.c.H * (a.c.D / 2);
   dim3 grid((total_pairs + 8 * NT - 1) / (8 * NT), (a.rows + 16 * MT - 1) / (16 * MT));
-  hipLaunchKernelGGL((qkv_rope_write_kernel<MT, NT, NW>), grid, dim3(NW * 64), 0, s, a);
+  hipLaunchKernelGGL((qkv_rope_write_kernel<MT, NT, NW, DEPTH>), grid, dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
