@@ -175,7 +175,7 @@ def main():
     traffic = load_traffic()
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "flash_cache_step (qkv_rope_write_kernel)",
+                "kernel": "flash_cache_step",
                 "algorithmic_bytes": fb, "avg_launch_us": round(fcs_ms * 1e3, 2)}
     log(f"step {ms_per_step * 1e3:.1f} us; flash_cache_step {fcs_ms * 1e3:.1f} us "
         f"({achieved:.0f} GB/s); scheduled_attention {att_ms * 1e3:.1f} us")

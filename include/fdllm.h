@@ -99,12 +99,23 @@ typedef struct fdl_two_view {
  *   rope_base  rotary base; pairs (i, i + D/2), angle position*base^(-2i/D).
  *   q_out      device bf16 [num_rows][H][D]
  *   slot_mapping_out  device int64 [num_rows] physical slot of each row, or NULL.
- * num_rows == 0 or batch == 0 is a no-op. */
+ *   workspace  device scratch of fdl_flash_cache_workspace_bytes(...) bytes
+ *              (no initialisation needed); NULL when that is 0.
+ * num_rows == 0 or batch == 0 is a no-op.  Output bits do not depend on the
+ * order in which workgroups finish: partial sums are added in a fixed order. */
 int flash_cache_step(const fdl_kv_cache *cache, const void *x, int32_t hidden,
                      const void *w_qkv, int32_t batch, int32_t num_rows,
                      const int32_t *cu_rows, const int32_t *positions,
                      const int32_t *slots, float rope_base, void *q_out,
-                     int64_t *slot_mapping_out, void *stream);
+                     int64_t *slot_mapping_out, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/* Workspace bytes flash_cache_step needs for these sizes (0: none; then
+ * workspace may be NULL).  It holds the fp32 partial sums of a reduction split
+ * across workgroups; two calls that may run at the same time must not share
+ * a workspace. */
+size_t fdl_flash_cache_workspace_bytes(int32_t num_rows, int32_t hidden,
+                                       int32_t num_heads, int32_t head_dim);
 
 /* Scheduled attention [P4 para 1: block-table scheduling over the ragged
  * lengths of a batch; P4 para 3: two-view mask] plus, when `mass` is not NULL,

@@ -27,7 +27,8 @@ from . import _lib
 from ._lib import FdlError, KVCacheStruct  # noqa: F401
 
 __all__ = ["PagedKVCache", "flash_cache_step", "scheduled_attention", "track_topb",
-           "verify_accept", "attention_workspace_bytes", "DecodeStep", "FdlError", "load"]
+           "verify_accept", "attention_workspace_bytes", "flash_cache_workspace_bytes",
+           "DecodeStep", "FdlError", "load"]
 
 
 def load():
@@ -49,6 +50,23 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: Optional[int] = 
         raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+
+
+_FC_WS = {}
+
+
+def _flash_cache_workspace(device, stream_handle: int, nbytes: int):
+    """Split-reduction scratch, one per (device, stream)."""
+    key = (device.index if device.index is not None else torch.cuda.current_device(), stream_handle)
+    ws = _FC_WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=device)
+        _FC_WS[key] = ws
+    return ws
+
+
+def flash_cache_workspace_bytes(num_rows, hidden, num_heads, head_dim) -> int:
+    return int(_lib.load().fdl_flash_cache_workspace_bytes(num_rows, hidden, num_heads, head_dim))
 
 
 def _stream(stream, device) -> int:
@@ -117,10 +135,13 @@ def flash_cache_step(cache: PagedKVCache, x, w_qkv, cu_rows, positions, slots, r
         slot_mapping_out = torch.empty((r,), dtype=torch.int64, device=x.device)
     _need(slot_mapping_out, "slot_mapping_out", torch.int64, 1)
     cs = cache.struct()
+    sh = _stream(stream, x.device)
+    need = flash_cache_workspace_bytes(r, hid, h, d)
+    ws = _flash_cache_workspace(x.device, sh, need) if need else None
     st = lib.flash_cache_step(ctypes.byref(cs), x.data_ptr(), hid, w_qkv.data_ptr(), batch, r,
                               cu_rows.data_ptr(), positions.data_ptr(), slots.data_ptr(),
                               float(rope_base), q_out.data_ptr(), slot_mapping_out.data_ptr(),
-                              _stream(stream, x.device))
+                              _ptr(ws), need, sh)
     _lib.check("flash_cache_step", st)
     return q_out, slot_mapping_out
 
@@ -244,10 +265,13 @@ class DecodeStep:
         need = attention_workspace_bytes(self.batch, r, h, d, int(max_kv_len),
                                          int(max_rows_per_seq), ms)
         self.workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+        fneed = flash_cache_workspace_bytes(r, x.shape[1], h, d)
+        self.fc_workspace = torch.empty((max(fneed, 1),), dtype=torch.uint8, device=dev)
         self.cs = cache.struct()
         self._fcs = (ctypes.byref(self.cs), x.data_ptr(), x.shape[1], w_qkv.data_ptr(),
                      self.batch, r, cu_rows.data_ptr(), positions.data_ptr(), slots.data_ptr(),
-                     float(rope_base), self.q.data_ptr(), self.slot_mapping.data_ptr())
+                     float(rope_base), self.q.data_ptr(), self.slot_mapping.data_ptr(),
+                     self.fc_workspace.data_ptr(), fneed)
         self._att = (ctypes.byref(self.cs), self.q.data_ptr(), self.batch, r, cu_rows.data_ptr(),
                      kv_len.data_ptr(), int(max_kv_len), int(max_rows_per_seq), _ptr(views),
                      float(softmax_scale), self.out.data_ptr(), _ptr(self.mass), ms,

@@ -37,15 +37,58 @@ __device__ __forceinline__ int row_to_seq(const int32_t *cu_rows, int batch, int
   return lo;
 }
 
-// cos/sin of position * base^(-2i/D): angle and its reduction to [-pi, pi] in
+// Rotary frequency base^(-2i/D) in fp64.
+__device__ __forceinline__ double rope_inv_freq(int i, int D, double log2_base) {
+  return exp2(-(2.0 * (double)i / (double)D) * log2_base);
+}
+
+// cos/sin of position * inv_freq: angle and its reduction to [-pi, pi] in
 // fp64, the trigonometric functions in fp32 on the reduced angle.
-__device__ __forceinline__ void rope_cs(int pos, int i, int D, double log2_base, float &c,
-                                        float &s) {
-  double theta = exp2(-(2.0 * (double)i / (double)D) * log2_base);
-  double ang = (double)pos * theta;
+__device__ __forceinline__ void rope_cs(int pos, double inv_freq, float &c, float &s) {
+  double ang = (double)pos * inv_freq;
   double k = rint(ang * (1.0 / kTwoPi));
   double red = fma(-k, kTwoPi, ang);
   sincosf((float)red, &s, &c);
+}
+
+// Rotate (Q and K parts), round and store one rotary pair of one row.
+__device__ __forceinline__ void store_pair(const FlashCacheArgs &a, int r, int p, float lo,
+                                           float hi, int blk, int off, int pos,
+                                           double inv_freq_i) {
+  const int H = a.c.H, D = a.c.D, half = D >> 1;
+  const int sh = p / half;  // section * H + head
+  const int i = p % half;
+  const int sec = sh / H;
+  const int h = sh % H;
+  if (sec < 2) {
+    float c, s;
+    rope_cs(pos, inv_freq_i, c, s);
+    const float rlo = lo * c - hi * s;
+    const float rhi = hi * c + lo * s;
+    lo = rlo;
+    hi = rhi;
+  }
+  uint16_t *dst;
+  if (sec == 0) {
+    dst = a.q_out + ((size_t)r * H + h) * D;
+  } else {
+    uint16_t *pool = sec == 1 ? a.c.k : a.c.v;
+    dst = pool + (((size_t)blk * H + h) * a.c.bs + off) * D;
+  }
+  dst[i] = f32_to_bf16_rne(lo);
+  dst[i + half] = f32_to_bf16_rne(hi);
+}
+
+// Row metadata (physical block, offset, position) of row r; also writes the
+// slot mapping when asked.
+__device__ __forceinline__ void row_meta(const FlashCacheArgs &a, int r, bool write_map, int &blk,
+                                         int &off, int &pos) {
+  const int b = row_to_seq(a.cu_rows, a.batch, r);
+  const int s = a.slots[r];
+  blk = a.c.block_table[(size_t)b * a.c.max_blocks + s / a.c.bs];
+  off = s % a.c.bs;
+  pos = a.positions[r];
+  if (write_map && a.slot_mapping) a.slot_mapping[r] = (int64_t)blk * a.c.bs + off;
 }
 
 template <int MT, int NT, int NW, int DEPTH>
@@ -55,6 +98,7 @@ __global__ __launch_bounds__(NW * 64) void qkv_rope_write_kernel(FlashCacheArgs 
   constexpr int PAIRS = 8 * NT;
   __shared__ float red[NW][ROWS][COLS + 1];
   __shared__ int s_blk[ROWS], s_off[ROWS], s_pos[ROWS];
+  __shared__ double s_freq[64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -64,6 +108,7 @@ __global__ __launch_bounds__(NW * 64) void qkv_rope_write_kernel(FlashCacheArgs 
   const int pair0 = blockIdx.x * PAIRS;
   const int row0 = blockIdx.y * ROWS;
   const int hidden = a.hidden;
+  if (tid < half) s_freq[tid] = rope_inv_freq(tid, D, a.log2_base);
 
   // Row metadata: sequence, physical slot, rotary position.
   if (tid < ROWS) {
@@ -182,7 +227,7 @@ __global__ __launch_bounds__(NW * 64) void qkv_rope_write_kernel(FlashCacheArgs 
     const int h = sh % H;
     if (sec < 2) {
       float c, s;
-      rope_cs(s_pos[rl], i, D, a.log2_base, c, s);
+      rope_cs(s_pos[rl], s_freq[i], c, s);
       const float rlo = lo * c - hi * s;
       const float rhi = hi * c + lo * s;
       lo = rlo;
@@ -201,6 +246,243 @@ __global__ __launch_bounds__(NW * 64) void qkv_rope_write_kernel(FlashCacheArgs 
   }
 }
 
+
+// Split-K projection for up to 64 active rows (the decode regime, where the
+// weight stream dominates).  Grid = G column groups x S reduction splits.  A
+// workgroup owns CW = 16*NTW*NGW output features (CW/2 rotary pairs) of 64 rows
+// over hidden/S reduction elements, staged through LDS in 128-element chunks:
+// every global load instruction reads whole 128-byte lines (16 lanes per
+// 256-byte row segment), and the 64 x hidden activations are read G times in
+// total instead of once per 48 features.  Chunk tiles are double-buffered in
+// LDS with a 16-byte-slot XOR swizzle (slot ^ row % 16) so the 16 lanes that
+// read one MFMA operand hit distinct banks; two register stages keep two
+// chunks of loads in flight.  8 waves: wave w owns N-tile group w % NGW and
+// reduction quarter w / NGW of each chunk.
+//
+// With S == 1 the workgroup runs the rotary / bf16 / cache-write epilogue
+// itself.  With S > 1 it stores its fp32 partial tile and qkv_reduce_kernel
+// (next launch on the stream) adds the S partials in split order, so the
+// result does not depend on which workgroup finishes first.  (Finishing the
+// reduction inside this kernel would need device-scope release/acquire fences,
+// which on a multi-XCD part write back and invalidate the L2 that the weight
+// stream is using.)
+struct SplitPlan {
+  int G, S, ks;     // column groups, splits, reduction elements per split
+  float *partials;  // [G][S][64][CW]
+};
+
+template <int NTW, int NGW, int NST, int NCH, int NW, int KC>
+__global__ __launch_bounds__(NW * 64) void qkv_splitk_kernel(FlashCacheArgs a, SplitPlan sp) {
+  constexpr int NKQ = NW / NGW;
+  constexpr int CW = 16 * NTW * NGW;
+  constexpr int PW = CW / 2;
+  constexpr int ROWS = 64;
+  constexpr int PIECES = KC / 8;            // 16-byte pieces per row per chunk (KC per chunk)
+  constexpr int KSTEPS = KC / 32;           // MFMA k-steps per chunk
+  constexpr int TROWS = ROWS + CW;          // staged rows per chunk
+  constexpr int LOADS = TROWS * PIECES / (NW * 64);
+  static_assert(TROWS * PIECES % (NW * 64) == 0, "chunk must split evenly");
+  static_assert(KSTEPS % NKQ == 0, "k-steps per chunk must split over the quarters");
+  __shared__ u32x4 lds[2][TROWS * PIECES];
+  __shared__ int s_blk[ROWS], s_off[ROWS], s_pos[ROWS];
+  __shared__ double s_freq[64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.c.H, D = a.c.D, half = D >> 1;
+  const int total_pairs = 3 * H * half;
+  const int hidden = a.hidden;
+  if (sp.S == 1 && tid < half) s_freq[tid] = rope_inv_freq(tid, D, a.log2_base);
+
+  // Block -> (group, split) so that the S splits of a group run on one XCD
+  // (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
+  const int nb = sp.G * sp.S;
+  int idx = blockIdx.x;
+  if (nb % 8 == 0) idx = (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8;
+  const int grp = idx / sp.S, split = idx % sp.S;
+  const int pair0 = grp * PW;
+  const int k_begin = split * sp.ks;
+
+  // Global rows this thread stages: row t/16 + 32*i of the chunk tile, piece t%16.
+  const int piece = tid % PIECES;
+  const uint16_t *src[LOADS];
+  int dst_slot[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int tr = tid / PIECES + (NW * 64 / PIECES) * i;
+    dst_slot[i] = tr * PIECES + (piece ^ (tr & 15));
+    static_assert(PIECES >= 16, "swizzle needs 16 pieces per row");
+    if (tr < ROWS) {
+      const int r = min(tr, a.rows - 1);
+      src[i] = a.x + (size_t)r * hidden + k_begin + piece * 8;
+    } else {
+      const int c = tr - ROWS;  // column in the group: tile c/16, lane col c%16
+      int p = pair0 + 8 * (c / 16) + (c & 7);
+      p = p < total_pairs ? p : total_pairs - 1;
+      const int feat = (p / half) * D + (p % half) + ((c & 8) ? half : 0);
+      src[i] = a.w + (size_t)feat * hidden + k_begin + piece * 8;
+    }
+  }
+
+  if (sp.S == 1 && tid < ROWS && tid < a.rows) {
+    int blk, off, pos;
+    row_meta(a, tid, idx == 0, blk, off, pos);
+    s_blk[tid] = blk;
+    s_off[tid] = off;
+    s_pos[tid] = pos;
+  }
+
+  const int g = lane >> 4, j = lane & 15;
+  const int ng = wave % NGW, kq = wave / NGW;
+  f32x4 acc[4][NTW];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const u32x4 *buf) {
+#pragma unroll
+    for (int q = 0; q < KSTEPS / NKQ; ++q) {
+      const int ks = kq * (KSTEPS / NKQ) + q;  // k-step of 32 inside the chunk
+      const int pc = 4 * ks + g;               // this lane's 16-byte piece
+      u32x4 af[4], bfr[NTW];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) af[mt] = buf[(16 * mt + j) * PIECES + (pc ^ j)];
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+        bfr[t] = buf[(ROWS + 16 * (ng * NTW + t) + j) * PIECES + (pc ^ j)];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) acc[mt][t] = mfma16(af[mt], bfr[t], acc[mt][t]);
+    }
+  };
+  // Column groups visit their chunks in rotated order: at any moment the
+  // groups read different 256-byte offsets of their weight rows (rows are a
+  // power-of-two stride apart), spreading requests over the HBM channels.
+#ifndef FDL_FC_ROT
+#define FDL_FC_ROT 1
+#endif
+  const int nch_rt = NCH > 0 ? NCH : sp.ks / KC;
+  const int rot = FDL_FC_ROT ? grp % nch_rt : 0;
+  auto load = [&](u32x4 *reg, int c) {
+    int cc = c + rot;
+    cc = cc >= nch_rt ? cc - nch_rt : cc;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) reg[i] = ld16(src[i] + (size_t)cc * KC);
+  };
+  auto store = [&](u32x4 *buf, const u32x4 *reg) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) buf[dst_slot[i]] = reg[i];
+  };
+
+  // NST register stages and two LDS buffers: while chunk c is multiplied out
+  // of one LDS buffer, chunk c + 1 moves from registers into the other and
+  // chunks c + 2 .. c + NST are in flight from HBM.  With a compile-time chunk
+  // count (NCH > 0) the loop is fully unrolled, so the compiler knows exactly
+  // which loads each LDS store waits for; scheduling barriers keep the load
+  // groups in issue order.  Loads past the last chunk re-read it (clamped).
+  const int nchunks = NCH > 0 ? NCH : sp.ks / KC;
+  u32x4 r[NST][LOADS];
+#pragma unroll
+  for (int t = 0; t < NST; ++t) {
+    load(r[t], min(t, nchunks - 1));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  store(lds[0], r[0]);
+  load(r[0], min(NST, nchunks - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  if constexpr (NCH > 0) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      compute(lds[c & 1]);
+      if (c + 1 < NCH) {
+        store(lds[(c + 1) & 1], r[(c + 1) % NST]);
+        if (c + 1 + NST < NCH) load(r[(c + 1) % NST], c + 1 + NST);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+      }
+    }
+  } else {
+    for (int c0 = 0; c0 < nchunks; c0 += 2 * NST) {
+#pragma unroll
+      for (int u = 0; u < 2 * NST; ++u) {
+        const int c = c0 + u;
+        if (c >= nchunks) break;
+        compute(lds[u & 1]);
+        store(lds[(u + 1) & 1], r[(u + 1) % NST]);
+        load(r[(u + 1) % NST], min(c + 1 + NST, nchunks - 1));
+        __syncthreads();
+      }
+    }
+  }
+  __syncthreads();
+
+  // Reduce the NKQ reduction quarters into Y[64][CW] (fp32, reusing the LDS).
+  float *Y = reinterpret_cast<float *>(&lds[0][0]);
+  constexpr int YS = CW + 4;  // padded row stride
+  static_assert(ROWS * YS * 4 <= (int)sizeof(lds), "LDS reuse");
+  for (int q = NKQ - 1; q >= 0; --q) {
+    if (kq == q) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float *y = &Y[(16 * mt + 4 * g + e) * YS + 16 * (ng * NTW + t) + j];
+            *y = (q == NKQ - 1) ? acc[mt][t][e] : acc[mt][t][e] + *y;
+          }
+    }
+    __syncthreads();
+  }
+
+  if (sp.S > 1) {
+    float *part = sp.partials + ((size_t)grp * sp.S + split) * ROWS * CW;
+    for (int e = tid; e < ROWS * CW / 4; e += NW * 64) {
+      const int row = (4 * e) / CW, col = (4 * e) % CW;
+      *reinterpret_cast<f32x4 *>(part + 4 * e) = *reinterpret_cast<const f32x4 *>(&Y[row * YS + col]);
+    }
+    return;
+  }
+  for (int item = tid; item < ROWS * PW; item += NW * 64) {
+    const int rl = item / PW, pl = item % PW;
+    const int p = pair0 + pl;
+    if (rl >= a.rows || p >= total_pairs) continue;
+    const int clo = 16 * (pl >> 3) + (pl & 7);
+    store_pair(a, rl, p, Y[rl * YS + clo], Y[rl * YS + clo + 8], s_blk[rl], s_off[rl], s_pos[rl],
+               s_freq[p % half]);
+  }
+}
+
+// Adds the S split partials of qkv_splitk_kernel in split order and runs the
+// epilogue.  One thread per (row, rotary pair); consecutive threads read
+// consecutive partial columns.
+template <int CW>
+__global__ __launch_bounds__(256) void qkv_reduce_kernel(FlashCacheArgs a, SplitPlan sp) {
+  constexpr int PW = CW / 2;
+  const int total_pairs = 3 * a.c.H * (a.c.D / 2);
+  const int item = blockIdx.x * blockDim.x + threadIdx.x;
+  const int per_group = a.rows * PW;
+  if (item >= sp.G * per_group) return;
+  const int grp = item / per_group;
+  const int rl = (item % per_group) / PW, pl = item % PW;
+  const int p = grp * PW + pl;
+  if (p >= total_pairs) return;
+  const int clo = 16 * (pl >> 3) + (pl & 7);
+  const size_t split_stride = (size_t)64 * CW;
+  const float *base = sp.partials + (size_t)grp * sp.S * split_stride + rl * CW + clo;
+  float lo = 0.f, hi = 0.f;
+  for (int q = 0; q < sp.S; ++q) {
+    lo += base[q * split_stride];
+    hi += base[q * split_stride + 8];
+  }
+  int blk, off, pos;
+  row_meta(a, rl, grp == 0 && pl == 0, blk, off, pos);
+  store_pair(a, rl, p, lo, hi, blk, off, pos,
+             rope_inv_freq(p % (a.c.D >> 1), a.c.D, a.log2_base));
+}
+
 }  // namespace
 
 // Tile shape of the skinny (few active rows) projection: 16*MT rows, 8*NT
@@ -215,7 +497,86 @@ __global__ __launch_bounds__(NW * 64) void qkv_rope_write_kernel(FlashCacheArgs 
 #define FDL_FC_DEPTH 4
 #endif
 
-hipError_t launch_flash_cache(const FlashCacheArgs &a, hipStream_t s) {
+#ifndef FDL_FC_NTW
+#define FDL_FC_NTW 3
+#endif
+#ifndef FDL_FC_NGW
+#define FDL_FC_NGW 1
+#endif
+#ifndef FDL_FC_NST
+#define FDL_FC_NST 2
+#endif
+#ifndef FDL_FC_SNW
+#define FDL_FC_SNW 8
+#endif
+#ifndef FDL_FC_KC
+#define FDL_FC_KC 256
+#endif
+#ifndef FDL_FC_SPLIT_CAP
+#define FDL_FC_SPLIT_CAP 320
+#endif
+namespace {
+constexpr int kSplitNTW = FDL_FC_NTW, kSplitNGW = FDL_FC_NGW;
+constexpr int kSplitCW = 16 * kSplitNTW * kSplitNGW;  // features per column group
+
+struct FcPlan {
+  bool splitk;
+  int G, S;
+  size_t bytes;
+};
+
+FcPlan plan_fc(int rows, int hidden, int H, int D) {
+  FcPlan p{};
+  const int total_pairs = 3 * H * (D / 2);
+  if (rows > 64 || hidden % FDL_FC_KC != 0) return p;  // row-strip kernel, no workspace
+  p.splitk = true;
+  p.G = (total_pairs + kSplitCW / 2 - 1) / (kSplitCW / 2);
+  p.S = 1;
+  while (p.S < 8 && p.G * 2 * p.S <= FDL_FC_SPLIT_CAP && hidden % (FDL_FC_KC * 2 * p.S) == 0) p.S *= 2;
+  if (p.S > 1) p.bytes = (size_t)p.G * p.S * 64 * kSplitCW * sizeof(float);
+  return p;
+}
+}  // namespace
+
+size_t flash_cache_workspace_bytes(int rows, int hidden, int H, int D) {
+  return plan_fc(rows, hidden, H, D).bytes;
+}
+
+hipError_t launch_flash_cache(const FlashCacheArgs &a, void *ws, size_t ws_bytes, hipStream_t s) {
+  const FcPlan fp = plan_fc(a.rows, a.hidden, a.c.H, a.c.D);
+  if (fp.splitk) {
+    if (ws_bytes < fp.bytes || (fp.bytes && !ws)) return hipErrorInvalidValue;
+    SplitPlan sp;
+    sp.G = fp.G;
+    sp.S = fp.S;
+    sp.ks = a.hidden / fp.S;
+    sp.partials = fp.bytes ? static_cast<float *>(ws) : nullptr;
+    const int nch = sp.ks / FDL_FC_KC;
+    const dim3 grid(fp.G * fp.S), block(FDL_FC_SNW * 64);
+    switch (nch) {
+      case 4:
+        hipLaunchKernelGGL((qkv_splitk_kernel<kSplitNTW, kSplitNGW, FDL_FC_NST, 4, FDL_FC_SNW, FDL_FC_KC>), grid, block, 0,
+                           s, a, sp);
+        break;
+      case 8:
+        hipLaunchKernelGGL((qkv_splitk_kernel<kSplitNTW, kSplitNGW, FDL_FC_NST, 8, FDL_FC_SNW, FDL_FC_KC>), grid, block, 0,
+                           s, a, sp);
+        break;
+      case 16:
+        hipLaunchKernelGGL((qkv_splitk_kernel<kSplitNTW, kSplitNGW, FDL_FC_NST, 16, FDL_FC_SNW, FDL_FC_KC>), grid, block,
+                           0, s, a, sp);
+        break;
+      default:
+        hipLaunchKernelGGL((qkv_splitk_kernel<kSplitNTW, kSplitNGW, FDL_FC_NST, 0, FDL_FC_SNW, FDL_FC_KC>), grid, block, 0,
+                           s, a, sp);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || fp.S == 1) return e;
+    const int items = fp.G * a.rows * (kSplitCW / 2);
+    hipLaunchKernelGGL((qkv_reduce_kernel<kSplitCW>), dim3((items + 255) / 256), dim3(256), 0, s,
+                       a, sp);
+    return hipGetLastError();
+  }
   constexpr int MT = 4, NT = FDL_FC_NT, NW = FDL_FC_NW, DEPTH = FDL_FC_DEPTH;
   const int total_pairs = 3 * a.c.H * (a.c.D / 2);
   dim3 grid((total_pairs + 8 * NT - 1) / (8 * NT), (a.rows + 16 * MT - 1) / (16 * MT));

@@ -24,7 +24,8 @@ struct FlashCacheArgs {
   int64_t *slot_mapping;
 };
 
-hipError_t launch_flash_cache(const FlashCacheArgs &a, hipStream_t s);
+size_t flash_cache_workspace_bytes(int rows, int hidden, int H, int D);
+hipError_t launch_flash_cache(const FlashCacheArgs &a, void *ws, size_t ws_bytes, hipStream_t s);
 
 struct AttnPlan {
   int row_tiles;      // ceil(max_rows_per_seq / 64)

@@ -33,17 +33,40 @@ __device__ __forceinline__ int block_excl_count(bool flag, int &total, int *sh) 
   return before + in_wave;
 }
 
+// Inclusive prefix sum over the 256 threads of the block (thread order).
+__device__ __forceinline__ unsigned block_incl_sum(unsigned v, unsigned *sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) sh[wave] = v;
+  __syncthreads();
+  unsigned before = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) before += w < wave ? sh[w] : 0u;
+  __syncthreads();
+  return v + before;
+}
+
 // One workgroup (256 threads) per sequence.  Masses are non-negative, so their
 // fp32 bit patterns order like the values: a 4-pass radix select over 8-bit
-// digits finds the bit pattern T of the B-th largest mass; every key above T is
-// taken, and keys equal to T are taken in index order until B are chosen.  A
-// final in-order scan writes the chosen indices ascending.
+// digits (LDS histogram, then a parallel scan from the top digit down) finds
+// the bit pattern T of the B-th largest mass; every key above T is taken, and
+// keys equal to T are taken in index order until B are chosen.  A final
+// in-order scan writes the chosen indices ascending.  Rows of up to kCached
+// keys are held in LDS across the passes.
+constexpr int kCached = 8192;
+
 __global__ __launch_bounds__(256) void topb_kernel(const float *mass, int stride,
                                                    const int32_t *kv_len, int topb,
                                                    int32_t *out) {
   __shared__ unsigned hist[256];
   __shared__ unsigned s_digit, s_remaining;
+  __shared__ unsigned shs[4];
   __shared__ int sh[4];
+  __shared__ uint32_t cache[kCached];
   const int b = blockIdx.x;
   const int L = kv_len[b];
   const uint32_t *mb = reinterpret_cast<const uint32_t *>(mass + (size_t)b * stride);
@@ -53,6 +76,10 @@ __global__ __launch_bounds__(256) void topb_kernel(const float *mass, int stride
     for (int k = threadIdx.x; k < topb; k += blockDim.x) ob[k] = k < L ? k : -1;
     return;
   }
+  const bool cached = L <= kCached;
+  if (cached)
+    for (int k = threadIdx.x; k < L; k += blockDim.x) cache[k] = mb[k];
+  auto key = [&](int k) -> uint32_t { return cached ? cache[k] : mb[k]; };
 
   uint32_t prefix = 0, pmask = 0;
   unsigned remaining = (unsigned)topb;
@@ -61,19 +88,16 @@ __global__ __launch_bounds__(256) void topb_kernel(const float *mass, int stride
     hist[threadIdx.x] = 0;
     __syncthreads();
     for (int k = threadIdx.x; k < L; k += blockDim.x) {
-      const uint32_t u = mb[k];
+      const uint32_t u = key(k);
       if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      unsigned cum = 0;
-      int d = 255;
-      for (; d > 0; --d) {
-        if (cum + hist[d] >= remaining) break;
-        cum += hist[d];
-      }
-      s_digit = (unsigned)d;
-      s_remaining = remaining - cum;
+    // Thread t looks at digit 255 - t; cum = number of candidates with digit >= it.
+    const unsigned c = hist[255 - threadIdx.x];
+    const unsigned cum = block_incl_sum(c, shs);
+    if (cum >= remaining && cum - c < remaining) {
+      s_digit = 255u - threadIdx.x;
+      s_remaining = remaining - (cum - c);
     }
     __syncthreads();
     prefix |= s_digit << shift;
@@ -86,7 +110,7 @@ __global__ __launch_bounds__(256) void topb_kernel(const float *mass, int stride
   int base_sel = 0, base_eq = 0;
   for (int c0 = 0; c0 < L; c0 += blockDim.x) {
     const int k = c0 + threadIdx.x;
-    const uint32_t u = k < L ? mb[k] : 0u;
+    const uint32_t u = k < L ? key(k) : 0u;
     const bool gt = k < L && u > T;
     const bool eq = k < L && u == T;
     int eq_total, sel_total;
@@ -96,6 +120,7 @@ __global__ __launch_bounds__(256) void topb_kernel(const float *mass, int stride
     if (sel && pos < topb) ob[pos] = k;
     base_eq += eq_total;
     base_sel += sel_total;
+    if (base_sel >= topb) break;
   }
 }
 

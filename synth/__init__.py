@@ -350,6 +350,16 @@ def small_d64_many_rows(materialize=True) -> Workload:
                  materialize=materialize)
 
 
+def small_splitk(materialize=True) -> Workload:
+    """Few rows (40) on a narrow layer (hidden 1024, 2 x 128) so the projection
+    splits its reduction across workgroups; batch 2, lengths 96 and 70."""
+    g = rng(14, 0, STREAM_POS)
+    specs = [SeqSpec(kv_len=96, window=(64, 16), tracked=distinct(g, 0, 64, 8)),
+             SeqSpec(kv_len=70, window=(40, 8), tracked=distinct(g, 0, 40, 8))]
+    return build("small_splitk_h1024", 14, 1024, 2, 128, 32, 1.0e4, specs, topb=8,
+                 materialize=materialize)
+
+
 WORKLOADS = {
     "tiny_h256_l128": tiny_h256,
     "llada8b_b1_l768": llada8b_b1,
@@ -358,4 +368,5 @@ WORKLOADS = {
     "small_ragged_b5": small_ragged,
     "small_verify_b3": small_verify,
     "small_d64_rows150": small_d64_many_rows,
+    "small_splitk_h1024": small_splitk,
 }

@@ -29,7 +29,8 @@ def lib():
 def test_header_lists_the_four_calls():
     names = declared_functions()
     for n in ("flash_cache_step", "scheduled_attention", "track_topb", "verify_accept",
-              "fdl_attention_workspace_bytes", "fdl_status_string", "fdl_last_hip_error",
+              "fdl_attention_workspace_bytes", "fdl_flash_cache_workspace_bytes",
+              "fdl_status_string", "fdl_last_hip_error",
               "fdl_version"):
         assert n in names, names
 
@@ -54,8 +55,10 @@ def _cache(h=4, d=64, bs=32, nb=4, mb=4, k=0x1000, v=0x2000, bt=0x3000):
 
 def test_flash_cache_step_validation(lib):
     fake = 0x10000
-    args = lambda c, hid=256, batch=1, rows=4, base=1e4: lib.flash_cache_step(
-        ctypes.byref(c), fake, hid, fake, batch, rows, fake, fake, fake, base, fake, None, None)
+    ws = lib.fdl_flash_cache_workspace_bytes(4, 256, 4, 64)
+    args = lambda c, hid=256, batch=1, rows=4, base=1e4, wsb=ws: lib.flash_cache_step(
+        ctypes.byref(c), fake, hid, fake, batch, rows, fake, fake, fake, base, fake, None, fake,
+        wsb, None)
     assert args(_cache(d=96)) == _lib.FDL_EUNSUPPORTED
     assert args(_cache(bs=48)) == _lib.FDL_EUNSUPPORTED
     assert args(_cache(), hid=200) == _lib.FDL_EUNSUPPORTED
@@ -70,9 +73,19 @@ def test_flash_cache_step_validation(lib):
     assert args(_cache(), rows=0) == _lib.FDL_OK
     assert args(_cache(), batch=0) == _lib.FDL_OK
     assert lib.flash_cache_step(ctypes.byref(_cache()), None, 256, fake, 1, 3, fake, fake, fake,
-                                1e4, fake, None, None) == _lib.FDL_EINVAL
+                                1e4, fake, None, fake, ws, None) == _lib.FDL_EINVAL
     assert lib.flash_cache_step(None, fake, 256, fake, 1, 3, fake, fake, fake, 1e4, fake, None,
-                                None) == _lib.FDL_EINVAL
+                                fake, ws, None) == _lib.FDL_EINVAL
+    # a narrow layer with few rows splits its reduction and needs scratch
+    ws2 = lib.fdl_flash_cache_workspace_bytes(40, 1024, 2, 128)
+    assert ws2 > 0
+    c2 = _cache(h=2, d=128)
+    assert lib.flash_cache_step(ctypes.byref(c2), fake, 1024, fake, 1, 40, fake, fake, fake, 1e4,
+                                fake, None, fake, ws2 - 1, None) == _lib.FDL_EWORKSPACE
+    assert lib.flash_cache_step(ctypes.byref(c2), fake, 1024, fake, 1, 40, fake, fake, fake, 1e4,
+                                fake, None, None, ws2, None) == _lib.FDL_EWORKSPACE
+    assert lib.fdl_flash_cache_workspace_bytes(65, 4096, 32, 128) == 0   # row-strip kernel
+    assert lib.fdl_flash_cache_workspace_bytes(-1, 4096, 32, 128) == 0
 
 
 def test_attention_validation_and_workspace(lib):
