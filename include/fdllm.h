@@ -26,7 +26,8 @@
  *     as for any paged-attention kernel; the caller validates them.
  *
  * Supported shapes: head_dim in {64, 128}; block_size in {32, 64, 128, 256};
- * hidden a multiple of 128 and at most 32768; num_heads * head_dim <= 16384.
+ * hidden a multiple of 128 and at most 32768; num_heads * head_dim <= 16384;
+ * at most 1024 cache pages per sequence (max_kv_len <= 1024 * block_size).
  */
 #ifndef FDLLM_H
 #define FDLLM_H

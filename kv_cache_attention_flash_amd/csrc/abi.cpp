@@ -124,6 +124,7 @@ int scheduled_attention(const fdl_kv_cache *cache, const void *q, int32_t batch,
   if (batch < 0 || num_rows < 0 || max_kv_len < 0 || max_rows_per_seq < 0) return FDL_EINVAL;
   if (!(softmax_scale >= 0.f) || !std::isfinite(softmax_scale)) return FDL_EINVAL;
   if ((long)max_kv_len > (long)cache->max_blocks_per_seq * cache->block_size) return FDL_EINVAL;
+  if ((max_kv_len + cache->block_size - 1) / cache->block_size > 1024) return FDL_EUNSUPPORTED;
   if (mass && mass_stride < max_kv_len) return FDL_EINVAL;
   if (mass && mass_stride <= 0) return FDL_EINVAL;
   if (batch == 0) return FDL_OK;

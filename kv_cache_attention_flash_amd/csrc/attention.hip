@@ -10,21 +10,23 @@
 //
 // Pass 1 (attn_fwd): one workgroup per (sequence, 64-row tile, head, KV split);
 // 4 waves, each owning 16 query rows.  Keys stream in 32-slot tiles: the tile's
-// K (row-major) and V (transposed) are staged in LDS and shared by the 4 waves.
+// K (row-major) and V (transposed) are staged in double-buffered LDS and shared
+// by the 4 waves; the next tile's loads are in flight while a tile is used.
 // Per wave S^T = K Q^T (v_mfma_f32_16x16x32_bf16, keys along M) so that each
 // lane holds one query row: row maxima and sums are in-lane plus two shuffles,
 // and the fp32 probabilities convert in-register into the B operand of
 // O^T += V^T P^T.  The K rows feeding the two 16-key M tiles are permuted so
 // that lane group g ends up holding the 8 consecutive keys 8g..8g+7, which
 // makes each V^T operand one 16-byte LDS read.  Online softmax in base 2.
-// With several KV splits the unnormalised partials meet in attn_merge (fixed
-// split order).
+// With several KV splits the unnormalised partials are merged in a fixed split
+// order: by attn_merge, or, when the mass is requested, by attn_finish.
 //
 // Mass: m[b][j] = sum_h sum_r exp(s_rj - LSE_r) needs every row's final
 // log-sum-exp, known only after all keys, so the mass is a second pass over K
-// (attn_mass) using the LSE of pass 1; per-(sequence, head) partial sums are
-// added over heads in head order by mass_head_reduce.  Nothing uses floating
-// atomics: results are bitwise reproducible.
+// (attn_mass) that first forms each row's LSE from the pass-1 maxima and
+// normalisers; per-(sequence, head) partial sums are added over heads in head
+// order by attn_finish, which also merges the split outputs.
+// Nothing uses floating atomics: results are bitwise reproducible.
 #include "device_common.h"
 #include "internal.h"
 
@@ -54,46 +56,108 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnArgs &a, int b) {
   return si;
 }
 
-// May local row t of a sequence see slot j?
-__device__ __forceinline__ bool visible(const SeqInfo &si, int t, int j) {
-  if (j >= si.L) return false;
-  if (si.wl == 0) return true;
-  if (t < si.wl) {
-    bool ctx = j < si.d0 && (j < si.w0 || j >= si.w0 + si.wl);
-    return ctx || (j >= si.d0 && j <= si.d0 + t);
+// The slots local row t of a sequence may see, as intervals: slot j is visible
+// iff (j < lim and not x0 <= j < x1) or y0 <= j <= y1.
+//   plain row:        [0, L)
+//   draft row i:      context [0, min(d0, L)) minus the window [w0, w0 + W),
+//                     plus the draft slots d0 .. d0 + i (causal)
+//   mask row:         [0, min(d0, L))  (context and the whole window)
+//   missing row:      nothing
+struct Vis {
+  int lim, x0, x1, y0, y1;
+  __device__ __forceinline__ bool operator()(int j) const {
+    return (j < lim && (j < x0 || j >= x1)) || (j >= y0 && j <= y1);
   }
-  return j < si.d0;
-}
+};
 
-// Stage one 32-key tile of head h: K as [key][D + 8], V transposed as [D][KT + 8].
-template <int D>
-__device__ __forceinline__ void stage_tile(const AttnArgs &a, int b, int h, int key0,
-                                           uint16_t (*klds)[D + 8], uint16_t (*vt)[KT + 8],
-                                           bool want_v) {
-  const int bs = a.c.bs;
-  const int page = a.c.block_table[(size_t)b * a.c.max_blocks + key0 / bs];
-  const size_t base = (((size_t)page * a.c.H + h) * bs + (key0 % bs)) * D;
-  constexpr int CH = D / 8;            // 16-byte chunks per key
-  constexpr int N = KT * CH;           // chunks per tile
-  for (int c = threadIdx.x; c < N; c += blockDim.x) {
-    const int key = c / CH, dc = c % CH;
-    u32x4 kv = ld16(a.c.k + base + (size_t)c * 8);
-    st16(&klds[key][dc * 8], kv);
-    if (want_v) {
-      u32x4 vv = ld16(a.c.v + base + (size_t)c * 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt[dc * 8 + 2 * e][key] = (uint16_t)(vv[e] & 0xffffu);
-        vt[dc * 8 + 2 * e + 1][key] = (uint16_t)(vv[e] >> 16);
-      }
+__device__ __forceinline__ Vis row_vis(const SeqInfo &si, int t, bool row_ok) {
+  Vis v{0, 0, 0, 1, 0};
+  if (!row_ok) return v;
+  if (si.wl == 0) {
+    v.lim = si.L;
+  } else {
+    v.lim = min(si.d0, si.L);
+    if (t < si.wl) {
+      v.x0 = si.w0;
+      v.x1 = si.w0 + si.wl;
+      v.y0 = si.d0;
+      v.y1 = min(si.d0 + t, si.L - 1);
     }
   }
+  return v;
+}
+
+// One 32-key tile of head h moves global -> registers -> LDS, K and V both
+// row-major ([key][D + pad]), by one group of 256 threads (NCH 16-byte chunks
+// of K and of V per thread).
+template <int D>
+struct Tile {
+  static constexpr int CH = D / 8;                  // 16-byte chunks per key
+  static constexpr int NCH = KT * CH / 256;         // chunks per thread
+  u32x4 k[NCH], v[NCH];
+};
+template <int D> constexpr int kKPad = D + 8;   // K row stride (elements)
+template <int D> constexpr int kVPad = D + 16;  // V row stride: conflict-free transposed reads
+
+// Physical pages of the tiles a workgroup visits, staged once in LDS so that a
+// tile's address never waits on a block-table load.
+constexpr int kMaxPages = 1024;
+
+__device__ __forceinline__ void stage_pages(const AttnArgs &a, int b, int tb, int te, int *s_page) {
+  const int bs = a.c.bs;
+  const int p0 = tb * KT / bs, p1 = te > tb ? ((te * KT - 1) / bs) + 1 : p0;
+  for (int i = threadIdx.x; i < p1 - p0; i += blockDim.x)
+    s_page[i] = a.c.block_table[(size_t)b * a.c.max_blocks + p0 + i];
+}
+
+template <int D>
+__device__ __forceinline__ void load_tile(Tile<D> &t, const AttnArgs &a, const int *s_page, int tb,
+                                          int h, int key0, bool want_v, int gtid) {
+  const int bs = a.c.bs;
+  const int page = s_page[key0 / bs - tb * KT / bs];
+  const size_t base = (((size_t)page * a.c.H + h) * bs + (key0 % bs)) * D;
+#pragma unroll
+  for (int i = 0; i < Tile<D>::NCH; ++i) {
+    const int c = gtid + 256 * i;
+    t.k[i] = ld16(a.c.k + base + (size_t)c * 8);
+    if (want_v) t.v[i] = ld16(a.c.v + base + (size_t)c * 8);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(const Tile<D> &t, uint16_t (*klds)[kKPad<D>],
+                                           uint16_t (*vlds)[kVPad<D>], bool want_v, int gtid) {
+#pragma unroll
+  for (int i = 0; i < Tile<D>::NCH; ++i) {
+    const int c = gtid + 256 * i;
+    const int key = c / Tile<D>::CH, dc = c % Tile<D>::CH;
+    st16(&klds[key][dc * 8], t.k[i]);
+    if (want_v) st16(&vlds[key][dc * 8], t.v[i]);
+  }
+}
+
+// V^T operand of O^T += V^T P^T for features 16*dm .. 16*dm+15: lane l needs
+// keys 8g .. 8g+7 (g = l / 16) of feature 16*dm + l % 16.  ds_read_tr16_b64
+// gives lane i of a 16-lane group element k = position i % 4 of the 8-byte
+// chunk addressed by lane 4k + i / 4; addressing V[kb + a/4][d0 + 4*(a%4)] from
+// lane a therefore hands lane i the keys kb .. kb+3 of feature d0 + i.
+template <int D>
+__device__ __forceinline__ u32x4 vt_operand(uint16_t (*vlds)[kVPad<D>], int dm, int lane) {
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const int g = lane >> 4, i = lane & 15;
+  const uint16_t *p0 = &vlds[8 * g + (i >> 2)][16 * dm + 4 * (i & 3)];
+  const uint16_t *p1 = &vlds[8 * g + 4 + (i >> 2)][16 * dm + 4 * (i & 3)];
+  bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p0));
+  bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p1));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
 
 // S^T tile (32 keys x 16 rows) for one wave: s[mt][e] is key 8g + 4mt + e for
 // query row (lane & 15).
 template <int D>
-__device__ __forceinline__ void scores(const uint16_t (*klds)[D + 8], const u32x4 *qf,
+__device__ __forceinline__ void scores(const uint16_t (*klds)[kKPad<D>], const u32x4 *qf,
                                        int lane, f32x4 s[2]) {
   const int g = lane >> 4, j = lane & 15;
 #pragma unroll
@@ -110,9 +174,23 @@ __device__ __forceinline__ void scores(const uint16_t (*klds)[D + 8], const u32x
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
-  __shared__ uint16_t klds[KT][D + 8];
-  __shared__ uint16_t vt[D][KT + 8];
+__device__ __forceinline__ void load_q(const AttnArgs &a, int r, int h, bool ok, int g,
+                                       u32x4 *qf) {
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+    qf[ks] = ok ? ld16(a.q + ((size_t)r * a.c.H + h) * D + 32 * ks + 8 * g)
+                : u32x4{0u, 0u, 0u, 0u};
+}
+
+// Pass 1.  8 waves: key group kg = wave / 4 takes the unit's even or odd
+// tiles, row group wave % 4 owns 16 query rows; the two key groups keep their
+// own online-softmax state and are combined through LDS at the end (group 0
+// first), so two waves per SIMD hide each other's latency.
+template <int D>
+__global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
+  constexpr int NPF = 2;  // tiles in flight per key group
+  __shared__ uint16_t klds[2][2][KT][kKPad<D>];
+  __shared__ uint16_t vlds[2][2][KT][kVPad<D>];
 
   int u = blockIdx.x;
   const int split = u % p.splits; u /= p.splits;
@@ -124,79 +202,125 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
   if (t0 >= si.nrows) return;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kg = wave >> 2, wr = wave & 3, gtid = threadIdx.x & 255;
   const int g = lane >> 4, j = lane & 15;
-  const int t = t0 + wave * 16 + j;  // local row of this lane
+  const int t = t0 + wr * 16 + j;  // local row of this lane
   const bool row_ok = t < si.nrows;
   const int r = si.r0 + (row_ok ? t : 0);
-
-  u32x4 qf[D / 32];
-#pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
-    qf[ks] = row_ok ? ld16(a.q + ((size_t)r * a.c.H + h) * D + 32 * ks + 8 * g)
-                    : u32x4{0u, 0u, 0u, 0u};
+  const Vis vis = row_vis(si, t, row_ok);
 
   const int tiles = (si.L + KT - 1) / KT;
   const int tps = (tiles + p.splits - 1) / p.splits;
   const int tb = split * tps, te = min(tiles, tb + tps);
+  const int niter = (te - tb + 1) / 2;  // iterations per key group (group 1 may idle in the last)
+
+  __shared__ int s_page[kMaxPages];
+  stage_pages(a, b, tb, te, s_page);
+  lds_barrier();
+  // Loads are unconditional (tile index clamped to the unit's last tile; the
+  // repeats hit L2) so the compiler keeps the other stage in flight.
+  const int tlast = max(te - 1, tb);
+  Tile<D> pf[NPF];
+  if (te > tb) {
+#pragma unroll
+    for (int i = 0; i < NPF; ++i)
+      load_tile<D>(pf[i], a, s_page, tb, h, min(tb + kg + 2 * i, tlast) * KT, true, gtid);
+  }
+  u32x4 qf[D / 32];
+  load_q<D>(a, r, h, row_ok, g, qf);
 
   f32x4 o[D / 16];
 #pragma unroll
   for (int dm = 0; dm < D / 16; ++dm) o[dm] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = kNegInf, l = 0.f;
 
-  for (int tile = tb; tile < te; ++tile) {
-    const int key0 = tile * KT;
-    stage_tile<D>(a, b, h, key0, klds, vt, true);
-    __syncthreads();
-    f32x4 s[2];
-    scores<D>(klds, qf, lane, s);
-    float v[8];
-    float tmax = kNegInf;
+  for (int it0 = 0; it0 < niter; it0 += NPF) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int ii = 0; ii < NPF; ++ii) {
+      const int it = it0 + ii;
+      if (it >= niter) break;
+      const int tile = tb + kg + 2 * it;
+      const bool have = tile < te;
+      const int buf = ii & 1;
+      store_tile<D>(pf[ii], klds[kg][buf], vlds[kg][buf], true, gtid);
+      load_tile<D>(pf[ii], a, s_page, tb, h, min(tile + 2 * NPF, tlast) * KT, true, gtid);
+      lds_barrier();
+      if (!have) continue;
+      const int key0 = tile * KT;
+      f32x4 s[2];
+      scores<D>(klds[kg][buf], qf, lane, s);
+      float v[8];
+      float tmax = kNegInf;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int jj = key0 + 8 * g + 4 * mt + e;
-        const bool vis = row_ok && visible(si, t, jj);
-        const float x = vis ? s[mt][e] * a.scale_log2 : kNegInf;
-        v[mt * 4 + e] = x;
-        tmax = fmaxf(tmax, x);
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int jj = key0 + 8 * g + 4 * mt + e;
+          const float x = vis(jj) ? s[mt][e] * a.scale_log2 : kNegInf;
+          v[mt * 4 + e] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+      const float mnew = fmaxf(m, tmax);
+      float pv[8];
+      float alpha = 1.f, rs = 0.f;
+      if (mnew == kNegInf) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = 0.f;
+      } else {
+        alpha = fast_exp2(m - mnew);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = v[e] == kNegInf ? 0.f : fast_exp2(v[e] - mnew);
+          rs += pv[e];
+        }
       }
-    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-    const float mnew = fmaxf(m, tmax);
-    float pv[8];
-    float alpha = 1.f, rs = 0.f;
-    if (mnew == kNegInf) {
+      rs += shfl_xor(rs, 16);
+      rs += shfl_xor(rs, 32);
+      l = l * alpha + rs;
+      m = mnew;
+      u32x4 pb;
+      pb[0] = pack_bf16x2(pv[0], pv[1]);
+      pb[1] = pack_bf16x2(pv[2], pv[3]);
+      pb[2] = pack_bf16x2(pv[4], pv[5]);
+      pb[3] = pack_bf16x2(pv[6], pv[7]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = 0.f;
-    } else {
-      alpha = exp2f(m - mnew);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pv[e] = v[e] == kNegInf ? 0.f : exp2f(v[e] - mnew);
-        rs += pv[e];
+      for (int dm = 0; dm < D / 16; ++dm) {
+        o[dm] *= alpha;
+        o[dm] = mfma16(vt_operand<D>(vlds[kg][buf], dm, lane), pb, o[dm]);
       }
     }
-    rs += shfl_xor(rs, 16);
-    rs += shfl_xor(rs, 32);
-    l = l * alpha + rs;
-    m = mnew;
-    u32x4 pb;
-    pb[0] = pack_bf16x2(pv[0], pv[1]);
-    pb[1] = pack_bf16x2(pv[2], pv[3]);
-    pb[2] = pack_bf16x2(pv[4], pv[5]);
-    pb[3] = pack_bf16x2(pv[6], pv[7]);
-#pragma unroll
-    for (int dm = 0; dm < D / 16; ++dm) {
-      o[dm] *= alpha;
-      u32x4 vf = ld16(&vt[16 * dm + j][8 * g]);
-      o[dm] = mfma16(vf, pb, o[dm]);
-    }
-    __syncthreads();
   }
 
-  if (!row_ok) return;
+  // Combine the two key groups (group 1's state through LDS, reusing the tiles).
+  lds_barrier();
+  float *mo = reinterpret_cast<float *>(&klds[0][0][0][0]);  // [4 row groups][16 rows][D]
+  float *mml = mo + 64 * D;                                   // [64 rows][2]
+  static_assert((64 * D + 128) * 4 <= (int)sizeof(klds), "merge scratch");
+  const int rl = wr * 16 + j;
+  if (kg == 1) {
+#pragma unroll
+    for (int dm = 0; dm < D / 16; ++dm)
+      *reinterpret_cast<f32x4 *>(&mo[rl * D + 16 * dm + 4 * g]) = o[dm];
+    if (g == 0) {
+      mml[2 * rl] = m;
+      mml[2 * rl + 1] = l;
+    }
+  }
+  lds_barrier();
+  if (kg == 1 || !row_ok) return;
+  {
+    const float m1 = mml[2 * rl], l1 = mml[2 * rl + 1];
+    const float mx = fmaxf(m, m1);
+    const float f0 = m == kNegInf ? 0.f : exp2f(m - mx);
+    const float f1 = m1 == kNegInf ? 0.f : exp2f(m1 - mx);
+    l = l * f0 + l1 * f1;
+    m = mx;
+#pragma unroll
+    for (int dm = 0; dm < D / 16; ++dm)
+      o[dm] = o[dm] * f0 + *reinterpret_cast<const f32x4 *>(&mo[rl * D + 16 * dm + 4 * g]) * f1;
+  }
   // o[dm][e] = O[row][16 dm + 4 g + e]
   if (p.splits == 1) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -224,43 +348,64 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
   }
 }
 
-// Merge KV-split partials: one thread per (row, head, 4 features).
+// Combine the KV-split partials of row r, head h: the global maximum, the
+// rescaled normaliser and, when asked, the DW output features starting at d0.
+template <int DW>
+__device__ __forceinline__ float merge_row(const AttnArgs &a, const AttnPlan &p, size_t rh,
+                                           int D, int d0, float *out_or_null) {
+  const float *po = reinterpret_cast<const float *>(a.ws + p.off_part_o);
+  const float *pml = reinterpret_cast<const float *>(a.ws + p.off_part_ml);
+  const size_t stride = (size_t)a.rows * a.c.H;
+  float mx = kNegInf;
+#pragma unroll 8
+  for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, pml[2 * (s * stride + rh)]);
+  f32x4 acc[DW / 4];
+#pragma unroll
+  for (int i = 0; i < DW / 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  if (mx != kNegInf) {
+#pragma unroll 4
+    for (int s = 0; s < p.splits; ++s) {
+      const size_t k = s * stride + rh;
+      const float ms = pml[2 * k];
+      const float f = ms == kNegInf ? 0.f : exp2f(ms - mx);
+      l += pml[2 * k + 1] * f;
+      if (out_or_null) {
+#pragma unroll
+        for (int i = 0; i < DW / 4; ++i)
+          acc[i] += *reinterpret_cast<const f32x4 *>(po + k * D + d0 + 4 * i) * f;
+      }
+    }
+  }
+  if (out_or_null) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int i = 0; i < DW / 4; ++i)
+      *reinterpret_cast<f32x4 *>(out_or_null + rh * D + d0 + 4 * i) = acc[i] * inv;
+  }
+  return l > 0.f ? mx + log2f(l) : kNegInf;
+}
+
+// Merge KV-split partials (no mass requested): one thread per (row, head, 4 features).
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, AttnPlan p) {
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t rh = idx / (D / 4);
   const int d4 = (int)(idx % (D / 4)) * 4;
   if (rh >= (size_t)a.rows * a.c.H) return;
-  const float *po = reinterpret_cast<const float *>(a.ws + p.off_part_o);
-  const float *pml = reinterpret_cast<const float *>(a.ws + p.off_part_ml);
-  const size_t stride = (size_t)a.rows * a.c.H;
-  float mx = kNegInf;
-  for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, pml[2 * (s * stride + rh)]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float l = 0.f;
-  if (mx != kNegInf) {
-    for (int s = 0; s < p.splits; ++s) {
-      const size_t k = s * stride + rh;
-      const float ms = pml[2 * k];
-      if (ms == kNegInf) continue;
-      const float f = exp2f(ms - mx);
-      l += pml[2 * k + 1] * f;
-      acc += *reinterpret_cast<const f32x4 *>(po + k * D + d4) * f;
-    }
-  }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  *reinterpret_cast<f32x4 *>(a.out + rh * D + d4) = acc * inv;
-  if (p.mass_splits && d4 == 0) {
-    float *lse = reinterpret_cast<float *>(a.ws + p.off_lse);
-    lse[rh] = l > 0.f ? mx + log2f(l) : kNegInf;
-  }
+  merge_row<4>(a, p, rh, D, d4, a.out);
 }
 
-// Attention mass pass: one workgroup per (sequence, head, key chunk).
+// Attention mass pass: one workgroup per (sequence, head, key chunk).  Each
+// lane first forms its row's LSE (from pass 1 directly, or by combining the
+// KV-split maxima and normalisers, loaded with the first K tile), then K
+// tiles stream through double-buffered LDS and P = exp2(s - LSE) is summed over
+// the rows: in-wave by a reduce-scatter over the 16 row lanes, across the
+// 4 waves in wave order.
 template <int D>
 __global__ __launch_bounds__(256) void attn_mass_kernel(AttnArgs a, AttnPlan p) {
   constexpr int MAXK = 32 * KT;  // keys per chunk (bounded by the host plan)
-  __shared__ uint16_t klds[KT][D + 8];
+  __shared__ uint16_t klds[2][KT][kKPad<D>];
   __shared__ float wsum[4][KT];
   __shared__ float macc[MAXK];
 
@@ -272,41 +417,53 @@ __global__ __launch_bounds__(256) void attn_mass_kernel(AttnArgs a, AttnPlan p) 
   const int tiles = (si.L + KT - 1) / KT;
   const int tpc = (tiles + p.mass_splits - 1) / p.mass_splits;
   const int tb = chunk * tpc, te = min(tiles, tb + tpc);
+  const int nrt = (si.nrows + 63) / 64;
   if (tb >= te) return;
-  const int nkeys = (te - tb) * KT;
+  const int nkeys = max(0, te - tb) * KT;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, j = lane & 15;
-  const float *lse = reinterpret_cast<const float *>(a.ws + p.off_lse);
+  const float *lse_ws = reinterpret_cast<const float *>(a.ws + p.off_lse);
 
+  __shared__ int s_page[kMaxPages];
+  stage_pages(a, b, tb, te, s_page);
   for (int k = threadIdx.x; k < nkeys; k += blockDim.x) macc[k] = 0.f;
+  lds_barrier();
 
-  const int nrt = (si.nrows + 63) / 64;
   for (int rt = 0; rt < nrt; ++rt) {
     const int t = rt * 64 + wave * 16 + j;
     const bool row_ok = t < si.nrows;
     const int r = si.r0 + (row_ok ? t : 0);
-    u32x4 qf[D / 32];
+    const size_t rh = (size_t)r * a.c.H + h;
+    const Vis vis = row_vis(si, t, row_ok);
+    Tile<D> pf[2];
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      qf[ks] = row_ok ? ld16(a.q + ((size_t)r * a.c.H + h) * D + 32 * ks + 8 * g)
-                      : u32x4{0u, 0u, 0u, 0u};
-    const float lr = row_ok ? lse[(size_t)r * a.c.H + h] : kNegInf;
+    for (int i = 0; i < 2; ++i)
+      load_tile<D>(pf[i], a, s_page, tb, h, min(tb + i, te - 1) * KT, false, threadIdx.x);
+    u32x4 qf[D / 32];
+    load_q<D>(a, r, h, row_ok, g, qf);
+    float lr = kNegInf;
+    if (row_ok) lr = p.splits == 1 ? lse_ws[rh] : merge_row<4>(a, p, rh, D, 0, nullptr);
 
-    for (int tile = tb; tile < te; ++tile) {
+    for (int tile0 = tb; tile0 < te; tile0 += 2) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int tile = tile0 + ii;
+      if (tile >= te) break;
+      const int buf = ii;
+      store_tile<D>(pf[ii], klds[buf], nullptr, false, threadIdx.x);
+      load_tile<D>(pf[ii], a, s_page, tb, h, min(tile + 2, te - 1) * KT, false, threadIdx.x);
+      lds_barrier();
       const int key0 = tile * KT;
-      stage_tile<D>(a, b, h, key0, klds, nullptr, false);
-      __syncthreads();
       f32x4 s[2];
-      scores<D>(klds, qf, lane, s);
+      scores<D>(klds[buf], qf, lane, s);
       float pv[8];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int jj = key0 + 8 * g + 4 * mt + e;
-          const bool vis = row_ok && lr != kNegInf && visible(si, t, jj);
-          pv[mt * 4 + e] = vis ? exp2f(s[mt][e] * a.scale_log2 - lr) : 0.f;
+          pv[mt * 4 + e] = (lr != kNegInf && vis(jj)) ? fast_exp2(s[mt][e] * a.scale_log2 - lr) : 0.f;
         }
       // Reduce over the 16 rows of the wave (lanes sharing g): reduce-scatter.
       const int b3 = (j >> 3) & 1, b2 = (j >> 2) & 1, b1 = (j >> 1) & 1;
@@ -334,14 +491,15 @@ __global__ __launch_bounds__(256) void attn_mass_kernel(AttnArgs a, AttnPlan p) 
       const float other = shfl_xor(q1, 1);
       const float tot = (j & 1) ? other + q1 : q1 + other;
       if ((j & 1) == 0) wsum[wave][8 * g + 4 * b3 + 2 * b2 + b1] = tot;
-      __syncthreads();
+      lds_barrier();
       if (threadIdx.x < KT) {
         const int k = threadIdx.x;
         const float sum = ((wsum[0][k] + wsum[1][k]) + wsum[2][k]) + wsum[3][k];
         macc[(tile - tb) * KT + k] += sum;
       }
-      __syncthreads();
     }
+    }
+    lds_barrier();
   }
   float *mp = reinterpret_cast<float *>(a.ws + p.off_mass_part) +
               ((size_t)b * a.c.H + h) * a.mass_stride;
@@ -351,17 +509,36 @@ __global__ __launch_bounds__(256) void attn_mass_kernel(AttnArgs a, AttnPlan p) 
   }
 }
 
-// mass[b][j] = sum over heads (in head order) of the per-head partials.
-__global__ __launch_bounds__(256) void mass_head_reduce_kernel(AttnArgs a, AttnPlan p) {
-  const int b = blockIdx.y;
-  const int jj = blockIdx.x * blockDim.x + threadIdx.x;
+// Last launch of a mass-requesting call: blocks [0, nb_mass) add the per-head
+// partial masses in head order (mass[b][j]; the loads of 32 heads are issued
+// before their sum), blocks after that merge the KV-split partial outputs
+// (one thread per row, head and 4 features), when there are splits.
+template <int D>
+__global__ __launch_bounds__(256) void attn_finish_kernel(AttnArgs a, AttnPlan p, int nb_mass) {
+  if ((int)blockIdx.x >= nb_mass) {
+    const size_t idx = (size_t)(blockIdx.x - nb_mass) * blockDim.x + threadIdx.x;
+    const size_t rh = idx / (D / 4);
+    const int d4 = (int)(idx % (D / 4)) * 4;
+    if (rh < (size_t)a.rows * a.c.H) merge_row<4>(a, p, rh, D, d4, a.out);
+    return;
+  }
+  const int per_b = (a.mass_stride + 255) / 256;
+  const int b = blockIdx.x / per_b;
+  const int jj = (blockIdx.x % per_b) * blockDim.x + threadIdx.x;
   if (jj >= a.mass_stride) return;
   const int L = a.kv_len[b];
   float sum = 0.f;
   if (jj < L) {
     const float *mp = reinterpret_cast<const float *>(a.ws + p.off_mass_part) +
                       (size_t)b * a.c.H * a.mass_stride + jj;
-    for (int h = 0; h < a.c.H; ++h) sum += mp[(size_t)h * a.mass_stride];
+    for (int h0 = 0; h0 < a.c.H; h0 += 32) {
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = h0 + i < a.c.H ? mp[(size_t)(h0 + i) * a.mass_stride] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if (h0 + i < a.c.H) sum += v[i];
+    }
   }
   a.mass[(size_t)b * a.mass_stride + jj] = sum;
 }
@@ -376,7 +553,10 @@ AttnPlan plan_attention(int batch, int rows, int H, int D, int max_kv_len,
   p.row_tiles = max(1, (max_rows_per_seq + 63) / 64);
   const int max_tiles = max(1, (max_kv_len + KT - 1) / KT);
   const long base = (long)batch * p.row_tiles * H;
-  int splits = (int)((512 + base - 1) / max(base, 1L));
+#ifndef FDL_ATTN_UNITS
+#define FDL_ATTN_UNITS 256
+#endif
+  int splits = (int)((FDL_ATTN_UNITS + base - 1) / max(base, 1L));
   splits = max(1, min(splits, (max_tiles + 1) / 2));
   p.splits = splits;
   if (mass_stride > 0) {
@@ -405,13 +585,13 @@ AttnPlan plan_attention(int batch, int rows, int H, int D, int max_kv_len,
 hipError_t launch_attention(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
   const int units = a.batch * p.row_tiles * a.c.H * p.splits;
   if (a.c.D == 128) {
-    hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(units), dim3(256), 0, s, a, p);
+    hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(units), dim3(512), 0, s, a, p);
   } else {
-    hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(units), dim3(256), 0, s, a, p);
+    hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(units), dim3(512), 0, s, a, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.splits > 1) {
+  if (p.splits > 1 && !p.mass_splits) {
     const size_t threads = (size_t)a.rows * a.c.H * (a.c.D / 4);
     const unsigned blocks = (unsigned)((threads + 255) / 256);
     if (blocks) {
@@ -429,8 +609,13 @@ hipError_t launch_attention(const AttnArgs &a, const AttnPlan &p, hipStream_t s)
     else
       hipLaunchKernelGGL(attn_mass_kernel<64>, dim3(mu), dim3(256), 0, s, a, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    dim3 grid((a.mass_stride + 255) / 256, a.batch);
-    hipLaunchKernelGGL(mass_head_reduce_kernel, grid, dim3(256), 0, s, a, p);
+    const int nb_mass = a.batch * ((a.mass_stride + 255) / 256);
+    const size_t mthreads = p.splits > 1 ? (size_t)a.rows * a.c.H * (a.c.D / 4) : 0;
+    const int nb = nb_mass + (int)((mthreads + 255) / 256);
+    if (a.c.D == 128)
+      hipLaunchKernelGGL(attn_finish_kernel<128>, dim3(nb), dim3(256), 0, s, a, p, nb_mass);
+    else
+      hipLaunchKernelGGL(attn_finish_kernel<64>, dim3(nb), dim3(256), 0, s, a, p, nb_mass);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

@@ -53,6 +53,18 @@ __device__ __forceinline__ T shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, kWave);
 }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS traffic,
+// not for its outstanding global loads (which stay in flight across it).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// 2^x with the hardware approximation (v_exp_f32, about 1 ulp; denormal
+// results flush to zero).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ u32x4 ld16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
