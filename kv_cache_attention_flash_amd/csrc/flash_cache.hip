@@ -483,6 +483,142 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(FlashCacheArgs a, Split
              rope_inv_freq(p % (a.c.D >> 1), a.c.D, a.log2_base));
 }
 
+
+// Tiled projection for many active rows (prefill-like batches), where the
+// product is MFMA-bound.  A workgroup computes BM rows x 128 output features
+// = 64 rotary pairs (tile columns 0..63 are the pairs' first elements, 64..127
+// their partners), with 4 waves as 2 (rows) x 2 (pair halves): wave (wm, wn)
+// owns BM/2 rows and pairs 32*wn .. 32*wn+31 through two 32x32 accumulator
+// columns (first elements, partners), so each lane holds both elements of its
+// rotary pairs and rotates them in registers.  v_mfma_f32_32x32x16_bf16 on
+// 64-element reduction stages staged through double-buffered LDS with a
+// (row / 2) % 8 XOR swizzle of the 16-byte slots (16 consecutive rows hit
+// distinct banks).  Workgroups of one feature tile are dealt to one XCD so the
+// weight tile is shared through its L2.
+template <int BM>
+__global__ __launch_bounds__(256) void qkv_tiled_kernel(FlashCacheArgs a, int nrow_tiles,
+                                                        int ncol_tiles) {
+  constexpr int BN = 128, BK = 64, PIECES = BK / 8;  // 8 slots of 16 B per row
+  constexpr int MTW = BM / 64;                       // 32-row M tiles per wave
+  constexpr int AL = BM * PIECES / 256, BL = BN * PIECES / 256;
+  __shared__ u32x4 lds[2][(BM + BN) * PIECES];
+  __shared__ int s_blk[BM], s_off[BM], s_pos[BM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.c.H, D = a.c.D, half = D >> 1;
+  const int total_pairs = 3 * H * half;
+  const int hidden = a.hidden;
+  const int nb = nrow_tiles * ncol_tiles;
+  int idx = blockIdx.x;
+  if (nb % 8 == 0) idx = (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8;
+  const int ct = idx / nrow_tiles, rtile = idx % nrow_tiles;
+  const int row0 = rtile * BM, pair0 = ct * 64;
+
+  // Row metadata for the tile's rows.
+  for (int rl = tid; rl < BM; rl += 256) {
+    const int r = row0 + rl;
+    if (r < a.rows) {
+      int blk, off, pos;
+      row_meta(a, r, ct == 0, blk, off, pos);
+      s_blk[rl] = blk;
+      s_off[rl] = off;
+      s_pos[rl] = pos;
+    }
+  }
+
+  // Global sources of this thread's 16-byte chunks (row tid/8 + 32 i, slot tid%8).
+  const int piece = tid % PIECES;
+  const uint16_t *asrc[AL];
+  const uint16_t *bsrc[BL];
+  int aslot[AL], bslot[BL];
+#pragma unroll
+  for (int i = 0; i < AL; ++i) {
+    const int tr = tid / PIECES + 32 * i;
+    const int r = min(row0 + tr, a.rows - 1);
+    asrc[i] = a.x + (size_t)r * hidden + piece * 8;
+    aslot[i] = tr * PIECES + (piece ^ ((tr >> 1) & 7));
+  }
+#pragma unroll
+  for (int i = 0; i < BL; ++i) {
+    const int tr = tid / PIECES + 32 * i;  // 0..127: first elements, then partners
+    int p = pair0 + (tr & 63);
+    p = p < total_pairs ? p : total_pairs - 1;
+    const int feat = (p / half) * D + (p % half) + (tr >= 64 ? half : 0);
+    bsrc[i] = a.w + (size_t)feat * hidden + piece * 8;
+    const int lr = BM + tr;
+    bslot[i] = lr * PIECES + (piece ^ ((lr >> 1) & 7));
+  }
+  u32x4 ra[AL], rb[BL];
+  const int nk = hidden / BK;
+  auto load = [&](int kt) {
+    const int k = min(kt, nk - 1) * BK;
+#pragma unroll
+    for (int i = 0; i < AL; ++i) ra[i] = ld16(asrc[i] + k);
+#pragma unroll
+    for (int i = 0; i < BL; ++i) rb[i] = ld16(bsrc[i] + k);
+  };
+  auto store = [&](u32x4 *buf) {
+#pragma unroll
+    for (int i = 0; i < AL; ++i) buf[aslot[i]] = ra[i];
+#pragma unroll
+    for (int i = 0; i < BL; ++i) buf[bslot[i]] = rb[i];
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+  f32x16 acc[MTW][2];
+#pragma unroll
+  for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mt][c][e] = 0.f;
+
+  load(0);
+  store(lds[0]);
+  load(1);
+  lds_barrier();
+  for (int kt = 0; kt < nk; ++kt) {
+    const u32x4 *buf = lds[kt & 1];
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int pc = 2 * ks + hi;
+      u32x4 af[MTW], bf[2];
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt) {
+        const int row = wm * (BM / 2) + 32 * mt + l32;
+        af[mt] = buf[row * PIECES + (pc ^ ((row >> 1) & 7))];
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int row = BM + 64 * c + 32 * wn + l32;
+        bf[c] = buf[row * PIECES + (pc ^ ((row >> 1) & 7))];
+      }
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) acc[mt][c] = mfma32(af[mt], bf[c], acc[mt][c]);
+    }
+    store(lds[(kt + 1) & 1]);
+    load(kt + 2);
+    lds_barrier();
+  }
+
+  // Epilogue: lane holds pair pair0 + 32 wn + l32 for 16 rows per M tile.
+  const int p = pair0 + 32 * wn + l32;
+  if (p >= total_pairs) return;
+  const double freq = rope_inv_freq(p % half, D, a.log2_base);
+#pragma unroll
+  for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int rl = wm * (BM / 2) + 32 * mt + 8 * (e / 4) + 4 * hi + (e % 4);
+      if (row0 + rl >= a.rows) continue;
+      store_pair(a, row0 + rl, p, acc[mt][0][e], acc[mt][1][e], s_blk[rl], s_off[rl], s_pos[rl],
+                 freq);
+    }
+}
+
 }  // namespace
 
 // Tile shape of the skinny (few active rows) projection: 16*MT rows, 8*NT
@@ -575,6 +711,20 @@ hipError_t launch_flash_cache(const FlashCacheArgs &a, void *ws, size_t ws_bytes
     const int items = fp.G * a.rows * (kSplitCW / 2);
     hipLaunchKernelGGL((qkv_reduce_kernel<kSplitCW>), dim3((items + 255) / 256), dim3(256), 0, s,
                        a, sp);
+    return hipGetLastError();
+  }
+  {
+    const int total_pairs = 3 * a.c.H * (a.c.D / 2);
+    const int ncol = (total_pairs + 63) / 64;
+    // Row tile chosen so that the grid fills the 256 CUs a few times over.
+    int bm = 128;  // (a 256-row tile spills its accumulators)
+    while (bm > 64 && (long)((a.rows + bm - 1) / bm) * ncol < 512) bm /= 2;
+    const int nrow = (a.rows + bm - 1) / bm;
+    const dim3 grid(nrow * ncol), block(256);
+    if (bm == 128)
+      hipLaunchKernelGGL((qkv_tiled_kernel<128>), grid, block, 0, s, a, nrow, ncol);
+    else
+      hipLaunchKernelGGL((qkv_tiled_kernel<64>), grid, block, 0, s, a, nrow, ncol);
     return hipGetLastError();
   }
   constexpr int MT = 4, NT = FDL_FC_NT, NW = FDL_FC_NW, DEPTH = FDL_FC_DEPTH;
