@@ -57,6 +57,44 @@ def step_bytes(wl) -> int:
     return flash_cache_bytes(wl) + kv_read + wl.rows * hd * 4 + (4 * int(sum(wl.kv_len)) if wl.topb else 0)
 
 
+class HipTimer:
+    """HIP events created with hipEventDisableSystemFence: recording them does
+    not write back and invalidate the caches, which would otherwise add a few
+    microseconds to every bracketed launch (the HIP runtime documents the flag
+    for timing).  Uses the HIP runtime torch has loaded (soname libamdhip64.so.7)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+        return e
+
+    def record(self, e, stream_handle):
+        rc = self.hip.hipEventRecord(e, self.ct.c_void_p(stream_handle))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def ms(self, a, b) -> float:
+        out = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(out), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return out.value
+
+
 def source_hash(path) -> str:
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -109,6 +147,9 @@ def main():
                     help="independent resident copies rotated so the working set exceeds the LLC")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle timing for the cpu_baseline (0 disables it)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 100 MiB device-to-device copy before timing (a dispatch of "
+                         "known size that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}). "
@@ -144,30 +185,36 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
 
+    if args.calibrate_copy:
+        src = torch.ones(100 * 1024 * 1024, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         steps[i % len(steps)].run(sh)
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    ht = HipTimer()
+    ev = [[ht.event() for _ in range(3)] for _ in range(K)]
+    start, end = ht.event(), ht.event()
     torch.cuda.synchronize()
-    start.record(stream)
+    ht.record(start, sh)
     for i in range(K):
         st = steps[i % len(steps)]
-        ev[i][0].record(stream)
+        ht.record(ev[i][0], sh)
         st.run_flash_cache(sh)
-        ev[i][1].record(stream)
+        ht.record(ev[i][1], sh)
         st.run_attention(sh)
-        ev[i][2].record(stream)
+        ht.record(ev[i][2], sh)
         st.run_topb(sh)
-    end.record(stream)
+    ht.record(end, sh)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
+    total_ms = ht.ms(start, end)
     ms_per_step = total_ms / K
-    fcs_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    att_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    fcs_ms = float(np.mean([ht.ms(e[0], e[1]) for e in ev]))
+    att_ms = float(np.mean([ht.ms(e[1], e[2]) for e in ev]))
     value = wl.rows / (ms_per_step / 1e3)
 
     fb = flash_cache_bytes(wl)
