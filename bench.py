@@ -2,20 +2,25 @@
 """Throughput of the per-layer Flash-dLLM decode step on one MI355X.
 
 One step = flash_cache_step (QKV projection + rotary embedding + paged K/V write)
--> scheduled_attention (with the attention mass) -> track_topb (next tracking
-set), on the LLaDA-8B-class single-layer decode workload: hidden 4096, 32 heads
-x 128, batch 1, cache 768 (256 prompt + 512 generated), 64 active rows (window
-of 32 + 32 tracked), rotary base 5e5, tracking budget 32.
+-> scheduled_attention (with the attention mass when the tracking set is
+re-selected) -> track_topb (next tracking set) [-> verify_accept on the two-view
+workload].  Default workload: the LLaDA-8B-class single-layer decode step,
+hidden 4096, 32 heads x 128, batch 1, cache 768 (256 prompt + 512 generated),
+64 active rows (window of 32 + 32 tracked), rotary base 5e5, tracking budget 32.
+``--workload`` selects the other shapes of the same layer (batch 32 ragged,
+two-view batch 8, the 32-layer batch-16 stack at cache 4096).
 
-Inputs are resident in HBM before timing.  The step's working set (~116 MB)
-would fit in the 256 MB last-level cache, so the benchmark rotates over
-``--copies`` independent copies of weights, hidden states and cache (a model's
-32 layers never share a weight either): every step streams its weight from HBM.
+Inputs are resident in HBM before timing.  A single-layer step's working set
+(~116 MB at batch 1) would fit in the 256 MB last-level cache, so the benchmark
+rotates over independent copies of weights, hidden states and cache (a model's
+32 layers never share a weight either) until the rotation exceeds ~560 MB:
+every step streams its weight and cache from HBM.
 
-Prints ONE JSON line (rank 0, N = 1): metric, value (active query tokens/s per
-layer), ms_per_step, the dominant kernel's roofline (flash_cache_step, HBM
-bound; duration from HIP events recorded around each launch on its stream in
-the timed loop), and the CPU oracle's throughput on the same workload.
+Prints ONE JSON line (N = 1): metric, value (active query tokens/s per layer),
+ms_per_step, the roofline of the call that takes longer (duration from HIP
+events recorded around each launch on its stream inside the timed loop) and of
+the other call, and the CPU oracle's throughput on a bounded sample of the same
+workload.
 """
 
 from __future__ import annotations
@@ -23,6 +28,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -31,10 +37,24 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "active query tokens/s per layer (fused QKV+RoPE+KV-write+attn); % HBM roofline"
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILE_DIR, "flash_cache_llada8b_b1_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "kv_cache_attention_flash_amd", "csrc", "flash_cache.hip")
+CSRC = os.path.join(ROOT, "kv_cache_attention_flash_amd", "csrc")
+SOURCES = {"flash_cache_step": [os.path.join(CSRC, "flash_cache.hip")],
+           "scheduled_attention": [os.path.join(CSRC, "attention.hip")]}
+ROTATION_BYTES = 560e6
+
+WORKLOADS = {
+    "llada8b_b1_l768": "hidden 4096, 32x128 MHA, batch 1, cache 768 (256 prompt + 512 generated), "
+                       "64 active rows (window 32 + 32 tracked), rope base 5e5, top-32 re-selection",
+    "llada8b_ragged_b32": "hidden 4096, 32x128 MHA, batch 32, cache U{512..1024} (block size 32), "
+                          "half refresh / half update stage, 64 active rows each (2048 total), top-32",
+    "llada8b_verify_b8": "hidden 4096, 32x128 MHA, batch 8, context 1024 + one draft block, "
+                         "32 draft + 32 mask rows per sequence (two-view mask), accept scan tau 0.9",
+    "llada8b_stack32_b16_l4096": "32 independent layers of hidden 4096, 32x128 MHA, batch 16, "
+                                 "cache 4096, 64 active rows each (1024 per layer), top-32 per layer",
+}
 
 
 def log(msg):
@@ -49,12 +69,63 @@ def flash_cache_bytes(wl) -> int:
     return 2 * 3 * hd * wl.hid + wl.rows * (2 * wl.hid + 2 * 3 * hd + 4 + 4 + 8)
 
 
-def step_bytes(wl) -> int:
-    """Algorithmic bytes of the whole step: flash_cache_step plus the K/V read
-    of attention (every visible slot once per head), fp32 output and mass."""
+def flash_cache_flops(wl) -> int:
+    return 2 * wl.rows * wl.hid * 3 * wl.num_heads * wl.head_dim
+
+
+def attention_bytes(wl) -> int:
+    """Algorithmic bytes of scheduled_attention: every cached K and V slot of a
+    sequence once per head, Q in (bf16), O out (fp32), the mass out (fp32)."""
     hd = wl.num_heads * wl.head_dim
-    kv_read = int(sum(wl.kv_len)) * hd * 2 * 2
-    return flash_cache_bytes(wl) + kv_read + wl.rows * hd * 4 + (4 * int(sum(wl.kv_len)) if wl.topb else 0)
+    kv = int(sum(int(v) for v in wl.kv_len)) * hd * 2 * 2
+    mass = 4 * int(sum(int(v) for v in wl.kv_len)) if wl.topb else 0
+    return kv + wl.rows * hd * (2 + 4) + mass
+
+
+def visible_pairs(wl) -> int:
+    """Sum over active rows of the number of slots the row attends to."""
+    tot = 0
+    for b in range(wl.batch):
+        n = int(wl.cu_rows[b + 1] - wl.cu_rows[b])
+        L = int(wl.kv_len[b])
+        if wl.views is None or int(wl.views[b][1]) == 0:
+            tot += n * L
+            continue
+        w0, W, d0 = (int(v) for v in wl.views[b])
+        lim = min(d0, L)
+        ctx = lim - max(0, min(w0 + W, lim) - w0)  # context outside the window
+        for t in range(n):
+            tot += ctx + min(t + 1, max(0, L - d0)) if t < W else lim
+    return tot
+
+
+def attention_flops(wl) -> int:
+    return 4 * wl.num_heads * wl.head_dim * visible_pairs(wl)
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(call, workload):
+    return os.path.join(PROFILE_DIR, f"{call}_{workload}_traffic.json")
+
+
+def load_traffic(call, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, only if
+    they were taken on the current kernel source."""
+    try:
+        with open(traffic_file(call, workload)) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != source_hash(SOURCES[call]):
+        return None
+    return t.get("bytes_per_launch")
 
 
 class HipTimer:
@@ -95,56 +166,106 @@ class HipTimer:
         return out.value
 
 
-def source_hash(path) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
-def load_traffic():
-    """HBM bytes per flash_cache_step launch from the committed rocprofv3 counter
-    runs, only if they were taken on the current kernel source."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if t.get("kernel_source_sha256_16") != source_hash(KERNEL_SOURCE):
-        return None
-    return t.get("bytes_per_launch")
-
-
-def cpu_baseline(wl, budget_s=12.0):
-    """The oracle as it stands, on the same workload, on this host's cores."""
-    import numpy as np
-    import oracle as O
+def _threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
-        threads = 1
+        return 1
+
+
+def sequence_subset(wl, seqs, x, k_cache, v_cache):
+    """Inputs of the sequences ``seqs`` alone (their rows, block-table rows,
+    lengths and views); the cache pools stay whole.  Selection only."""
+    import numpy as np
+    rows = np.concatenate([np.arange(wl.cu_rows[b], wl.cu_rows[b + 1]) for b in seqs])
+    cu = np.cumsum([0] + [int(wl.cu_rows[b + 1] - wl.cu_rows[b]) for b in seqs]).astype(np.int32)
+    return dict(rows=rows, x=x[rows], positions=wl.positions[rows], slots=wl.slots[rows], cu=cu,
+                bt=wl.block_table[seqs], kv_len=wl.kv_len[seqs], k=k_cache, v=v_cache,
+                views=None if wl.views is None else wl.views[seqs], seqs=list(seqs))
+
+
+def cpu_baseline(wl, sub, w, budget_s, sample_desc):
+    """The oracle as it stands, on a bounded sample of the workload, on this
+    host's cores; tokens/s per layer = sampled active rows / oracle time."""
+    import numpy as np
+    import oracle as O
     times, res = [], None
     t_end = time.perf_counter() + budget_s
     while not times or time.perf_counter() < t_end:
         t0 = time.perf_counter()
-        res = O.decode_step(wl.x, wl.w, wl.num_heads, wl.head_dim, wl.positions, wl.rope_base,
-                            wl.cu_rows, wl.slots, wl.block_table, wl.block_size, wl.k_cache,
-                            wl.v_cache, wl.kv_len, views=wl.views, topb=wl.topb,
+        res = O.decode_step(sub["x"], w, wl.num_heads, wl.head_dim, sub["positions"], wl.rope_base,
+                            sub["cu"], sub["slots"], sub["bt"], wl.block_size, sub["k"], sub["v"],
+                            sub["kv_len"], views=sub["views"], topb=wl.topb,
                             mass_stride=wl.max_kv_len)
         times.append(time.perf_counter() - t0)
     mean = float(np.mean(times))
-    return ({"value": wl.rows / mean, "unit": "tokens/s/layer", "cores": int(threads),
+    n = len(sub["rows"])
+    return ({"value": n / mean, "unit": "tokens/s/layer", "cores": int(_threads()),
              "kind": "oracle",
-             "sample": f"{len(times)} full oracle step(s) of the benchmark workload "
-                       f"(fp64 numpy, {mean:.2f} s each)"}, res)
+             "sample": f"{len(times)} oracle step(s) over {sample_desc} ({n} active rows, "
+                       f"fp64 numpy, {mean:.2f} s each)"}, res)
+
+
+def parity_against(res, sub, st, wl):
+    """GPU outputs of the sampled sequences against the oracle: slot mapping,
+    tracking set (the oracle's rule on the GPU's mass) and accepted lengths
+    exact, output within the float tolerance."""
+    import numpy as np
+    import oracle as O
+    rows = sub["rows"]
+    ok = bool(np.array_equal(st.slot_mapping.cpu().numpy()[rows], res["slot_mapping"]))
+    o = st.out.cpu().numpy().astype(np.float64)[rows]
+    err = float(np.max(np.abs(o - res["out"])) / np.max(np.abs(res["out"])))
+    ok &= err <= 2e-2
+    if wl.topb:
+        m = st.mass.cpu().numpy().astype(np.float64)
+        idx = st.idx.cpu().numpy()
+        for b in sub["seqs"]:
+            ok &= bool(np.array_equal(idx[b], O.top_b(m[b], int(wl.kv_len[b]), wl.topb)))
+    if wl.verify is not None:
+        v = wl.verify
+        want = [O.accept_length(v["draft"][b], v["mask"][b], v["conf"][b], v["threshold"])
+                for b in range(wl.batch)]
+        ok &= [int(a) for a in st.accept_len.cpu().numpy()] == want
+    return {"ok": bool(ok), "out_max_rel_err": err, "sequences": len(sub["seqs"])}
+
+
+def roofline_entry(call, wl, ms, workload):
+    """Roofline of one library call from its measured average duration; the
+    bound is HBM if the call's algorithmic flops per byte are below the ridge
+    point (2.5 PFLOP/s / 8 TB/s = 312.5), else MFMA."""
+    if call == "flash_cache_step":
+        nbytes, flops = flash_cache_bytes(wl), flash_cache_flops(wl)
+    else:
+        nbytes, flops = attention_bytes(wl), attention_flops(wl)
+    ridge = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if flops / nbytes < ridge:
+        achieved = nbytes / (ms / 1e3) / 1e9
+        e = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = flops / (ms / 1e3) / 1e12
+        e = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFS,
+             "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4)}
+    e["traffic"] = load_traffic(call, workload)
+    e["kernel"] = call
+    e["algorithmic_bytes"] = nbytes
+    e["algorithmic_flops"] = flops
+    e["avg_launch_us"] = round(ms * 1e3, 2)
+    return e
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--copies", type=int, default=5,
-                    help="independent resident copies rotated so the working set exceeds the LLC")
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 200; 5 for the 32-layer stack)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps (default 20; 1 for the 32-layer stack)")
+    ap.add_argument("--workload", default="llada8b_b1_l768", choices=sorted(WORKLOADS))
+    ap.add_argument("--copies", type=int, default=0,
+                    help="resident copies rotated per step (0: enough to exceed ~560 MB)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle timing for the cpu_baseline (0 disables it)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -155,6 +276,9 @@ def main():
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    stack = args.workload == "llada8b_stack32_b16_l4096"
+    steps_k = args.steps if args.steps is not None else (5 if stack else 200)
+    warmup = args.warmup if args.warmup is not None else (1 if stack else 20)
 
     import numpy as np
     import torch
@@ -165,9 +289,13 @@ def main():
     fd.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = synth.llada8b_b1()
+    if stack:
+        wl = synth.llada8b_stack32_layout()
+    else:
+        wl = {"llada8b_b1_l768": synth.llada8b_b1, "llada8b_ragged_b32": synth.llada8b_ragged_b32,
+              "llada8b_verify_b8": synth.llada8b_verify_b8}[args.workload]()
     log(f"workload {wl.name}: rows={wl.rows} hidden={wl.hid} heads={wl.num_heads}x{wl.head_dim} "
-        f"kv_len={wl.kv_len.tolist()} topb={wl.topb} copies={args.copies}")
+        f"batch={wl.batch} max_kv_len={wl.max_kv_len} topb={wl.topb} layers={wl.layers}")
 
     def bf(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -176,12 +304,38 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
 
     cu, pos, slots, kv = i32(wl.cu_rows), i32(wl.positions), i32(wl.slots), i32(wl.kv_len)
+    bt = i32(wl.block_table)
+    views = i32(wl.views) if wl.views is not None else None
+    verify = None
+    if wl.verify is not None:
+        v = wl.verify
+        nb = wl.batch  # the scan runs on the step's sequences (the crafted rows are test cases)
+        verify = (i32(v["draft"][:nb]), i32(v["mask"][:nb]),
+                  torch.from_numpy(np.ascontiguousarray(v["conf"][:nb])).to(dev),
+                  float(v["threshold"]))
     max_rows = int(np.diff(wl.cu_rows).max())
-    steps = []
-    for _ in range(max(1, args.copies)):
-        cache = fd.PagedKVCache(bf(wl.k_cache), bf(wl.v_cache), i32(wl.block_table))
-        steps.append(fd.DecodeStep(cache, bf(wl.x), bf(wl.w), cu, pos, slots, kv, wl.rope_base,
-                                   wl.max_kv_len, max_rows, views=None, topb=wl.topb))
+
+    def make_step(cache, x, w):
+        return fd.DecodeStep(cache, x, w, cu, pos, slots, kv, wl.rope_base, wl.max_kv_len,
+                             max_rows, views=views, topb=wl.topb, verify=verify)
+
+    # units[i % len(units)] = the per-layer steps that make up logical step i
+    units = []
+    if stack:
+        layer_steps = []
+        for layer in range(wl.layers):
+            x, w, k, v = synth.stack_layer_tensors(wl, layer, dev)
+            layer_steps.append(make_step(fd.PagedKVCache(k, v, bt), x, w))
+        units.append(layer_steps)
+        layers_per_step = wl.layers
+        log(f"stack resident: {torch.cuda.memory_allocated(dev) / 1e9:.1f} GB")
+    else:
+        per_copy = 2 * (wl.x.size + wl.w.size + wl.k_cache.size + wl.v_cache.size)
+        copies = args.copies or max(1, math.ceil(ROTATION_BYTES / per_copy))
+        for _ in range(copies):
+            cache = fd.PagedKVCache(bf(wl.k_cache), bf(wl.v_cache), bt)
+            units.append([make_step(cache, bf(wl.x), bf(wl.w))])
+        layers_per_step = 1
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
 
@@ -191,75 +345,87 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for i in range(args.warmup):
-        steps[i % len(steps)].run(sh)
+    for i in range(warmup):
+        for st in units[i % len(units)]:
+            st.run(sh)
     torch.cuda.synchronize()
+    log(f"warm-up done ({warmup} steps, {len(units)} resident unit(s))")
 
-    K = args.steps
+    K = steps_k
     ht = HipTimer()
-    ev = [[ht.event() for _ in range(3)] for _ in range(K)]
+    ev = [[[ht.event() for _ in range(3)] for _ in units[i % len(units)]] for i in range(K)]
     start, end = ht.event(), ht.event()
     torch.cuda.synchronize()
     ht.record(start, sh)
     for i in range(K):
-        st = steps[i % len(steps)]
-        ht.record(ev[i][0], sh)
-        st.run_flash_cache(sh)
-        ht.record(ev[i][1], sh)
-        st.run_attention(sh)
-        ht.record(ev[i][2], sh)
-        st.run_topb(sh)
+        for st, e in zip(units[i % len(units)], ev[i]):
+            ht.record(e[0], sh)
+            st.run_flash_cache(sh)
+            ht.record(e[1], sh)
+            st.run_attention(sh)
+            ht.record(e[2], sh)
+            st.run_topb(sh)
+            st.run_verify(sh)
     ht.record(end, sh)
     torch.cuda.synchronize()
     total_ms = ht.ms(start, end)
     ms_per_step = total_ms / K
-    fcs_ms = float(np.mean([ht.ms(e[0], e[1]) for e in ev]))
-    att_ms = float(np.mean([ht.ms(e[1], e[2]) for e in ev]))
-    value = wl.rows / (ms_per_step / 1e3)
+    fcs_ms = float(np.mean([ht.ms(e[0], e[1]) for evs in ev for e in evs]))
+    att_ms = float(np.mean([ht.ms(e[1], e[2]) for evs in ev for e in evs]))
+    value = wl.rows * layers_per_step / (ms_per_step / 1e3)
 
-    fb = flash_cache_bytes(wl)
-    achieved = fb / (fcs_ms / 1e3) / 1e9
-    traffic = load_traffic()
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "flash_cache_step",
-                "algorithmic_bytes": fb, "avg_launch_us": round(fcs_ms * 1e3, 2)}
-    log(f"step {ms_per_step * 1e3:.1f} us; flash_cache_step {fcs_ms * 1e3:.1f} us "
-        f"({achieved:.0f} GB/s); scheduled_attention {att_ms * 1e3:.1f} us")
+    rf_fc = roofline_entry("flash_cache_step", wl, fcs_ms, args.workload)
+    rf_att = roofline_entry("scheduled_attention", wl, att_ms, args.workload)
+    dominant, other = (rf_fc, rf_att) if fcs_ms >= att_ms else (rf_att, rf_fc)
+    log(f"step {ms_per_step * 1e3:.1f} us ({layers_per_step} layer(s)); flash_cache_step "
+        f"{fcs_ms * 1e3:.1f} us ({rf_fc['achieved']} {rf_fc['unit']}); scheduled_attention "
+        f"{att_ms * 1e3:.1f} us ({rf_att['achieved']} {rf_att['unit']})")
 
     cpu, parity = None, None
     if args.cpu_budget > 0:
-        cpu, ref = cpu_baseline(wl, args.cpu_budget)
-        import oracle as O
-        st = steps[0]
-        ok = np.array_equal(st.slot_mapping.cpu().numpy(), ref["slot_mapping"])
-        o = st.out.cpu().numpy().astype(np.float64)
-        err = float(np.max(np.abs(o - ref["out"])) / np.max(np.abs(ref["out"])))
-        ok &= err <= 2e-2
-        m = st.mass.cpu().numpy().astype(np.float64)
-        ok &= bool(np.array_equal(st.idx.cpu().numpy()[0], O.top_b(m[0], int(wl.kv_len[0]), wl.topb)))
-        parity = {"ok": bool(ok), "out_max_rel_err": err}
+        st = units[0][0]
+        if stack:
+            # Layer 0 as it is on the device now: the timed steps rewrote the
+            # active slots with the same values, so the pools are valid inputs.
+            def host(t):
+                return t.view(torch.int16).cpu().numpy().view(np.uint16)
+            x_h, w_h = host(st.x), host(st.w)
+            k_h, v_h = host(st.cache.k_cache), host(st.cache.v_cache)
+            seqs, desc = [0], "layer 0, sequence 0 of 16"
+        else:
+            x_h, w_h, k_h, v_h = wl.x, wl.w, wl.k_cache, wl.v_cache
+            seqs = list(range(wl.batch)) if wl.batch <= 8 else [0, 1]
+            desc = ("the whole workload" if len(seqs) == wl.batch
+                    else f"sequences {seqs} of {wl.batch}")
+        sub = sequence_subset(wl, seqs, x_h, k_h, v_h)
+        cpu, ref = cpu_baseline(wl, sub, w_h, args.cpu_budget, desc)
+        parity = parity_against(ref, sub, st, wl)
         log(f"cpu oracle {cpu['value']:.1f} tokens/s/layer on {cpu['cores']} threads; parity {parity}")
 
-    sb = step_bytes(wl)
+    hd = wl.num_heads * wl.head_dim
+    sb = flash_cache_bytes(wl) + attention_bytes(wl)
+    tail = (" + scheduled_attention(+mass) + track_topb" if wl.topb else " + scheduled_attention")
+    tail += " + verify_accept" if verify is not None else ""
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s/layer", "n_gpus": 1,
-        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "steps": K, "warmup": warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "llada8b_b1_l768: hidden 4096, 32x128 MHA, batch 1, cache 768 "
-                               "(256 prompt + 512 generated), 64 active rows (window 32 + 32 tracked), "
-                               "rope base 5e5, top-32 re-selection; step = flash_cache_step + "
-                               "scheduled_attention(+mass) + track_topb",
-                   "batch": 1, "active_rows": wl.rows, "kv_len": int(wl.kv_len[0]),
+        "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}; "
+                               f"step = flash_cache_step{tail}",
+                   "batch": wl.batch, "active_rows": wl.rows, "max_kv_len": wl.max_kv_len,
                    "hidden": wl.hid, "heads": wl.num_heads, "head_dim": wl.head_dim,
-                   "resident_copies": len(steps)},
-        "roofline": roofline,
+                   "layers_per_step": layers_per_step, "resident_units": len(units)},
+        "roofline": dominant,
+        "roofline_other": other,
         "cpu_baseline": cpu,
         "step_breakdown_us": {"flash_cache_step": round(fcs_ms * 1e3, 2),
                               "scheduled_attention": round(att_ms * 1e3, 2),
-                              "step_total": round(ms_per_step * 1e3, 2)},
-        "step_hbm_fraction": round(sb / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "layer_total": round(ms_per_step * 1e3 / layers_per_step, 2)},
+        "step_hbm_fraction": round(sb / (ms_per_step / layers_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                   4),
+        "step_algorithmic_bytes": sb,
+        "qkv_dims": [wl.rows, wl.hid, 3 * hd],
         "parity": parity,
     }
     print(json.dumps(line), flush=True)

@@ -234,7 +234,8 @@ def verify_accept(draft_tok, mask_tok, conf, threshold, out=None, stream=None):
 
 class DecodeStep:
     """One per-layer decode step bound to fixed device buffers:
-    flash_cache_step -> scheduled_attention (+ mass) -> track_topb.
+    flash_cache_step -> scheduled_attention (+ mass) -> track_topb, and the
+    accept scan when ``verify`` inputs are given.
 
     The ctypes argument lists are built once, so ``run()`` only issues the three
     asynchronous library calls on the given stream (suitable for timing loops
@@ -242,7 +243,7 @@ class DecodeStep:
 
     def __init__(self, cache: PagedKVCache, x, w_qkv, cu_rows, positions, slots, kv_len,
                  rope_base, max_kv_len, max_rows_per_seq, views=None, topb=0,
-                 softmax_scale=0.0):
+                 softmax_scale=0.0, verify=None):
         self.lib = _lib.load()
         dev = x.device
         r = x.shape[0]
@@ -278,6 +279,17 @@ class DecodeStep:
                      self.workspace.data_ptr(), self.workspace.numel())
         self._top = ((self.mass.data_ptr(), self.mass_stride, kv_len.data_ptr(), self.batch,
                       self.topb, self.idx.data_ptr()) if self.topb else None)
+        # Optional accept scan after the step: (draft, mask, conf, threshold).
+        self._ver = None
+        if verify is not None:
+            d, m, c, thr = verify
+            _need(d, "draft_tok", torch.int32, 2)
+            _need(m, "mask_tok", torch.int32, 2)
+            _need(c, "conf", torch.float32, 2)
+            self.verify_inputs = (d, m, c)
+            self.accept_len = torch.empty((d.shape[0],), dtype=torch.int32, device=dev)
+            self._ver = (d.data_ptr(), m.data_ptr(), c.data_ptr(), d.shape[0], d.shape[1],
+                         ctypes.c_float(float(thr)), self.accept_len.data_ptr())
 
     def run_flash_cache(self, stream: int):
         _lib.check("flash_cache_step", self.lib.flash_cache_step(*self._fcs, stream))
@@ -289,8 +301,13 @@ class DecodeStep:
         if self._top is not None:
             _lib.check("track_topb", self.lib.track_topb(*self._top, stream))
 
+    def run_verify(self, stream: int):
+        if self._ver is not None:
+            _lib.check("verify_accept", self.lib.verify_accept(*self._ver, stream))
+
     def run(self, stream: Optional[int] = None):
         s = _stream(stream, self.x.device) if not isinstance(stream, int) else stream
         self.run_flash_cache(s)
         self.run_attention(s)
         self.run_topb(s)
+        self.run_verify(s)

@@ -9,15 +9,15 @@
 //
 // Work decomposition.  Output features are grouped in rotary PAIRS (i, i + D/2)
 // of one head of one of Q, K, V, so a pair's two outputs always land in the
-// same workgroup and the rotation needs no extra memory traffic.  A workgroup
-// owns NT x 8 consecutive pairs (16 x NT output features) for a strip of
-// 16 x MT rows and the WHOLE reduction dimension, split across its NW waves:
-// every weight byte is read from HBM exactly once per row strip.  The waves'
-// partial sums meet in LDS; the epilogue adds them in wave order (deterministic),
-// rotates in fp32 with an fp64-reduced angle, rounds to bf16 (RNE) and scatters
-// K/V through the block table.  MFMA: v_mfma_f32_16x16x32_bf16, both operands
-// loaded 16 bytes per lane straight from global memory (the weight is stored
-// feature-major, so each lane's 8 reduction elements are contiguous).
+// same workgroup and the rotation needs no extra memory traffic.  Two kernels:
+//   qkv_splitk_kernel  up to 64 active rows (the decode regime, where reading
+//                      the weight dominates): each workgroup streams a slice
+//                      of the weight once, staged through LDS in whole lines;
+//   qkv_tiled_kernel   more rows: a 2-D tiled MFMA GEMM (32x32x16 bf16).
+// Both finish in an fp32 epilogue: rotation with an fp64-reduced angle, bf16
+// rounding (RNE), Q to its buffer and K/V scattered through the block table.
+// Partial sums are always added in a fixed order, so results are bitwise
+// reproducible.
 #include "device_common.h"
 #include "internal.h"
 
@@ -91,168 +91,12 @@ __device__ __forceinline__ void row_meta(const FlashCacheArgs &a, int r, bool wr
   if (write_map && a.slot_mapping) a.slot_mapping[r] = (int64_t)blk * a.c.bs + off;
 }
 
-template <int MT, int NT, int NW, int DEPTH>
-__global__ __launch_bounds__(NW * 64) void qkv_rope_write_kernel(FlashCacheArgs a) {
-  constexpr int ROWS = 16 * MT;
-  constexpr int COLS = 16 * NT;
-  constexpr int PAIRS = 8 * NT;
-  __shared__ float red[NW][ROWS][COLS + 1];
-  __shared__ int s_blk[ROWS], s_off[ROWS], s_pos[ROWS];
-  __shared__ double s_freq[64];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int H = a.c.H, D = a.c.D, half = D >> 1;
-  const int total_pairs = 3 * H * half;
-  const int pair0 = blockIdx.x * PAIRS;
-  const int row0 = blockIdx.y * ROWS;
-  const int hidden = a.hidden;
-  if (tid < half) s_freq[tid] = rope_inv_freq(tid, D, a.log2_base);
-
-  // Row metadata: sequence, physical slot, rotary position.
-  if (tid < ROWS) {
-    int r = row0 + tid;
-    if (r < a.rows) {
-      int b = row_to_seq(a.cu_rows, a.batch, r);
-      int s = a.slots[r];
-      int blk = a.c.block_table[(size_t)b * a.c.max_blocks + s / a.c.bs];
-      int off = s % a.c.bs;
-      s_blk[tid] = blk;
-      s_off[tid] = off;
-      s_pos[tid] = a.positions[r];
-      if (blockIdx.x == 0 && a.slot_mapping)
-        a.slot_mapping[r] = (int64_t)blk * a.c.bs + off;
-    }
-  }
-
-  // Operand rows of this lane.
-  const int g = lane >> 4;  // reduction slot group
-  const int j = lane & 15;  // A row / B column inside a 16-tile
-  const uint16_t *xrow[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    int r = row0 + mt * 16 + j;
-    r = r < a.rows ? r : a.rows - 1;
-    xrow[mt] = a.x + (size_t)r * hidden + 8 * g;
-  }
-  const uint16_t *wrow[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    int p = pair0 + 8 * t + (j & 7);
-    p = p < total_pairs ? p : total_pairs - 1;
-    int feat = (p / half) * D + (p % half) + ((j & 8) ? half : 0);
-    wrow[t] = a.w + (size_t)feat * hidden + 8 * g;
-  }
-
-  // Reduction steps of 32 split evenly over the waves.
-  const int steps = hidden / 32;
-  const int per = (steps + NW - 1) / NW;
-  const int s_begin = wave * per;
-  const int s_end = min(steps, s_begin + per);
-
-  f32x4 acc[MT][NT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Register ring of DEPTH reduction steps in flight per wave: the loads of
-  // step st + DEPTH are issued as soon as step st's operands are consumed, so
-  // every wave keeps DEPTH * (MT + NT) KiB of loads outstanding.
-  // Loads are unconditional (addresses clamped to the last valid step) so the
-  // compiler can count outstanding loads exactly across the unrolled ring.
-  u32x4 abuf[DEPTH][MT], bbuf[DEPTH][NT];
-  const int nsteps = max(0, s_end - s_begin);
-  const int nfull = nsteps / DEPTH * DEPTH;
-  // Workgroups start their step loop at different offsets (rotation by the
-  // workgroup's index within its XCD) so that the many workgroups sharing an
-  // L2 do not all read the same activation lines at the same moment.
-#ifndef FDL_FC_ROTATE
-#define FDL_FC_ROTATE 1
-#endif
-  const int rot = FDL_FC_ROTATE ? (int)(blockIdx.x >> 3) : 0;
-  auto issue = [&](int d, int st) {
-    const int rel = min(st, s_end - 1) - s_begin;
-    const int k = (nsteps > 0 ? s_begin + (rel + rot) % nsteps : 0) * 32;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) bbuf[d][t] = ld16(wrow[t] + k);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) abuf[d][mt] = ld16(xrow[mt] + k);
-  };
-  auto consume = [&](int d) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[mt][t] = mfma16(abuf[d][mt], bbuf[d][t], acc[mt][t]);
-  };
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) issue(d, s_begin + d);
-  for (int st0 = 0; st0 < nfull; st0 += DEPTH) {
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      consume(d);
-      issue(d, s_begin + st0 + d + DEPTH);
-    }
-  }
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (d < nsteps - nfull) consume(d);
-
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) red[wave][mt * 16 + 4 * g + e][t * 16 + j] = acc[mt][t][e];
-  __syncthreads();
-
-  // Epilogue: one (row, pair) per thread and iteration.
-  for (int item = tid; item < ROWS * PAIRS; item += NW * 64) {
-    const int rl = item / PAIRS;
-    const int pl = item % PAIRS;
-    const int r = row0 + rl;
-    const int p = pair0 + pl;
-    if (r >= a.rows || p >= total_pairs) continue;
-    const int clo = (pl >> 3) * 16 + (pl & 7);
-    float lo = 0.f, hi = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      lo += red[w][rl][clo];
-      hi += red[w][rl][clo + 8];
-    }
-    const int sh = p / half;  // section * H + head
-    const int i = p % half;
-    const int sec = sh / H;
-    const int h = sh % H;
-    if (sec < 2) {
-      float c, s;
-      rope_cs(s_pos[rl], s_freq[i], c, s);
-      const float rlo = lo * c - hi * s;
-      const float rhi = hi * c + lo * s;
-      lo = rlo;
-      hi = rhi;
-    }
-    const uint16_t blo = f32_to_bf16_rne(lo), bhi = f32_to_bf16_rne(hi);
-    uint16_t *dst;
-    if (sec == 0) {
-      dst = a.q_out + ((size_t)r * H + h) * D;
-    } else {
-      uint16_t *pool = sec == 1 ? a.c.k : a.c.v;
-      dst = pool + (((size_t)s_blk[rl] * H + h) * a.c.bs + s_off[rl]) * D;
-    }
-    dst[i] = blo;
-    dst[i + half] = bhi;
-  }
-}
-
-
 // Split-K projection for up to 64 active rows (the decode regime, where the
 // weight stream dominates).  Grid = G column groups x S reduction splits.  A
 // workgroup owns CW = 16*NTW*NGW output features (CW/2 rotary pairs) of 64 rows
-// over hidden/S reduction elements, staged through LDS in 128-element chunks:
-// every global load instruction reads whole 128-byte lines (16 lanes per
-// 256-byte row segment), and the 64 x hidden activations are read G times in
+// over hidden/S reduction elements, staged through LDS in KC-element chunks:
+// every global load instruction reads whole 128-byte lines (consecutive lanes
+// cover consecutive 16-byte pieces of a row), and the 64 x hidden activations are read G times in
 // total instead of once per 48 features.  Chunk tiles are double-buffered in
 // LDS with a 16-byte-slot XOR swizzle (slot ^ row % 16) so the 16 lanes that
 // read one MFMA operand hit distinct banks; two register stages keep two
@@ -621,17 +465,9 @@ __global__ __launch_bounds__(256) void qkv_tiled_kernel(FlashCacheArgs a, int nr
 
 }  // namespace
 
-// Tile shape of the skinny (few active rows) projection: 16*MT rows, 8*NT
-// rotary pairs and NW waves per workgroup, DEPTH reduction steps in flight.
-#ifndef FDL_FC_NT
-#define FDL_FC_NT 3
-#endif
-#ifndef FDL_FC_NW
-#define FDL_FC_NW 8
-#endif
-#ifndef FDL_FC_DEPTH
-#define FDL_FC_DEPTH 4
-#endif
+// Tile shape of the split-K projection: NTW 16-feature tiles per wave, NGW
+// wave groups across features, NST register stages, SNW waves, KC reduction
+// elements per staged chunk; at most SPLIT_CAP workgroups before splitting.
 
 #ifndef FDL_FC_NTW
 #define FDL_FC_NTW 3
@@ -664,7 +500,7 @@ struct FcPlan {
 FcPlan plan_fc(int rows, int hidden, int H, int D) {
   FcPlan p{};
   const int total_pairs = 3 * H * (D / 2);
-  if (rows > 64 || hidden % FDL_FC_KC != 0) return p;  // row-strip kernel, no workspace
+  if (rows > 64 || hidden % FDL_FC_KC != 0) return p;  // tiled kernel, no workspace
   p.splitk = true;
   p.G = (total_pairs + kSplitCW / 2 - 1) / (kSplitCW / 2);
   p.S = 1;
@@ -713,25 +549,20 @@ hipError_t launch_flash_cache(const FlashCacheArgs &a, void *ws, size_t ws_bytes
                        a, sp);
     return hipGetLastError();
   }
-  {
-    const int total_pairs = 3 * a.c.H * (a.c.D / 2);
-    const int ncol = (total_pairs + 63) / 64;
-    // Row tile chosen so that the grid fills the 256 CUs a few times over.
-    int bm = 128;  // (a 256-row tile spills its accumulators)
-    while (bm > 64 && (long)((a.rows + bm - 1) / bm) * ncol < 512) bm /= 2;
-    const int nrow = (a.rows + bm - 1) / bm;
-    const dim3 grid(nrow * ncol), block(256);
-    if (bm == 128)
-      hipLaunchKernelGGL((qkv_tiled_kernel<128>), grid, block, 0, s, a, nrow, ncol);
-    else
-      hipLaunchKernelGGL((qkv_tiled_kernel<64>), grid, block, 0, s, a, nrow, ncol);
-    return hipGetLastError();
-  }
-  constexpr int MT = 4, NT = FDL_FC_NT, NW = FDL_FC_NW, DEPTH = FDL_FC_DEPTH;
+  // More than 64 rows (or a hidden size the chunking does not divide): tiled
+  // MFMA kernel, row tile chosen so that the grid fills the 256 CUs a few times.
   const int total_pairs = 3 * a.c.H * (a.c.D / 2);
-  dim3 grid((total_pairs + 8 * NT - 1) / (8 * NT), (a.rows + 16 * MT - 1) / (16 * MT));
-  hipLaunchKernelGGL((qkv_rope_write_kernel<MT, NT, NW, DEPTH>), grid, dim3(NW * 64), 0, s, a);
+  const int ncol = (total_pairs + 63) / 64;
+  int bm = 128;  // (a 256-row tile spills its accumulators)
+  while (bm > 64 && (long)((a.rows + bm - 1) / bm) * ncol < 512) bm /= 2;
+  const int nrow = (a.rows + bm - 1) / bm;
+  const dim3 grid(nrow * ncol), block(256);
+  if (bm == 128)
+    hipLaunchKernelGGL((qkv_tiled_kernel<128>), grid, block, 0, s, a, nrow, ncol);
+  else
+    hipLaunchKernelGGL((qkv_tiled_kernel<64>), grid, block, 0, s, a, nrow, ncol);
   return hipGetLastError();
 }
 
 }  // namespace fdl
+

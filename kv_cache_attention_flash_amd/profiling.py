@@ -2,11 +2,12 @@
 
     python -m kv_cache_attention_flash_amd.profiling stats  <kernel_stats.csv> <out.md> <command...>
     python -m kv_cache_attention_flash_amd.profiling traffic <fetch_counter.csv> <write_counter.csv> \
-        <out.json> <kernel-name-substring> <calibration-bytes> <command...>
+        <out.json> <kernel-substrings> <calibration-bytes> <source-file> <command...>
 
 ``stats`` writes a Markdown table of per-kernel call counts and durations.
 ``traffic`` turns two counter runs (FETCH_SIZE, then WRITE_SIZE, KiB per
-dispatch) into HBM bytes per launch of one kernel.  Each counter is scaled by
+dispatch) into HBM bytes per call of one library entry point: the sum over
+its kernels (comma-separated name substrings) of each kernel's median.  Each counter is scaled by
 what it reads for the plain device-to-device copy of ``calibration-bytes``
 bytes that ran in the same process (the ``copyBuffer`` dispatch of that size):
 on gfx950 FETCH_SIZE reads half of the bytes a copy actually fetches.  The
@@ -63,7 +64,7 @@ def _calibration(vals, grid_hint=None):
     return best
 
 
-def traffic(fetch_csv, write_csv, kernel_substr, calib_bytes, source_file):
+def traffic(fetch_csv, write_csv, kernel_substrs, calib_bytes, source_file):
     fv = _per_dispatch(fetch_csv, "FETCH_SIZE")
     wv = _per_dispatch(write_csv, "WRITE_SIZE")
     cf, cw = _calibration(fv), _calibration(wv)
@@ -71,16 +72,22 @@ def traffic(fetch_csv, write_csv, kernel_substr, calib_bytes, source_file):
         raise SystemExit("no copy calibration dispatch found")
     scale_f = calib_bytes / (cf * 1024.0)
     scale_w = calib_bytes / (cw * 1024.0)
-    kf = [x for (n, _), v in fv.items() if kernel_substr in n for x in v]
-    kw = [x for (n, _), v in wv.items() if kernel_substr in n for x in v]
-    if not kf or not kw:
-        raise SystemExit(f"no dispatch of a kernel matching {kernel_substr!r}")
-    fetch_b = statistics.median(kf) * 1024.0 * scale_f
-    write_b = statistics.median(kw) * 1024.0 * scale_w
+    per_kernel = {}
+    for ks in kernel_substrs.split(","):
+        kf = [x for (n, _), v in fv.items() if ks in n for x in v]
+        kw = [x for (n, _), v in wv.items() if ks in n for x in v]
+        if not kf or not kw:
+            raise SystemExit(f"no dispatch of a kernel matching {ks!r}")
+        per_kernel[ks] = {"dispatches": [len(kf), len(kw)],
+                          "fetch_size_kib_median": statistics.median(kf),
+                          "write_size_kib_median": statistics.median(kw),
+                          "fetch_bytes": statistics.median(kf) * 1024.0 * scale_f,
+                          "write_bytes": statistics.median(kw) * 1024.0 * scale_w}
+    fetch_b = sum(k["fetch_bytes"] for k in per_kernel.values())
+    write_b = sum(k["write_bytes"] for k in per_kernel.values())
     with open(source_file, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()[:16]
-    return {"kernel": kernel_substr, "dispatches": [len(kf), len(kw)],
-            "fetch_size_kib_median": statistics.median(kf), "write_size_kib_median": statistics.median(kw),
+    return {"kernels": per_kernel,
             "copy_calibration_bytes": calib_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
             "fetch_scale": scale_f, "write_scale": scale_w,
             "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
@@ -96,10 +103,9 @@ def main(argv):
             f.write(md)
         print(md)
     elif argv[0] == "traffic":
-        fetch_csv, write_csv, out, kernel, calib = argv[1:6]
-        t = traffic(fetch_csv, write_csv, kernel, float(calib),
-                    os.path.join(HERE, "csrc", "flash_cache.hip"))
-        t["commands"] = " ".join(argv[6:])
+        fetch_csv, write_csv, out, kernels, calib, source = argv[1:7]
+        t = traffic(fetch_csv, write_csv, kernels, float(calib), source)
+        t["commands"] = " ".join(argv[7:])
         with open(out, "w") as f:
             json.dump(t, f, indent=1)
         print(json.dumps(t, indent=1))
