@@ -124,8 +124,11 @@ size_t fdl_flash_cache_workspace_bytes(int32_t num_rows, int32_t hidden,
  * For sequence b, head h and row r: P = softmax(scale * q_r . k_j) over the
  * visible slots j < kv_len[b] (see fdl_two_view), out_r = sum_j P_j v_j.
  *   q          device bf16 [num_rows][H][D] (as written by flash_cache_step)
- *   kv_len     device int32 [batch]; max_kv_len >= every kv_len[b] (host bound).
+ *   kv_len     device int32 [batch]; max_kv_len >= every kv_len[b] (host bound;
+ *              a larger kv_len[b] is read as max_kv_len).
  *   max_rows_per_seq  host upper bound on cu_rows[b+1]-cu_rows[b].
+ *   Cache slots at or past kv_len[b] are never used, whatever they hold (NaN
+ *   included), even when they share a page with visible slots.
  *   views      device fdl_two_view [batch], or NULL (all sequences plain).
  *   softmax_scale  0 selects 1/sqrt(D).
  *   out        device fp32 [num_rows][H][D]; a row that sees no key gets 0.
@@ -155,6 +158,7 @@ size_t fdl_attention_workspace_bytes(int32_t batch, int32_t num_rows,
  * per sequence the topb keys j < kv_len[b] with the largest mass[b][j]; equal
  * masses go to the lower index.  Written as a set in ascending index order to
  * idx_out (device int32 [batch][topb]); when kv_len[b] < topb the tail is -1.
+ * A kv_len[b] larger than mass_stride is read as mass_stride.
  * mass values must be non-negative and not NaN (attention masses are). */
 int track_topb(const float *mass, int32_t mass_stride, const int32_t *kv_len,
                int32_t batch, int32_t topb, int32_t *idx_out, void *stream);

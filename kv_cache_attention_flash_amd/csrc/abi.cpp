@@ -38,6 +38,8 @@ fdl::CacheView view_of(const fdl_kv_cache *c) {
   v.H = c->num_heads;
   v.D = c->head_dim;
   v.bs = c->block_size;
+  v.bs_shift = 0;
+  while ((1 << v.bs_shift) < v.bs) ++v.bs_shift;  // block sizes are powers of two
   v.num_blocks = c->num_blocks;
   v.max_blocks = c->max_blocks_per_seq;
   v.k = static_cast<uint16_t *>(c->k_cache);
@@ -144,6 +146,7 @@ int scheduled_attention(const fdl_kv_cache *cache, const void *q, int32_t batch,
   a.rows = num_rows;
   a.cu_rows = cu_rows;
   a.kv_len = kv_len;
+  a.max_kv_len = max_kv_len;
   a.views = reinterpret_cast<const int32_t *>(views);
   const double scale = softmax_scale > 0.f ? (double)softmax_scale
                                             : 1.0 / std::sqrt((double)cache->head_dim);

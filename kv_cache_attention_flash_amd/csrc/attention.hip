@@ -35,6 +35,12 @@ namespace fdl {
 namespace {
 
 constexpr int KT = 32;  // keys per tile
+#ifndef FDL_ATTN_NPF
+#define FDL_ATTN_NPF 2
+#endif
+#ifndef FDL_ATTN_MNPF
+#define FDL_ATTN_MNPF 2
+#endif
 constexpr float kNegInf = -__builtin_huge_valf();
 
 struct SeqInfo {
@@ -45,7 +51,7 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnArgs &a, int b) {
   SeqInfo si;
   si.r0 = a.cu_rows[b];
   si.nrows = a.cu_rows[b + 1] - si.r0;
-  si.L = a.kv_len[b];
+  si.L = min(a.kv_len[b], a.max_kv_len);  // a length past the stated bound is clamped
   if (a.views) {
     si.w0 = a.views[3 * b];
     si.wl = a.views[3 * b + 1];
@@ -65,10 +71,78 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnArgs &a, int b) {
 //   missing row:      nothing
 struct Vis {
   int lim, x0, x1, y0, y1;
+  // Non-short-circuit operators: compares and mask logic, no branches.
   __device__ __forceinline__ bool operator()(int j) const {
-    return (j < lim && (j < x0 || j >= x1)) || (j >= y0 && j <= y1);
+    return ((j < lim) & ((j < x0) | (j >= x1))) | ((j >= y0) & (j <= y1));
+  }
+  // Every slot of [k0, k0 + n) visible.
+  __device__ __forceinline__ bool all(int k0, int n) const {
+    return (k0 + n <= lim) & ((k0 + n <= x0) | (k0 >= x1));
+  }
+  // No slot of [k0, k0 + n) visible.
+  __device__ __forceinline__ bool none(int k0, int n) const {
+    return ((k0 >= lim) | ((k0 >= x0) & (k0 + n <= x1))) &
+           ((y1 < k0) | (y0 >= k0 + n) | (y0 > y1));
   }
 };
+
+// Whole-wave visibility of one 32-key tile: 2 = every lane sees every key,
+// 0 = no lane sees any key, 1 = mixed (test key by key).
+__device__ __forceinline__ int tile_vis(const Vis &vis, int key0) {
+  if (__all(vis.all(key0, 32))) return 2;
+  if (__all(vis.none(key0, 32))) return 0;
+  return 1;
+}
+
+// Online-softmax step for one 32-key tile held as S^T fragments (lane: query
+// row lane % 16, keys key0 + 8g + 4mt + e).  Updates the row's running max m
+// (log2 units) and normaliser l, writes the scaled scores to xs (-inf where
+// not visible), rescales o by the change of max and returns the bf16 P^T
+// operand of the PV product.  exp2(-inf) is 0, so hidden keys need no select.
+template <int NO>
+__device__ __forceinline__ u32x4 tile_softmax(const f32x4 s[2], const Vis &vis, int tv, int key0,
+                                              int g, float scale, float &m, float &l, f32x4 *o,
+                                              float *xs) {
+  if (tv == 2) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xs[mt * 4 + e] = s[mt][e] * scale;
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        xs[mt * 4 + e] = vis(key0 + 8 * g + 4 * mt + e) ? s[mt][e] * scale : kNegInf;
+  }
+  float tmax = fmaxf(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])),
+                     fmaxf(fmaxf(xs[4], xs[5]), fmaxf(xs[6], xs[7])));
+  tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+  const float mnew = fmaxf(m, tmax);
+  const float msafe = mnew == kNegInf ? 0.f : mnew;  // a row that has seen nothing keeps zeros
+  const float alpha = fast_exp2(m - msafe);
+  float pv[8], rs = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    pv[e] = fast_exp2(xs[e] - msafe);
+    rs += pv[e];
+  }
+  rs += shfl_xor(rs, 16);
+  rs += shfl_xor(rs, 32);
+  l = l * alpha + rs;
+  m = mnew;
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int dm = 0; dm < NO; ++dm) o[dm] *= alpha;
+  }
+  u32x4 pb;
+  pb[0] = cvt_pk_bf16(pv[0], pv[1]);
+  pb[1] = cvt_pk_bf16(pv[2], pv[3]);
+  pb[2] = cvt_pk_bf16(pv[4], pv[5]);
+  pb[3] = cvt_pk_bf16(pv[6], pv[7]);
+  return pb;
+}
 
 __device__ __forceinline__ Vis row_vis(const SeqInfo &si, int t, bool row_ok) {
   Vis v{0, 0, 0, 1, 0};
@@ -104,8 +178,8 @@ template <int D> constexpr int kVPad = D + 16;  // V row stride: conflict-free t
 constexpr int kMaxPages = 1024;
 
 __device__ __forceinline__ void stage_pages(const AttnArgs &a, int b, int tb, int te, int *s_page) {
-  const int bs = a.c.bs;
-  const int p0 = tb * KT / bs, p1 = te > tb ? ((te * KT - 1) / bs) + 1 : p0;
+  const int sh = a.c.bs_shift;
+  const int p0 = (tb * KT) >> sh, p1 = te > tb ? ((te * KT - 1) >> sh) + 1 : p0;
   for (int i = threadIdx.x; i < p1 - p0; i += blockDim.x)
     s_page[i] = a.c.block_table[(size_t)b * a.c.max_blocks + p0 + i];
 }
@@ -113,9 +187,9 @@ __device__ __forceinline__ void stage_pages(const AttnArgs &a, int b, int tb, in
 template <int D>
 __device__ __forceinline__ void load_tile(Tile<D> &t, const AttnArgs &a, const int *s_page, int tb,
                                           int h, int key0, bool want_v, int gtid) {
-  const int bs = a.c.bs;
-  const int page = s_page[key0 / bs - tb * KT / bs];
-  const size_t base = (((size_t)page * a.c.H + h) * bs + (key0 % bs)) * D;
+  const int sh = a.c.bs_shift;
+  const int page = s_page[(key0 >> sh) - ((tb * KT) >> sh)];
+  const size_t base = ((((size_t)page * a.c.H + h) << sh) + (key0 & (a.c.bs - 1))) * D;
 #pragma unroll
   for (int i = 0; i < Tile<D>::NCH; ++i) {
     const int c = gtid + 256 * i;
@@ -124,15 +198,21 @@ __device__ __forceinline__ void load_tile(Tile<D> &t, const AttnArgs &a, const i
   }
 }
 
+// V rows at or past the cached length (vkeys valid keys in the tile) are
+// stored as zeros: those slots' contents are unspecified, and a zero weight
+// times a NaN would still poison the product.
 template <int D>
 __device__ __forceinline__ void store_tile(const Tile<D> &t, uint16_t (*klds)[kKPad<D>],
-                                           uint16_t (*vlds)[kVPad<D>], bool want_v, int gtid) {
+                                           uint16_t (*vlds)[kVPad<D>], bool want_v, int gtid,
+                                           int vkeys = KT) {
+  const bool part = vkeys < KT;
 #pragma unroll
   for (int i = 0; i < Tile<D>::NCH; ++i) {
     const int c = gtid + 256 * i;
     const int key = c / Tile<D>::CH, dc = c % Tile<D>::CH;
     st16(&klds[key][dc * 8], t.k[i]);
-    if (want_v) st16(&vlds[key][dc * 8], t.v[i]);
+    if (want_v)
+      st16(&vlds[key][dc * 8], part && key >= vkeys ? u32x4{0u, 0u, 0u, 0u} : t.v[i]);
   }
 }
 
@@ -188,7 +268,7 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, int r, int h, bool ok,
 // first), so two waves per SIMD hide each other's latency.
 template <int D>
 __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
-  constexpr int NPF = 2;  // tiles in flight per key group
+  constexpr int NPF = FDL_ATTN_NPF;  // tiles in flight per key group
   __shared__ uint16_t klds[2][2][KT][kKPad<D>];
   __shared__ uint16_t vlds[2][2][KT][kVPad<D>];
 
@@ -234,61 +314,31 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
   for (int dm = 0; dm < D / 16; ++dm) o[dm] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = kNegInf, l = 0.f;
 
-  for (int it0 = 0; it0 < niter; it0 += NPF) {
+  // Every iteration has the same shape: one ring stage stored to LDS, the
+  // same stage reloaded, a barrier, then the tile's math only if the tile
+  // exists.  With no branch around a load, the compiler waits for exactly
+  // the stage it needs and keeps the other stages in flight.
+  const int niter_r = (niter + NPF - 1) / NPF * NPF;
+  for (int it0 = 0; it0 < niter_r; it0 += NPF) {
 #pragma unroll
     for (int ii = 0; ii < NPF; ++ii) {
       const int it = it0 + ii;
-      if (it >= niter) break;
       const int tile = tb + kg + 2 * it;
-      const bool have = tile < te;
-      const int buf = ii & 1;
-      store_tile<D>(pf[ii], klds[kg][buf], vlds[kg][buf], true, gtid);
+      const bool have = it < niter && tile < te;
+      const int buf = it & 1;  // alternates across iterations for any NPF
+      store_tile<D>(pf[ii], klds[kg][buf], vlds[kg][buf], true, gtid, si.L - tile * KT);
       load_tile<D>(pf[ii], a, s_page, tb, h, min(tile + 2 * NPF, tlast) * KT, true, gtid);
       lds_barrier();
-      if (!have) continue;
       const int key0 = tile * KT;
-      f32x4 s[2];
-      scores<D>(klds[kg][buf], qf, lane, s);
-      float v[8];
-      float tmax = kNegInf;
+      const int tv = have ? tile_vis(vis, key0) : 0;
+      if (tv != 0) {
+        f32x4 s[2];
+        scores<D>(klds[kg][buf], qf, lane, s);
+        float xs[8];
+        const u32x4 pb = tile_softmax<D / 16>(s, vis, tv, key0, g, a.scale_log2, m, l, o, xs);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int jj = key0 + 8 * g + 4 * mt + e;
-          const float x = vis(jj) ? s[mt][e] * a.scale_log2 : kNegInf;
-          v[mt * 4 + e] = x;
-          tmax = fmaxf(tmax, x);
-        }
-      tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-      const float mnew = fmaxf(m, tmax);
-      float pv[8];
-      float alpha = 1.f, rs = 0.f;
-      if (mnew == kNegInf) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = 0.f;
-      } else {
-        alpha = fast_exp2(m - mnew);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pv[e] = v[e] == kNegInf ? 0.f : fast_exp2(v[e] - mnew);
-          rs += pv[e];
-        }
-      }
-      rs += shfl_xor(rs, 16);
-      rs += shfl_xor(rs, 32);
-      l = l * alpha + rs;
-      m = mnew;
-      u32x4 pb;
-      pb[0] = pack_bf16x2(pv[0], pv[1]);
-      pb[1] = pack_bf16x2(pv[2], pv[3]);
-      pb[2] = pack_bf16x2(pv[4], pv[5]);
-      pb[3] = pack_bf16x2(pv[6], pv[7]);
-#pragma unroll
-      for (int dm = 0; dm < D / 16; ++dm) {
-        o[dm] *= alpha;
-        o[dm] = mfma16(vt_operand<D>(vlds[kg][buf], dm, lane), pb, o[dm]);
+        for (int dm = 0; dm < D / 16; ++dm)
+          o[dm] = mfma16(vt_operand<D>(vlds[kg][buf], dm, lane), pb, o[dm]);
       }
     }
   }
@@ -436,35 +486,47 @@ __global__ __launch_bounds__(256) void attn_mass_kernel(AttnArgs a, AttnPlan p) 
     const int r = si.r0 + (row_ok ? t : 0);
     const size_t rh = (size_t)r * a.c.H + h;
     const Vis vis = row_vis(si, t, row_ok);
-    Tile<D> pf[2];
+    constexpr int MNPF = FDL_ATTN_MNPF;  // K tiles in flight
+    Tile<D> pf[MNPF];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MNPF; ++i)
       load_tile<D>(pf[i], a, s_page, tb, h, min(tb + i, te - 1) * KT, false, threadIdx.x);
     u32x4 qf[D / 32];
     load_q<D>(a, r, h, row_ok, g, qf);
     float lr = kNegInf;
     if (row_ok) lr = p.splits == 1 ? lse_ws[rh] : merge_row<4>(a, p, rh, D, 0, nullptr);
+    // A row that sees no key has LSE -inf; subtracting +inf instead sends
+    // every exp2 to 0.
+    const float lsafe = lr == kNegInf ? __builtin_huge_valf() : lr;
 
-    for (int tile0 = tb; tile0 < te; tile0 += 2) {
+    // Same uniform ring as pass 1: no branch around a load.
+    const int te_r = tb + (te - tb + MNPF - 1) / MNPF * MNPF;
+    for (int tile0 = tb; tile0 < te_r; tile0 += MNPF) {
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
+    for (int ii = 0; ii < MNPF; ++ii) {
       const int tile = tile0 + ii;
-      if (tile >= te) break;
-      const int buf = ii;
+      const bool have = tile < te;
+      const int buf = ii & 1;
       store_tile<D>(pf[ii], klds[buf], nullptr, false, threadIdx.x);
-      load_tile<D>(pf[ii], a, s_page, tb, h, min(tile + 2, te - 1) * KT, false, threadIdx.x);
+      load_tile<D>(pf[ii], a, s_page, tb, h, min(tile + MNPF, te - 1) * KT, false, threadIdx.x);
       lds_barrier();
+      if (have) {
       const int key0 = tile * KT;
-      f32x4 s[2];
-      scores<D>(klds[buf], qf, lane, s);
+      const int tv = tile_vis(vis, key0);
       float pv[8];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int e = 0; e < 8; ++e) pv[e] = 0.f;
+      if (tv != 0) {
+        f32x4 s[2];
+        scores<D>(klds[buf], qf, lane, s);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int jj = key0 + 8 * g + 4 * mt + e;
-          pv[mt * 4 + e] = (lr != kNegInf && vis(jj)) ? fast_exp2(s[mt][e] * a.scale_log2 - lr) : 0.f;
-        }
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = fast_exp2(s[mt][e] * a.scale_log2 - lsafe);
+            pv[mt * 4 + e] = (tv == 2 || vis(key0 + 8 * g + 4 * mt + e)) ? x : 0.f;
+          }
+      }
       // Reduce over the 16 rows of the wave (lanes sharing g): reduce-scatter.
       const int b3 = (j >> 3) & 1, b2 = (j >> 2) & 1, b1 = (j >> 1) & 1;
       float q4[4];
@@ -491,8 +553,9 @@ __global__ __launch_bounds__(256) void attn_mass_kernel(AttnArgs a, AttnPlan p) 
       const float other = shfl_xor(q1, 1);
       const float tot = (j & 1) ? other + q1 : q1 + other;
       if ((j & 1) == 0) wsum[wave][8 * g + 4 * b3 + 2 * b2 + b1] = tot;
+      }
       lds_barrier();
-      if (threadIdx.x < KT) {
+      if (have && threadIdx.x < KT) {
         const int k = threadIdx.x;
         const float sum = ((wsum[0][k] + wsum[1][k]) + wsum[2][k]) + wsum[3][k];
         macc[(tile - tb) * KT + k] += sum;
@@ -526,7 +589,7 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnArgs a, AttnPlan p
   const int b = blockIdx.x / per_b;
   const int jj = (blockIdx.x % per_b) * blockDim.x + threadIdx.x;
   if (jj >= a.mass_stride) return;
-  const int L = a.kv_len[b];
+  const int L = min(a.kv_len[b], a.max_kv_len);
   float sum = 0.f;
   if (jj < L) {
     const float *mp = reinterpret_cast<const float *>(a.ws + p.off_mass_part) +
@@ -543,18 +606,283 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnArgs a, AttnPlan p
   a.mass[(size_t)b * a.mass_stride + jj] = sum;
 }
 
+
+// Row-group attention: one workgroup per (sequence, head, 16-row group) over
+// the whole cached length.  The workgroup therefore ends with every row's
+// final log-sum-exp and needs no split merge; with the mass requested it also
+// needs no second pass over K.  8 waves = 8 key groups, wave w taking tiles
+// w, w + 8, ...  A wave's K operands load straight from HBM into MFMA
+// registers (lane j of M-tile mt reads 16 bytes of key 8(j/4) + 4mt + j%4, the
+// permutation that leaves lane group g holding keys 8g .. 8g+7 of S^T); its V
+// tile passes through a wave-private LDS buffer for the transposing read, so
+// the key loop has no workgroup barrier.  Two tiles per wave are in flight.
+// With the mass requested each wave keeps its scaled scores (at most MAXT
+// tiles) in registers and, once the workgroup has combined the waves' maxima
+// and normalisers, sums exp2(s - LSE) over its 16 rows for each of its keys.
+constexpr int kRowWaves = 8;
+
+template <int D, int MAXT, bool MASS>
+__global__ __launch_bounds__(512) void attn_rows_kernel(AttnArgs a, AttnPlan p) {
+  constexpr int KS = D / 32;            // MFMA k-steps per key row
+  constexpr int CH = D / 8;             // 16-byte chunks per key row
+  constexpr int VLD = KT * CH / 64;     // V chunks per lane per tile
+  constexpr int NST = 2;                // tiles in flight per wave
+  static_assert(kRowWaves * 16 * D * 4 <= kRowWaves * KT * kVPad<D> * 2, "merge scratch");
+  __shared__ uint16_t vbuf[kRowWaves][KT][kVPad<D>];
+  __shared__ int s_page[kMaxPages];
+  __shared__ float s_ml[kRowWaves][16][2];
+  __shared__ float s_inv[16];
+
+  // Blocks are dealt to the 8 XCDs round-robin; map them so that the row
+  // groups of one (sequence, head) run on one XCD and share its L2.
+  const int nb = gridDim.x;
+  int u = blockIdx.x;
+  if ((nb & 7) == 0) u = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
+  const int rg = u % p.rgroups;
+  u /= p.rgroups;
+  const int h = u % a.c.H;
+  const int b = u / a.c.H;
+  const SeqInfo si = seq_info(a, b);
+  const int t0 = rg * 16;
+  if (t0 >= si.nrows) return;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, j = lane & 15;
+  const int t = t0 + j;  // local row of this lane
+  const bool row_ok = t < si.nrows;
+  const int r = si.r0 + (row_ok ? t : 0);
+  const Vis vis = row_vis(si, t, row_ok);
+  const int tiles = (si.L + KT - 1) / KT;
+  const int n_w = tiles > w ? (tiles - 1 - w) / kRowWaves + 1 : 0;  // this wave's tiles
+
+  stage_pages(a, b, 0, tiles, s_page);
+  u32x4 qf[KS];
+  load_q<D>(a, r, h, row_ok, g, qf);
+  lds_barrier();
+
+  struct Stage {
+    u32x4 k[2 * KS];
+    u32x4 v[VLD];
+  };
+  // Loads of the wave's kk-th tile.  Past the wave's last tile the same number
+  // of load instructions is issued at one fixed 16-byte address (every lane
+  // alike), so the count of loads in flight never depends on the data.
+  auto issue = [&](Stage &st, int kk) {
+    const bool real = kk < n_w;
+    const int key0 = (w + kRowWaves * kk) * KT;
+    size_t base = 0;
+    if (real) {
+      const int page = s_page[key0 / a.c.bs];
+      base = (((size_t)page * a.c.H + h) * a.c.bs + (key0 % a.c.bs)) * D;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int key = 8 * (j >> 2) + 4 * mt + (j & 3);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        st.k[mt * KS + ks] =
+            ld16(a.c.k + (real ? base + (size_t)key * D + 32 * ks + 8 * g : (size_t)0));
+    }
+#pragma unroll
+    for (int i = 0; i < VLD; ++i)
+      st.v[i] = ld16(a.c.v + (real ? base + (size_t)(lane + 64 * i) * 8 : (size_t)0));
+  };
+
+  f32x4 o[D / 16];
+#pragma unroll
+  for (int dm = 0; dm < D / 16; ++dm) o[dm] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf, l = 0.f;
+  uint16_t(*vb)[kVPad<D>] = vbuf[w];
+
+  // One tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  xs receives the
+  // scaled scores (-inf where not visible).
+  auto process = [&](const Stage &st, int kk, float *xs) {
+    const int key0 = (w + kRowWaves * kk) * KT;
+    const int tv = tile_vis(vis, key0);
+    if (tv == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xs[e] = kNegInf;
+      return;
+    }
+    f32x4 s[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma16(st.k[mt * KS + ks], qf[ks], acc);
+      s[mt] = acc;
+    }
+    const bool part = key0 + KT > si.L;
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+      const int c = lane + 64 * i;
+      const int key = c / CH;
+      st16(&vb[key][(c % CH) * 8],
+           part && key0 + key >= si.L ? u32x4{0u, 0u, 0u, 0u} : st.v[i]);
+    }
+    const u32x4 pb = tile_softmax<D / 16>(s, vis, tv, key0, g, a.scale_log2, m, l, o, xs);
+#pragma unroll
+    for (int dm = 0; dm < D / 16; ++dm) o[dm] = mfma16(vt_operand<D>(vb, dm, lane), pb, o[dm]);
+  };
+
+  Stage st[NST];
+  float sc[MASS ? MAXT : 1][8];
+  if (n_w > 0) {
+#pragma unroll
+    for (int i = 0; i < NST; ++i) issue(st[i], i);
+    if constexpr (MASS) {
+#pragma unroll
+      for (int kk = 0; kk < MAXT; ++kk) {
+        if (kk < n_w) process(st[kk % NST], kk, sc[kk]);
+        issue(st[kk % NST], kk + NST);
+      }
+    } else {
+      for (int kk0 = 0; kk0 < n_w; kk0 += NST) {
+#pragma unroll
+        for (int i = 0; i < NST; ++i) {
+          if (kk0 + i < n_w) process(st[i], kk0 + i, sc[0]);
+          issue(st[i], kk0 + i + NST);
+        }
+      }
+    }
+  }
+
+  // Combine the 8 waves (fixed wave order): maxima and normalisers per row,
+  // then the rescaled partial outputs through LDS (reusing the V buffers).
+  if (g == 0) {
+    s_ml[w][j][0] = m;
+    s_ml[w][j][1] = l;
+  }
+  lds_barrier();
+  float mx = kNegInf;
+#pragma unroll
+  for (int ww = 0; ww < kRowWaves; ++ww) mx = fmaxf(mx, s_ml[ww][j][0]);
+  float lsum = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < kRowWaves; ++ww) {
+    const float mw = s_ml[ww][j][0];
+    lsum += mw == kNegInf ? 0.f : s_ml[ww][j][1] * exp2f(mw - mx);
+  }
+  const float fself = m == kNegInf ? 0.f : exp2f(m - mx);
+  const float lse = lsum > 0.f ? mx + log2f(lsum) : kNegInf;
+  float *ob = reinterpret_cast<float *>(&vbuf[0][0][0]);  // [8 waves][16 rows][D]
+#pragma unroll
+  for (int dm = 0; dm < D / 16; ++dm)
+    *reinterpret_cast<f32x4 *>(&ob[(w * 16 + j) * D + 16 * dm + 4 * g]) = o[dm] * fself;
+  if (w == 0 && g == 0) s_inv[j] = lsum > 0.f ? 1.f / lsum : 0.f;
+  lds_barrier();
+  if (threadIdx.x < 16 * D / 4) {
+    const int row = threadIdx.x / (D / 4), f4 = (threadIdx.x % (D / 4)) * 4;
+    f32x4 acc = *reinterpret_cast<const f32x4 *>(&ob[row * D + f4]);
+#pragma unroll
+    for (int ww = 1; ww < kRowWaves; ++ww)
+      acc += *reinterpret_cast<const f32x4 *>(&ob[(ww * 16 + row) * D + f4]);
+    if (t0 + row < si.nrows)
+      *reinterpret_cast<f32x4 *>(a.out + ((size_t)(si.r0 + t0 + row) * a.c.H + h) * D + f4) =
+          acc * s_inv[row];
+  }
+
+  if constexpr (MASS) {
+    // Mass of the wave's keys over its 16 rows: a reduce-scatter over the
+    // 16 row lanes leaves lanes j, j^1 with one key each.
+    float *mp = reinterpret_cast<float *>(a.ws + p.off_mass_part) +
+                (((size_t)b * a.c.H + h) * p.rgroups + rg) * a.mass_stride;
+    const int b3 = (j >> 3) & 1, b2 = (j >> 2) & 1, b1 = (j >> 1) & 1;
+#pragma unroll
+    for (int kk = 0; kk < MAXT; ++kk) {
+      if (kk >= n_w) break;
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pv[e] = (sc[kk][e] != kNegInf && lse != kNegInf) ? fast_exp2(sc[kk][e] - lse) : 0.f;
+      float q4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float give = b3 ? pv[i] : pv[i + 4];
+        const float keep = b3 ? pv[i + 4] : pv[i];
+        q4[i] = keep + shfl_xor(give, 8);
+      }
+      float q2[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float give = b2 ? q4[i] : q4[i + 2];
+        const float keep = b2 ? q4[i + 2] : q4[i];
+        q2[i] = keep + shfl_xor(give, 4);
+      }
+      const float give = b1 ? q2[0] : q2[1];
+      const float keep = b1 ? q2[1] : q2[0];
+      const float q1 = keep + shfl_xor(give, 2);
+      const float other = shfl_xor(q1, 1);
+      const float tot = (j & 1) ? other + q1 : q1 + other;
+      const int jj = (w + kRowWaves * kk) * KT + 8 * g + 4 * b3 + 2 * b2 + b1;
+      if ((j & 1) == 0 && jj < si.L) mp[jj] = tot;
+    }
+  }
+}
+
+// Mass of the row-group path: mass[b][j] = sum over heads and row groups (in
+// that fixed order) of the partial sums; zero from kv_len to the stride.
+__global__ __launch_bounds__(256) void attn_rows_mass_kernel(AttnArgs a, AttnPlan p) {
+  const int per_b = (a.mass_stride + 255) / 256;
+  const int b = blockIdx.x / per_b;
+  const int jj = (blockIdx.x % per_b) * blockDim.x + threadIdx.x;
+  if (jj >= a.mass_stride) return;
+  const int L = min(a.kv_len[b], a.max_kv_len);
+  float sum = 0.f;
+  if (jj < L) {
+    const int nrows = a.cu_rows[b + 1] - a.cu_rows[b];
+    const int nrg = min(p.rgroups, (nrows + 15) / 16);
+    const float *mp = reinterpret_cast<const float *>(a.ws + p.off_mass_part) +
+                      (size_t)b * a.c.H * p.rgroups * a.mass_stride + jj;
+    const int n = a.c.H * p.rgroups;
+    for (int i0 = 0; i0 < n; i0 += 32) {
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int hr = i0 + i;
+        v[i] = (hr < n && hr % p.rgroups < nrg) ? mp[(size_t)hr * a.mass_stride] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) sum += v[i];
+    }
+  }
+  a.mass[(size_t)b * a.mass_stride + jj] = sum;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+// Row-group path only when the split path cannot fill the GPU (few
+// sequences x heads) and the mass is asked for: there it saves the split
+// merge and the second pass over K, which at that size cost more than the
+// row groups' repeated reads of the head's keys (served from L2).
+#ifndef FDL_ATTN_ROWS_MAX_GRID
+#define FDL_ATTN_ROWS_MAX_GRID 256
+#endif
+
 AttnPlan plan_attention(int batch, int rows, int H, int D, int max_kv_len,
                         int max_rows_per_seq, int mass_stride) {
   AttnPlan p{};
-  p.row_tiles = max(1, (max_rows_per_seq + 63) / 64);
   const int max_tiles = max(1, (max_kv_len + KT - 1) / KT);
+  // Row-group path: with the mass, while each wave's scores fit in registers
+  // (at most 4 tiles per wave, 1024 keys) and the grid is small.
+  const bool mass = mass_stride > 0;
+  const int rgroups = max(1, (max_rows_per_seq + 15) / 16);
+  if (mass && max_tiles <= kRowWaves * 4 && (long)batch * H * rgroups <= FDL_ATTN_ROWS_MAX_GRID) {
+    p.rows_path = 1;
+    p.rgroups = rgroups;
+    p.maxt = max_tiles <= kRowWaves ? 1 : max_tiles <= 2 * kRowWaves ? 2 : 4;
+    if (mass) {
+      p.off_mass_part = 0;
+      p.bytes = align256((size_t)batch * H * p.rgroups * mass_stride * sizeof(float));
+    }
+    return p;
+  }
+  p.row_tiles = max(1, (max_rows_per_seq + 63) / 64);
   const long base = (long)batch * p.row_tiles * H;
 #ifndef FDL_ATTN_UNITS
-#define FDL_ATTN_UNITS 256
+#define FDL_ATTN_UNITS 128
 #endif
   int splits = (int)((FDL_ATTN_UNITS + base - 1) / max(base, 1L));
   splits = max(1, min(splits, (max_tiles + 1) / 2));
@@ -582,7 +910,28 @@ AttnPlan plan_attention(int batch, int rows, int H, int D, int max_kv_len,
   return p;
 }
 
+template <int D>
+hipError_t launch_rows(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
+  const dim3 grid(a.batch * a.c.H * p.rgroups), block(kRowWaves * 64);
+  if (!a.mass) {
+    hipLaunchKernelGGL((attn_rows_kernel<D, 1, false>), grid, block, 0, s, a, p);
+    return hipGetLastError();
+  }
+  if (p.maxt == 1)
+    hipLaunchKernelGGL((attn_rows_kernel<D, 1, true>), grid, block, 0, s, a, p);
+  else if (p.maxt == 2)
+    hipLaunchKernelGGL((attn_rows_kernel<D, 2, true>), grid, block, 0, s, a, p);
+  else
+    hipLaunchKernelGGL((attn_rows_kernel<D, 4, true>), grid, block, 0, s, a, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nb = a.batch * ((a.mass_stride + 255) / 256);
+  hipLaunchKernelGGL(attn_rows_mass_kernel, dim3(nb), dim3(256), 0, s, a, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
+  if (p.rows_path) return a.c.D == 128 ? launch_rows<128>(a, p, s) : launch_rows<64>(a, p, s);
   const int units = a.batch * p.row_tiles * a.c.H * p.splits;
   if (a.c.D == 128) {
     hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(units), dim3(512), 0, s, a, p);

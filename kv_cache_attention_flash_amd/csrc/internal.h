@@ -8,7 +8,7 @@
 namespace fdl {
 
 struct CacheView {
-  int H, D, bs, num_blocks, max_blocks;
+  int H, D, bs, bs_shift, num_blocks, max_blocks;  // bs = 1 << bs_shift
   uint16_t *k, *v;
   const int32_t *block_table;
 };
@@ -28,9 +28,12 @@ size_t flash_cache_workspace_bytes(int rows, int hidden, int H, int D);
 hipError_t launch_flash_cache(const FlashCacheArgs &a, void *ws, size_t ws_bytes, hipStream_t s);
 
 struct AttnPlan {
-  int row_tiles;      // ceil(max_rows_per_seq / 64)
-  int splits;         // KV splits of the first pass
-  int mass_splits;    // KV chunks of the mass pass (0: no mass)
+  int rows_path;      // 1: row-group kernel (whole cache per workgroup)
+  int rgroups;        // ceil(max_rows_per_seq / 16), row-group path
+  int maxt;           // tiles per wave kept for the mass, row-group path
+  int row_tiles;      // ceil(max_rows_per_seq / 64), split path
+  int splits;         // KV splits of the first pass, split path
+  int mass_splits;    // KV chunks of the mass pass (0: no mass), split path
   size_t off_part_o, off_part_ml, off_lse, off_mass_part, bytes;
 };
 
@@ -42,6 +45,7 @@ struct AttnArgs {
   const uint16_t *q;
   int batch, rows;
   const int32_t *cu_rows, *kv_len, *views;
+  int max_kv_len;
   float scale_log2;
   float *out, *mass;
   int mass_stride;

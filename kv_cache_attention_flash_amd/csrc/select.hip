@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void topb_kernel(const float *mass, int stride
   __shared__ int sh[4];
   __shared__ uint32_t cache[kCached];
   const int b = blockIdx.x;
-  const int L = kv_len[b];
+  const int L = min(kv_len[b], stride);  // a length past the row stride is clamped
   const uint32_t *mb = reinterpret_cast<const uint32_t *>(mass + (size_t)b * stride);
   int32_t *ob = out + (size_t)b * topb;
 

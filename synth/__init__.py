@@ -360,6 +360,17 @@ def small_splitk(materialize=True) -> Workload:
                  materialize=materialize)
 
 
+def small_long(materialize=True) -> Workload:
+    """Caches past 1024 keys on a narrow layer (hidden 256, 2 x 64): batch 2,
+    lengths 1500 and 1100 (not multiples of the block size), 24 rows each,
+    top-8."""
+    g = rng(15, 0, STREAM_POS)
+    specs = [SeqSpec(kv_len=1500, window=(1200, 16), tracked=distinct(g, 0, 1200, 8)),
+             SeqSpec(kv_len=1100, window=(1050, 16), tracked=distinct(g, 0, 1050, 8))]
+    return build("small_long_l1500", 15, 256, 2, 64, 32, 1.0e4, specs, topb=8,
+                 materialize=materialize)
+
+
 WORKLOADS = {
     "tiny_h256_l128": tiny_h256,
     "llada8b_b1_l768": llada8b_b1,
@@ -369,4 +380,5 @@ WORKLOADS = {
     "small_verify_b3": small_verify,
     "small_d64_rows150": small_d64_many_rows,
     "small_splitk_h1024": small_splitk,
+    "small_long_l1500": small_long,
 }

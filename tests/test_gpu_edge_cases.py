@@ -167,3 +167,34 @@ def test_verify_long_window():
     want = [O.accept_length(d[i], m[i], c[i], v["threshold"]) for i in range(len(d))]
     assert list(got) == want
     assert want[:3] == [150, 97, 64]
+
+
+@pytest.mark.parametrize("name", ["small_ragged_b5", "small_long_l1500", "small_verify_b3"])
+def test_unused_slots_never_read(name):
+    """NaN in every cache slot at or past kv_len (the tail of each sequence's
+    last page): outputs stay finite and match the oracle, which never reads
+    those slots.  Covers the row-group path (short caches) and the split path
+    with a second mass pass (caches past 1024 keys)."""
+    _banner(f"NaN past kv_len: {name}")
+    wl = synth.WORKLOADS[name]()
+    k, v = wl.k_cache.copy(), wl.v_cache.copy()
+    bs = wl.block_size
+    poisoned = 0
+    for b in range(wl.batch):
+        L = int(wl.kv_len[b])
+        for slot in range(L, -(-L // bs) * bs):
+            blk, off = wl.block_table[b, slot // bs], slot % bs
+            k[blk, :, off, :] = 0x7FC0
+            v[blk, :, off, :] = 0x7FC0
+            poisoned += 1
+    assert poisoned > 0
+    dev = "cuda:0"
+    run = G.GpuRun(wl, dev, k=G.bf16_tensor(k, dev), v=G.bf16_tensor(v, dev)).step()
+    out = run.out.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    ref = G.oracle_step(wl)
+    G.assert_close(out[ref["rows"]], ref["out"], "attention output with NaN past kv_len")
+    if wl.topb:
+        mass = run.mass.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(mass))
+        G.assert_close(mass, ref["mass"], "mass with NaN past kv_len")

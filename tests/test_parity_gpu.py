@@ -75,7 +75,7 @@ def full_check(wl, run=None, seqs=None, staged=True, check_untouched=True):
 
 
 SMALL = ["tiny_h256_l128", "small_ragged_b5", "small_verify_b3", "small_d64_rows150",
-         "small_splitk_h1024"]
+         "small_splitk_h1024", "small_long_l1500"]
 
 
 @pytest.mark.parametrize("name", SMALL)

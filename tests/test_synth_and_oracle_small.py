@@ -8,7 +8,7 @@ import oracle as O
 import synth
 
 SMALL = ["tiny_h256_l128", "small_ragged_b5", "small_verify_b3", "small_d64_rows150",
-         "small_splitk_h1024"]
+         "small_splitk_h1024", "small_long_l1500"]
 
 
 def _check_layout(wl):
