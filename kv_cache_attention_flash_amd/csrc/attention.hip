@@ -459,7 +459,10 @@ __global__ __launch_bounds__(256) void attn_mass_kernel(AttnArgs a, AttnPlan p) 
   __shared__ float wsum[4][KT];
   __shared__ float macc[MAXK];
 
-  int u = blockIdx.x;
+  // Reverse order, blocks and tiles alike: pass 1 read the last units' last
+  // tiles most recently, so they are the likeliest still to sit in the
+  // last-level cache.  Per-key sums do not depend on this order.
+  int u = gridDim.x - 1 - blockIdx.x;
   const int chunk = u % p.mass_splits; u /= p.mass_splits;
   const int h = u % a.c.H;
   const int b = u / a.c.H;
@@ -490,7 +493,7 @@ __global__ __launch_bounds__(256) void attn_mass_kernel(AttnArgs a, AttnPlan p) 
     Tile<D> pf[MNPF];
 #pragma unroll
     for (int i = 0; i < MNPF; ++i)
-      load_tile<D>(pf[i], a, s_page, tb, h, min(tb + i, te - 1) * KT, false, threadIdx.x);
+      load_tile<D>(pf[i], a, s_page, tb, h, max(te - 1 - i, tb) * KT, false, threadIdx.x);
     u32x4 qf[D / 32];
     load_q<D>(a, r, h, row_ok, g, qf);
     float lr = kNegInf;
@@ -500,15 +503,15 @@ __global__ __launch_bounds__(256) void attn_mass_kernel(AttnArgs a, AttnPlan p) 
     const float lsafe = lr == kNegInf ? __builtin_huge_valf() : lr;
 
     // Same uniform ring as pass 1: no branch around a load.
-    const int te_r = tb + (te - tb + MNPF - 1) / MNPF * MNPF;
-    for (int tile0 = tb; tile0 < te_r; tile0 += MNPF) {
+    const int nt_r = (te - tb + MNPF - 1) / MNPF * MNPF;
+    for (int it0 = 0; it0 < nt_r; it0 += MNPF) {
 #pragma unroll
     for (int ii = 0; ii < MNPF; ++ii) {
-      const int tile = tile0 + ii;
-      const bool have = tile < te;
+      const int tile = te - 1 - (it0 + ii);  // descending
+      const bool have = tile >= tb;
       const int buf = ii & 1;
       store_tile<D>(pf[ii], klds[buf], nullptr, false, threadIdx.x);
-      load_tile<D>(pf[ii], a, s_page, tb, h, min(tile + MNPF, te - 1) * KT, false, threadIdx.x);
+      load_tile<D>(pf[ii], a, s_page, tb, h, max(tile - MNPF, tb) * KT, false, threadIdx.x);
       lds_barrier();
       if (have) {
       const int key0 = tile * KT;

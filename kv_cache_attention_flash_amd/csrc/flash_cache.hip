@@ -13,7 +13,7 @@
 //   qkv_splitk_kernel  up to 64 active rows (the decode regime, where reading
 //                      the weight dominates): each workgroup streams a slice
 //                      of the weight once, staged through LDS in whole lines;
-//   qkv_tiled_kernel   more rows: a 2-D tiled MFMA GEMM (32x32x16 bf16).
+//   qkv_gemm_kernel    more rows: a 2-D tiled MFMA GEMM (32x32x16 bf16).
 // Both finish in an fp32 epilogue: rotation with an fp64-reduced angle, bf16
 // rounding (RNE), Q to its buffer and K/V scattered through the block table.
 // Partial sums are always added in a fixed order, so results are bitwise
@@ -25,7 +25,7 @@ namespace fdl {
 
 namespace {
 
-constexpr double kTwoPi = 6.283185307179586476925286766559;
+constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
 
 // Largest b with cu_rows[b] <= r (empty sequences are skipped over).
 __device__ __forceinline__ int row_to_seq(const int32_t *cu_rows, int batch, int r) {
@@ -37,18 +37,20 @@ __device__ __forceinline__ int row_to_seq(const int32_t *cu_rows, int batch, int
   return lo;
 }
 
-// Rotary frequency base^(-2i/D) in fp64.
+// Rotary frequency base^(-2i/D), in turns (revolutions) per position, fp64.
 __device__ __forceinline__ double rope_inv_freq(int i, int D, double log2_base) {
-  return exp2(-(2.0 * (double)i / (double)D) * log2_base);
+  return exp2(-(2.0 * (double)i / (double)D) * log2_base) * kInvTwoPi;
 }
 
-// cos/sin of position * inv_freq: angle and its reduction to [-pi, pi] in
-// fp64, the trigonometric functions in fp32 on the reduced angle.
-__device__ __forceinline__ void rope_cs(int pos, double inv_freq, float &c, float &s) {
-  double ang = (double)pos * inv_freq;
-  double k = rint(ang * (1.0 / kTwoPi));
-  double red = fma(-k, kTwoPi, ang);
-  sincosf((float)red, &s, &c);
+// cos/sin of the angle position * frequency: the angle in turns and its
+// reduction to [-1/2, 1/2] in fp64, then the hardware sine and cosine
+// (v_sin_f32 / v_cos_f32 take turns; absolute error far below the bf16
+// rounding that follows).
+__device__ __forceinline__ void rope_cs(int pos, double turns_per_pos, float &c, float &s) {
+  double t = (double)pos * turns_per_pos;
+  t -= rint(t);
+  s = __builtin_amdgcn_sinf((float)t);
+  c = __builtin_amdgcn_cosf((float)t);
 }
 
 // Rotate (Q and K parts), round and store one rotary pair of one row.
@@ -329,23 +331,31 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(FlashCacheArgs a, Split
 
 
 // Tiled projection for many active rows (prefill-like batches), where the
-// product is MFMA-bound.  A workgroup computes BM rows x 128 output features
-// = 64 rotary pairs (tile columns 0..63 are the pairs' first elements, 64..127
-// their partners), with 4 waves as 2 (rows) x 2 (pair halves): wave (wm, wn)
-// owns BM/2 rows and pairs 32*wn .. 32*wn+31 through two 32x32 accumulator
-// columns (first elements, partners), so each lane holds both elements of its
-// rotary pairs and rotates them in registers.  v_mfma_f32_32x32x16_bf16 on
-// 64-element reduction stages staged through double-buffered LDS with a
-// (row / 2) % 8 XOR swizzle of the 16-byte slots (16 consecutive rows hit
-// distinct banks).  Workgroups of one feature tile are dealt to one XCD so the
-// weight tile is shared through its L2.
-template <int BM>
-__global__ __launch_bounds__(256) void qkv_tiled_kernel(FlashCacheArgs a, int nrow_tiles,
-                                                        int ncol_tiles) {
-  constexpr int BN = 128, BK = 64, PIECES = BK / 8;  // 8 slots of 16 B per row
-  constexpr int MTW = BM / 64;                       // 32-row M tiles per wave
-  constexpr int AL = BM * PIECES / 256, BL = BN * PIECES / 256;
-  __shared__ u32x4 lds[2][(BM + BN) * PIECES];
+// product is MFMA-bound.  A workgroup computes BM rows x
+// 32*NWN rotary pairs (tile columns: the pairs' first elements, then their
+// partners), with 2 x NWN waves: wave (wm, wn) owns BM/2 rows and pairs
+// 32*wn .. 32*wn+31 through 32x32 accumulator columns (first elements,
+// partners), so each lane holds both elements of its pairs and rotates them in
+// registers.  K advances 32 elements at a time through double-buffered LDS
+// (four 16-byte slots per row, XOR-swizzled by (row / 4) % 4: a 16-byte read
+// is served 16 lanes at a time from 64 banks, and 16 consecutive rows then land
+// on 16 distinct 16-byte bank groups); NREG register stages of global loads
+// run ahead of the LDS stores, and every iteration issues the same loads
+// (clamped past the end) so the compiler waits for exactly one stage.
+// Workgroups of one feature tile are dealt to one XCD so the weight tile is
+// shared through its L2.
+template <int BM, int NWN, int NREG>
+__global__ __launch_bounds__(128 * NWN) void qkv_gemm_kernel(FlashCacheArgs a, int nrow_tiles,
+                                                              int ncol_tiles) {
+  constexpr int NT = 128 * NWN;                        // threads
+  constexpr int BP = 32 * NWN;                         // pairs per tile
+  constexpr int BN = 2 * BP;                           // output features per tile
+  constexpr int BK = 32, PIECES = BK / 8;              // 4 slots of 16 B per row
+  constexpr int MTW = BM / 64;                         // 32-row M tiles per wave
+  constexpr int TR = BM + BN;                          // staged rows per step
+  constexpr int LD = TR * PIECES / NT;                 // 16-byte loads per thread per step
+  static_assert(TR * PIECES % NT == 0, "step must split evenly over the threads");
+  __shared__ u32x4 lds[2][TR * PIECES];
   __shared__ int s_blk[BM], s_off[BM], s_pos[BM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -356,10 +366,9 @@ __global__ __launch_bounds__(256) void qkv_tiled_kernel(FlashCacheArgs a, int nr
   int idx = blockIdx.x;
   if (nb % 8 == 0) idx = (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8;
   const int ct = idx / nrow_tiles, rtile = idx % nrow_tiles;
-  const int row0 = rtile * BM, pair0 = ct * 64;
+  const int row0 = rtile * BM, pair0 = ct * BP;
 
-  // Row metadata for the tile's rows.
-  for (int rl = tid; rl < BM; rl += 256) {
+  for (int rl = tid; rl < BM; rl += NT) {
     const int r = row0 + rl;
     if (r < a.rows) {
       int blk, off, pos;
@@ -370,45 +379,38 @@ __global__ __launch_bounds__(256) void qkv_tiled_kernel(FlashCacheArgs a, int nr
     }
   }
 
-  // Global sources of this thread's 16-byte chunks (row tid/8 + 32 i, slot tid%8).
+  // This thread's 16-byte chunks of a step: staged row tid / 4 + (NT / 4) * i, slot tid % 4.
   const int piece = tid % PIECES;
-  const uint16_t *asrc[AL];
-  const uint16_t *bsrc[BL];
-  int aslot[AL], bslot[BL];
+  const uint16_t *src[LD];
+  int slot[LD];
 #pragma unroll
-  for (int i = 0; i < AL; ++i) {
-    const int tr = tid / PIECES + 32 * i;
-    const int r = min(row0 + tr, a.rows - 1);
-    asrc[i] = a.x + (size_t)r * hidden + piece * 8;
-    aslot[i] = tr * PIECES + (piece ^ ((tr >> 1) & 7));
+  for (int i = 0; i < LD; ++i) {
+    const int tr = tid / PIECES + (NT / PIECES) * i;
+    if (tr < BM) {
+      const int r = min(row0 + tr, a.rows - 1);
+      src[i] = a.x + (size_t)r * hidden + piece * 8;
+    } else {
+      const int c = tr - BM;  // 0..BN-1: first elements, then partners
+      int p = pair0 + (c % BP);
+      p = p < total_pairs ? p : total_pairs - 1;
+      const int feat = (p / half) * D + (p % half) + (c >= BP ? half : 0);
+      src[i] = a.w + (size_t)feat * hidden + piece * 8;
+    }
+    slot[i] = tr * PIECES + (piece ^ ((tr >> 2) & 3));
   }
-#pragma unroll
-  for (int i = 0; i < BL; ++i) {
-    const int tr = tid / PIECES + 32 * i;  // 0..127: first elements, then partners
-    int p = pair0 + (tr & 63);
-    p = p < total_pairs ? p : total_pairs - 1;
-    const int feat = (p / half) * D + (p % half) + (tr >= 64 ? half : 0);
-    bsrc[i] = a.w + (size_t)feat * hidden + piece * 8;
-    const int lr = BM + tr;
-    bslot[i] = lr * PIECES + (piece ^ ((lr >> 1) & 7));
-  }
-  u32x4 ra[AL], rb[BL];
   const int nk = hidden / BK;
-  auto load = [&](int kt) {
+  u32x4 rg[NREG][LD];
+  auto load = [&](u32x4 *r, int kt) {
     const int k = min(kt, nk - 1) * BK;
 #pragma unroll
-    for (int i = 0; i < AL; ++i) ra[i] = ld16(asrc[i] + k);
-#pragma unroll
-    for (int i = 0; i < BL; ++i) rb[i] = ld16(bsrc[i] + k);
+    for (int i = 0; i < LD; ++i) r[i] = ld16(src[i] + k);
   };
-  auto store = [&](u32x4 *buf) {
+  auto store = [&](u32x4 *buf, const u32x4 *r) {
 #pragma unroll
-    for (int i = 0; i < AL; ++i) buf[aslot[i]] = ra[i];
-#pragma unroll
-    for (int i = 0; i < BL; ++i) buf[bslot[i]] = rb[i];
+    for (int i = 0; i < LD; ++i) buf[slot[i]] = r[i];
   };
 
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / NWN, wn = wave % NWN;
   const int l32 = lane & 31, hi = lane >> 5;
   f32x16 acc[MTW][2];
 #pragma unroll
@@ -418,34 +420,45 @@ __global__ __launch_bounds__(256) void qkv_tiled_kernel(FlashCacheArgs a, int nr
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[mt][c][e] = 0.f;
 
-  load(0);
-  store(lds[0]);
-  load(1);
-  lds_barrier();
-  for (int kt = 0; kt < nk; ++kt) {
-    const u32x4 *buf = lds[kt & 1];
+  // Prologue: step 0 in LDS, steps 1 .. NREG in registers.
+  {
+    u32x4 r0[LD];
+    load(r0, 0);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int pc = 2 * ks + hi;
-      u32x4 af[MTW], bf[2];
+    for (int s = 0; s < NREG; ++s) load(rg[s], 1 + s);
+    store(lds[0], r0);
+  }
+  const int nk_r = (nk + NREG - 1) / NREG * NREG;
+  for (int k0 = 0; k0 < nk_r; k0 += NREG) {
 #pragma unroll
-      for (int mt = 0; mt < MTW; ++mt) {
-        const int row = wm * (BM / 2) + 32 * mt + l32;
-        af[mt] = buf[row * PIECES + (pc ^ ((row >> 1) & 7))];
+    for (int s = 0; s < NREG; ++s) {
+      const int kt = k0 + s;
+      lds_barrier();
+      if (kt < nk) {
+        const u32x4 *buf = lds[kt & 1];
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+          const int pc = 2 * ks + hi;
+          u32x4 af[MTW], bfr[2];
+#pragma unroll
+          for (int mt = 0; mt < MTW; ++mt) {
+            const int row = wm * (BM / 2) + 32 * mt + l32;
+            af[mt] = buf[row * PIECES + (pc ^ ((row >> 2) & 3))];
+          }
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int row = BM + BP * c + 32 * wn + l32;
+            bfr[c] = buf[row * PIECES + (pc ^ ((row >> 2) & 3))];
+          }
+#pragma unroll
+          for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) acc[mt][c] = mfma32(af[mt], bfr[c], acc[mt][c]);
+        }
       }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int row = BM + 64 * c + 32 * wn + l32;
-        bf[c] = buf[row * PIECES + (pc ^ ((row >> 1) & 7))];
-      }
-#pragma unroll
-      for (int mt = 0; mt < MTW; ++mt)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) acc[mt][c] = mfma32(af[mt], bf[c], acc[mt][c]);
+      store(lds[(kt + 1) & 1], rg[s]);  // step kt + 1 (a clamped repeat past the end)
+      load(rg[s], kt + 1 + NREG);
     }
-    store(lds[(kt + 1) & 1]);
-    load(kt + 2);
-    lds_barrier();
   }
 
   // Epilogue: lane holds pair pair0 + 32 wn + l32 for 16 rows per M tile.
@@ -538,6 +551,10 @@ hipError_t launch_flash_cache(const FlashCacheArgs &a, void *ws, size_t ws_bytes
         hipLaunchKernelGGL((qkv_splitk_kernel<kSplitNTW, kSplitNGW, FDL_FC_NST, 16, FDL_FC_SNW, FDL_FC_KC>), grid, block,
                            0, s, a, sp);
         break;
+      case 32:
+        hipLaunchKernelGGL((qkv_splitk_kernel<kSplitNTW, kSplitNGW, FDL_FC_NST, 32, FDL_FC_SNW, FDL_FC_KC>), grid, block,
+                           0, s, a, sp);
+        break;
       default:
         hipLaunchKernelGGL((qkv_splitk_kernel<kSplitNTW, kSplitNGW, FDL_FC_NST, 0, FDL_FC_SNW, FDL_FC_KC>), grid, block, 0,
                            s, a, sp);
@@ -549,18 +566,13 @@ hipError_t launch_flash_cache(const FlashCacheArgs &a, void *ws, size_t ws_bytes
                        a, sp);
     return hipGetLastError();
   }
-  // More than 64 rows (or a hidden size the chunking does not divide): tiled
-  // MFMA kernel, row tile chosen so that the grid fills the 256 CUs a few times.
+  // More than 64 rows (or a hidden size the chunking does not divide): the
+  // tiled MFMA kernel, 128 rows x 128 rotary pairs per workgroup.
   const int total_pairs = 3 * a.c.H * (a.c.D / 2);
-  const int ncol = (total_pairs + 63) / 64;
-  int bm = 128;  // (a 256-row tile spills its accumulators)
-  while (bm > 64 && (long)((a.rows + bm - 1) / bm) * ncol < 512) bm /= 2;
-  const int nrow = (a.rows + bm - 1) / bm;
-  const dim3 grid(nrow * ncol), block(256);
-  if (bm == 128)
-    hipLaunchKernelGGL((qkv_tiled_kernel<128>), grid, block, 0, s, a, nrow, ncol);
-  else
-    hipLaunchKernelGGL((qkv_tiled_kernel<64>), grid, block, 0, s, a, nrow, ncol);
+  constexpr int BM = 128, NWN = 4, BP = 32 * NWN;
+  const int nrow = (a.rows + BM - 1) / BM, ncol = (total_pairs + BP - 1) / BP;
+  hipLaunchKernelGGL((qkv_gemm_kernel<BM, NWN, 2>), dim3(nrow * ncol), dim3(128 * NWN), 0, s, a,
+                     nrow, ncol);
   return hipGetLastError();
 }
 
