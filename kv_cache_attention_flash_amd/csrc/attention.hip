@@ -823,33 +823,47 @@ __global__ __launch_bounds__(512) void attn_rows_kernel(AttnArgs a, AttnPlan p) 
   }
 }
 
-// Mass of the row-group path: mass[b][j] = sum over heads and row groups (in
-// that fixed order) of the partial sums; zero from kv_len to the stride.
+// Mass of the row-group path: mass[b][j] = sum over heads and row groups of the
+// partial sums, zero from kv_len to the stride.  A block covers 32 keys with
+// 8 lanes per key: lane group g adds partials g, g + 8, g + 16, ... in order,
+// then the 8 group sums are added in group order (a fixed order throughout).
 __global__ __launch_bounds__(256) void attn_rows_mass_kernel(AttnArgs a, AttnPlan p) {
-  const int per_b = (a.mass_stride + 255) / 256;
+  __shared__ float part[8][32];
+  const int per_b = (a.mass_stride + 31) / 32;
   const int b = blockIdx.x / per_b;
-  const int jj = (blockIdx.x % per_b) * blockDim.x + threadIdx.x;
-  if (jj >= a.mass_stride) return;
+  const int k = threadIdx.x & 31, grp = threadIdx.x >> 5;
+  const int jj = (blockIdx.x % per_b) * 32 + k;
+  // Partial loads are issued with the length loads (every entry read lies in
+  // the workspace; entries no workgroup wrote are selected away, not added).
+  const int jc = min(jj, a.mass_stride - 1);
+  const float *mp = reinterpret_cast<const float *>(a.ws + p.off_mass_part) +
+                    (size_t)b * a.c.H * p.rgroups * a.mass_stride + jc;
+  const int n = a.c.H * p.rgroups;
   const int L = min(a.kv_len[b], a.max_kv_len);
+  const int nrows = a.cu_rows[b + 1] - a.cu_rows[b];
+  const int nrg = min(p.rgroups, (nrows + 15) / 16);
   float sum = 0.f;
-  if (jj < L) {
-    const int nrows = a.cu_rows[b + 1] - a.cu_rows[b];
-    const int nrg = min(p.rgroups, (nrows + 15) / 16);
-    const float *mp = reinterpret_cast<const float *>(a.ws + p.off_mass_part) +
-                      (size_t)b * a.c.H * p.rgroups * a.mass_stride + jj;
-    const int n = a.c.H * p.rgroups;
-    for (int i0 = 0; i0 < n; i0 += 32) {
-      float v[32];
+  for (int hr0 = grp; hr0 < n; hr0 += 8 * 16) {
+    float v[16];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int hr = i0 + i;
-        v[i] = (hr < n && hr % p.rgroups < nrg) ? mp[(size_t)hr * a.mass_stride] : 0.f;
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int hr = min(hr0 + 8 * i, n - 1);
+      v[i] = mp[(size_t)hr * a.mass_stride];
+    }
 #pragma unroll
-      for (int i = 0; i < 32; ++i) sum += v[i];
+    for (int i = 0; i < 16; ++i) {
+      const int hr = hr0 + 8 * i;
+      sum += (hr < n && hr % p.rgroups < nrg && jj < L) ? v[i] : 0.f;
     }
   }
-  a.mass[(size_t)b * a.mass_stride + jj] = sum;
+  part[grp][k] = sum;
+  __syncthreads();
+  if (grp == 0 && jj < a.mass_stride) {
+    float t = part[0][k];
+#pragma unroll
+    for (int g = 1; g < 8; ++g) t += part[g][k];
+    a.mass[(size_t)b * a.mass_stride + jj] = t;
+  }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -928,7 +942,7 @@ hipError_t launch_rows(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
     hipLaunchKernelGGL((attn_rows_kernel<D, 4, true>), grid, block, 0, s, a, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nb = a.batch * ((a.mass_stride + 255) / 256);
+  const int nb = a.batch * ((a.mass_stride + 31) / 32);
   hipLaunchKernelGGL(attn_rows_mass_kernel, dim3(nb), dim3(256), 0, s, a, p);
   return hipGetLastError();
 }

@@ -68,17 +68,18 @@ __global__ __launch_bounds__(256) void topb_kernel(const float *mass, int stride
   __shared__ int sh[4];
   __shared__ uint32_t cache[kCached];
   const int b = blockIdx.x;
-  const int L = min(kv_len[b], stride);  // a length past the row stride is clamped
   const uint32_t *mb = reinterpret_cast<const uint32_t *>(mass + (size_t)b * stride);
+  // The row's loads go out with the length's (the stride bounds them).
+  const bool cached = stride <= kCached;
+  if (cached)
+    for (int k = threadIdx.x; k < stride; k += blockDim.x) cache[k] = mb[k];
+  const int L = min(kv_len[b], stride);  // a length past the row stride is clamped
   int32_t *ob = out + (size_t)b * topb;
 
   if (L <= topb) {
     for (int k = threadIdx.x; k < topb; k += blockDim.x) ob[k] = k < L ? k : -1;
     return;
   }
-  const bool cached = L <= kCached;
-  if (cached)
-    for (int k = threadIdx.x; k < L; k += blockDim.x) cache[k] = mb[k];
   auto key = [&](int k) -> uint32_t { return cached ? cache[k] : mb[k]; };
 
   uint32_t prefix = 0, pmask = 0;
