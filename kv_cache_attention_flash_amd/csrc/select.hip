@@ -14,7 +14,8 @@ namespace fdl {
 namespace {
 
 // Exclusive prefix count of `flag` over the block (in thread order) and the
-// block total.  256 threads = 4 waves.
+// block total; NW waves.
+template <int NW>
 __device__ __forceinline__ int block_excl_count(bool flag, int &total, int *sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const unsigned long long bal = __ballot(flag);
@@ -24,7 +25,7 @@ __device__ __forceinline__ int block_excl_count(bool flag, int &total, int *sh) 
   int before = 0;
   total = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int c = sh[w];
     before += w < wave ? c : 0;
     total += c;
@@ -33,7 +34,8 @@ __device__ __forceinline__ int block_excl_count(bool flag, int &total, int *sh) 
   return before + in_wave;
 }
 
-// Inclusive prefix sum over the 256 threads of the block (thread order).
+// Inclusive prefix sum over the block's threads (thread order); NW waves.
+template <int NW>
 __device__ __forceinline__ unsigned block_incl_sum(unsigned v, unsigned *sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -45,39 +47,44 @@ __device__ __forceinline__ unsigned block_incl_sum(unsigned v, unsigned *sh) {
   __syncthreads();
   unsigned before = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) before += w < wave ? sh[w] : 0u;
+  for (int w = 0; w < NW; ++w) before += w < wave ? sh[w] : 0u;
   __syncthreads();
   return v + before;
 }
 
-// One workgroup (256 threads) per sequence.  Masses are non-negative, so their
+// One workgroup of NT threads per sequence (1024 for long rows, so a few
+// sequences still keep many waves busy).  Masses are non-negative, so their
 // fp32 bit patterns order like the values: a 4-pass radix select over 8-bit
-// digits (LDS histogram, then a parallel scan from the top digit down) finds
-// the bit pattern T of the B-th largest mass; every key above T is taken, and
-// keys equal to T are taken in index order until B are chosen.  A final
-// in-order scan writes the chosen indices ascending.  Rows of up to kCached
-// keys are held in LDS across the passes.
+// digits (LDS histogram, then a parallel scan from the top digit down over
+// the first 256 threads) finds the bit pattern T of the B-th largest mass;
+// every key above T is taken, and keys equal to T are taken in index order
+// until B are chosen.  A final in-order scan writes the chosen indices
+// ascending.  Rows of up to kCached keys (by stride) are held in LDS across
+// the passes.
 constexpr int kCached = 8192;
 
-__global__ __launch_bounds__(256) void topb_kernel(const float *mass, int stride,
-                                                   const int32_t *kv_len, int topb,
-                                                   int32_t *out) {
+template <int NT>
+__global__ __launch_bounds__(NT) void topb_kernel(const float *mass, int stride,
+                                                  const int32_t *kv_len, int topb,
+                                                  int32_t *out) {
+  constexpr int NW = NT / 64;
+  static_assert(NT >= 256, "the digit scan needs one thread per bin");
   __shared__ unsigned hist[256];
   __shared__ unsigned s_digit, s_remaining;
-  __shared__ unsigned shs[4];
-  __shared__ int sh[4];
+  __shared__ unsigned shs[NW];
+  __shared__ int sh[NW];
   __shared__ uint32_t cache[kCached];
   const int b = blockIdx.x;
   const uint32_t *mb = reinterpret_cast<const uint32_t *>(mass + (size_t)b * stride);
   // The row's loads go out with the length's (the stride bounds them).
   const bool cached = stride <= kCached;
   if (cached)
-    for (int k = threadIdx.x; k < stride; k += blockDim.x) cache[k] = mb[k];
+    for (int k = threadIdx.x; k < stride; k += NT) cache[k] = mb[k];
   const int L = min(kv_len[b], stride);  // a length past the row stride is clamped
   int32_t *ob = out + (size_t)b * topb;
 
   if (L <= topb) {
-    for (int k = threadIdx.x; k < topb; k += blockDim.x) ob[k] = k < L ? k : -1;
+    for (int k = threadIdx.x; k < topb; k += NT) ob[k] = k < L ? k : -1;
     return;
   }
   auto key = [&](int k) -> uint32_t { return cached ? cache[k] : mb[k]; };
@@ -86,17 +93,17 @@ __global__ __launch_bounds__(256) void topb_kernel(const float *mass, int stride
   unsigned remaining = (unsigned)topb;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    hist[threadIdx.x] = 0;
+    if (threadIdx.x < 256) hist[threadIdx.x] = 0;
     __syncthreads();
-    for (int k = threadIdx.x; k < L; k += blockDim.x) {
+    for (int k = threadIdx.x; k < L; k += NT) {
       const uint32_t u = key(k);
       if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
     }
     __syncthreads();
-    // Thread t looks at digit 255 - t; cum = number of candidates with digit >= it.
-    const unsigned c = hist[255 - threadIdx.x];
-    const unsigned cum = block_incl_sum(c, shs);
-    if (cum >= remaining && cum - c < remaining) {
+    // Thread t < 256 looks at digit 255 - t; cum = candidates with digit >= it.
+    const unsigned c = threadIdx.x < 256 ? hist[255 - threadIdx.x] : 0u;
+    const unsigned cum = block_incl_sum<NW>(c, shs);
+    if (c > 0 && cum >= remaining && cum - c < remaining) {
       s_digit = 255u - threadIdx.x;
       s_remaining = remaining - (cum - c);
     }
@@ -109,15 +116,15 @@ __global__ __launch_bounds__(256) void topb_kernel(const float *mass, int stride
   const uint32_t T = prefix;
   // `remaining` keys equal to T are needed (after all keys above T).
   int base_sel = 0, base_eq = 0;
-  for (int c0 = 0; c0 < L; c0 += blockDim.x) {
+  for (int c0 = 0; c0 < L; c0 += NT) {
     const int k = c0 + threadIdx.x;
     const uint32_t u = k < L ? key(k) : 0u;
     const bool gt = k < L && u > T;
     const bool eq = k < L && u == T;
     int eq_total, sel_total;
-    const int eq_rank = base_eq + block_excl_count(eq, eq_total, sh);
+    const int eq_rank = base_eq + block_excl_count<NW>(eq, eq_total, sh);
     const bool sel = gt || (eq && eq_rank < (int)remaining);
-    const int pos = base_sel + block_excl_count(sel, sel_total, sh);
+    const int pos = base_sel + block_excl_count<NW>(sel, sel_total, sh);
     if (sel && pos < topb) ob[pos] = k;
     base_eq += eq_total;
     base_sel += sel_total;
@@ -152,7 +159,12 @@ __global__ __launch_bounds__(256) void verify_kernel(const int32_t *draft, const
 
 hipError_t launch_topb(const float *mass, int stride, const int32_t *kv_len, int batch,
                        int topb, int32_t *out, hipStream_t s) {
-  hipLaunchKernelGGL(topb_kernel, dim3(batch), dim3(256), 0, s, mass, stride, kv_len, topb, out);
+  if (stride > 2048)
+    hipLaunchKernelGGL(topb_kernel<1024>, dim3(batch), dim3(1024), 0, s, mass, stride, kv_len,
+                       topb, out);
+  else
+    hipLaunchKernelGGL(topb_kernel<256>, dim3(batch), dim3(256), 0, s, mass, stride, kv_len, topb,
+                       out);
   return hipGetLastError();
 }
 

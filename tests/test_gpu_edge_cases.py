@@ -144,12 +144,16 @@ def test_topb_crafted_masses():
             rng.random(4096, dtype=np.float32),
             np.zeros(4096, np.float32)]
     lens = [7, 4096, 3000, 10]
-    mass = torch.from_numpy(np.stack(rows)).to(dev)
-    kv = G.i32(lens, dev)
-    for b_ in (1, 3, 8, 32, 100):
-        got = fd.track_topb(mass, kv, b_).cpu().numpy()
-        for i, L in enumerate(lens):
-            assert np.array_equal(got[i], O.top_b(rows[i].astype(np.float64), L, b_)), (b_, i)
+    # stride 4096 (the 1024-thread workgroup) and 2000 (the 256-thread one)
+    for width in (4096, 2000):
+        mass = torch.from_numpy(np.ascontiguousarray(np.stack(rows)[:, :width])).to(dev)
+        wl = [min(L, width) for L in lens]
+        kv = G.i32(wl, dev)
+        for b_ in (1, 3, 8, 32, 100):
+            got = fd.track_topb(mass, kv, b_).cpu().numpy()
+            for i, L in enumerate(wl):
+                want = O.top_b(rows[i][:width].astype(np.float64), L, b_)
+                assert np.array_equal(got[i], want), (width, b_, i)
 
 
 def test_verify_long_window():
