@@ -42,6 +42,7 @@ MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "kv_cache_attention_flash_amd", "csrc")
 SOURCES = {"flash_cache_step": [os.path.join(CSRC, "flash_cache.hip")],
+           "flash_cache_step_unfused": [os.path.join(CSRC, "flash_cache.hip")],
            "scheduled_attention": [os.path.join(CSRC, "attention.hip")]}
 ROTATION_BYTES = 560e6
 
@@ -235,7 +236,7 @@ def roofline_entry(call, wl, ms, workload):
     """Roofline of one library call from its measured average duration; the
     bound is HBM if the call's algorithmic flops per byte are below the ridge
     point (2.5 PFLOP/s / 8 TB/s = 312.5), else MFMA."""
-    if call == "flash_cache_step":
+    if call.startswith("flash_cache_step"):
         nbytes, flops = flash_cache_bytes(wl), flash_cache_flops(wl)
     else:
         nbytes, flops = attention_bytes(wl), attention_flops(wl)
@@ -268,6 +269,9 @@ def main():
                     help="resident copies rotated per step (0: enough to exceed ~560 MB)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle timing for the cpu_baseline (0 disables it)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the three-launch ablation (flash_cache_step_unfused) instead of the "
+                         "fused projection step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 100 MiB device-to-device copy before timing (a dispatch of "
                          "known size that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -317,7 +321,8 @@ def main():
 
     def make_step(cache, x, w):
         return fd.DecodeStep(cache, x, w, cu, pos, slots, kv, wl.rope_base, wl.max_kv_len,
-                             max_rows, views=views, topb=wl.topb, verify=verify)
+                             max_rows, views=views, topb=wl.topb, verify=verify,
+                             unfused=args.unfused)
 
     # units[i % len(units)] = the per-layer steps that make up logical step i
     units = []
@@ -374,7 +379,8 @@ def main():
     att_ms = float(np.mean([ht.ms(e[1], e[2]) for evs in ev for e in evs]))
     value = wl.rows * layers_per_step / (ms_per_step / 1e3)
 
-    rf_fc = roofline_entry("flash_cache_step", wl, fcs_ms, args.workload)
+    fc_call = "flash_cache_step_unfused" if args.unfused else "flash_cache_step"
+    rf_fc = roofline_entry(fc_call, wl, fcs_ms, args.workload)
     rf_att = roofline_entry("scheduled_attention", wl, att_ms, args.workload)
     dominant, other = (rf_fc, rf_att) if fcs_ms >= att_ms else (rf_att, rf_fc)
     log(f"step {ms_per_step * 1e3:.1f} us ({layers_per_step} layer(s)); flash_cache_step "
@@ -405,6 +411,8 @@ def main():
     hd = wl.num_heads * wl.head_dim
     sb = flash_cache_bytes(wl) + attention_bytes(wl)
     tail = (" + scheduled_attention(+mass) + track_topb" if wl.topb else " + scheduled_attention")
+    if args.unfused:
+        tail += " [ablation: flash_cache_step_unfused, three launches with HBM intermediates]"
     tail += " + verify_accept" if verify is not None else ""
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s/layer", "n_gpus": 1,

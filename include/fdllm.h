@@ -111,6 +111,26 @@ int flash_cache_step(const fdl_kv_cache *cache, const void *x, int32_t hidden,
                      int64_t *slot_mapping_out, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+/* Ablation of Flash-Cache [P4 para 1: the prior practice of separate kernel
+ * launches per layer that move intermediates to and from HBM]: the same
+ * results as flash_cache_step (bitwise: the same projection kernels and the
+ * same rotation/rounding helper), computed as three launches -- the
+ * projection writes fp32 Y [num_rows][3HD] to the workspace, a rotary kernel
+ * writes bf16 Q to q_out and bf16 K, V rows to workspace staging, and a
+ * scatter kernel copies them into the paged cache.  Same arguments and error
+ * behaviour as flash_cache_step; the workspace must hold
+ * fdl_flash_cache_unfused_workspace_bytes(...) bytes. */
+int flash_cache_step_unfused(const fdl_kv_cache *cache, const void *x, int32_t hidden,
+                             const void *w_qkv, int32_t batch, int32_t num_rows,
+                             const int32_t *cu_rows, const int32_t *positions,
+                             const int32_t *slots, float rope_base, void *q_out,
+                             int64_t *slot_mapping_out, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/* Workspace bytes flash_cache_step_unfused needs (0 for invalid sizes). */
+size_t fdl_flash_cache_unfused_workspace_bytes(int32_t num_rows, int32_t hidden,
+                                               int32_t num_heads, int32_t head_dim);
+
 /* Workspace bytes flash_cache_step needs for these sizes (0: none; then
  * workspace may be NULL).  It holds the fp32 partial sums of a reduction split
  * across workgroups; two calls that may run at the same time must not share

@@ -26,9 +26,10 @@ import torch
 from . import _lib
 from ._lib import FdlError, KVCacheStruct  # noqa: F401
 
-__all__ = ["PagedKVCache", "flash_cache_step", "scheduled_attention", "track_topb",
-           "verify_accept", "attention_workspace_bytes", "flash_cache_workspace_bytes",
-           "DecodeStep", "FdlError", "load"]
+__all__ = ["PagedKVCache", "flash_cache_step", "flash_cache_step_unfused", "scheduled_attention",
+           "track_topb", "verify_accept", "attention_workspace_bytes",
+           "flash_cache_workspace_bytes", "flash_cache_unfused_workspace_bytes", "DecodeStep",
+           "FdlError", "load"]
 
 
 def load():
@@ -112,10 +113,8 @@ class PagedKVCache:
                              self.v_cache.data_ptr(), self.block_table.data_ptr())
 
 
-def flash_cache_step(cache: PagedKVCache, x, w_qkv, cu_rows, positions, slots, rope_base,
-                     q_out=None, slot_mapping_out=None, stream=None):
-    """Fused QKV projection + RoPE + K/V cache write for the active rows.
-    Returns (q_out bf16 [R, H, D], slot_mapping int64 [R])."""
+def _flash_cache_call(unfused, cache, x, w_qkv, cu_rows, positions, slots, rope_base, q_out,
+                      slot_mapping_out, stream):
     lib = _lib.load()
     _need(x, "x", torch.bfloat16, 2)
     _need(w_qkv, "w_qkv", torch.bfloat16, 2)
@@ -136,15 +135,39 @@ def flash_cache_step(cache: PagedKVCache, x, w_qkv, cu_rows, positions, slots, r
     _need(slot_mapping_out, "slot_mapping_out", torch.int64, 1)
     cs = cache.struct()
     sh = _stream(stream, x.device)
-    need = flash_cache_workspace_bytes(r, hid, h, d)
+    if unfused:
+        need = flash_cache_unfused_workspace_bytes(r, hid, h, d)
+        fn, name = lib.flash_cache_step_unfused, "flash_cache_step_unfused"
+    else:
+        need = flash_cache_workspace_bytes(r, hid, h, d)
+        fn, name = lib.flash_cache_step, "flash_cache_step"
     ws = _flash_cache_workspace(x.device, sh, need) if need else None
-    st = lib.flash_cache_step(ctypes.byref(cs), x.data_ptr(), hid, w_qkv.data_ptr(), batch, r,
-                              cu_rows.data_ptr(), positions.data_ptr(), slots.data_ptr(),
-                              float(rope_base), q_out.data_ptr(), slot_mapping_out.data_ptr(),
-                              _ptr(ws), need, sh)
-    _lib.check("flash_cache_step", st)
+    st = fn(ctypes.byref(cs), x.data_ptr(), hid, w_qkv.data_ptr(), batch, r, cu_rows.data_ptr(),
+            positions.data_ptr(), slots.data_ptr(), float(rope_base), q_out.data_ptr(),
+            slot_mapping_out.data_ptr(), _ptr(ws), need, sh)
+    _lib.check(name, st)
     return q_out, slot_mapping_out
 
+
+def flash_cache_step(cache: PagedKVCache, x, w_qkv, cu_rows, positions, slots, rope_base,
+                     q_out=None, slot_mapping_out=None, stream=None):
+    """Fused QKV projection + RoPE + K/V cache write for the active rows.
+    Returns (q_out bf16 [R, H, D], slot_mapping int64 [R])."""
+    return _flash_cache_call(False, cache, x, w_qkv, cu_rows, positions, slots, rope_base, q_out,
+                             slot_mapping_out, stream)
+
+
+def flash_cache_step_unfused(cache: PagedKVCache, x, w_qkv, cu_rows, positions, slots,
+                             rope_base, q_out=None, slot_mapping_out=None, stream=None):
+    """The same step as three launches with the intermediates in HBM (the
+    unfused ablation); bitwise the same results as flash_cache_step."""
+    return _flash_cache_call(True, cache, x, w_qkv, cu_rows, positions, slots, rope_base, q_out,
+                             slot_mapping_out, stream)
+
+
+def flash_cache_unfused_workspace_bytes(num_rows, hidden, num_heads, head_dim) -> int:
+    return int(_lib.load().fdl_flash_cache_unfused_workspace_bytes(num_rows, hidden, num_heads,
+                                                                  head_dim))
 
 def attention_workspace_bytes(batch, num_rows, num_heads, head_dim, max_kv_len,
                               max_rows_per_seq, mass_stride=0) -> int:
@@ -243,7 +266,7 @@ class DecodeStep:
 
     def __init__(self, cache: PagedKVCache, x, w_qkv, cu_rows, positions, slots, kv_len,
                  rope_base, max_kv_len, max_rows_per_seq, views=None, topb=0,
-                 softmax_scale=0.0, verify=None):
+                 softmax_scale=0.0, verify=None, unfused=False):
         self.lib = _lib.load()
         dev = x.device
         r = x.shape[0]
@@ -266,7 +289,11 @@ class DecodeStep:
         need = attention_workspace_bytes(self.batch, r, h, d, int(max_kv_len),
                                          int(max_rows_per_seq), ms)
         self.workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
-        fneed = flash_cache_workspace_bytes(r, x.shape[1], h, d)
+        # unfused: the three-launch ablation of the projection step
+        self._fc_fn = self.lib.flash_cache_step_unfused if unfused else self.lib.flash_cache_step
+        self._fc_name = "flash_cache_step_unfused" if unfused else "flash_cache_step"
+        fneed = (flash_cache_unfused_workspace_bytes if unfused else flash_cache_workspace_bytes)(
+            r, x.shape[1], h, d)
         self.fc_workspace = torch.empty((max(fneed, 1),), dtype=torch.uint8, device=dev)
         self.cs = cache.struct()
         self._fcs = (ctypes.byref(self.cs), x.data_ptr(), x.shape[1], w_qkv.data_ptr(),
@@ -292,7 +319,7 @@ class DecodeStep:
                          ctypes.c_float(float(thr)), self.accept_len.data_ptr())
 
     def run_flash_cache(self, stream: int):
-        _lib.check("flash_cache_step", self.lib.flash_cache_step(*self._fcs, stream))
+        _lib.check(self._fc_name, self._fc_fn(*self._fcs, stream))
 
     def run_attention(self, stream: int):
         _lib.check("scheduled_attention", self.lib.scheduled_attention(*self._att, stream))

@@ -31,6 +31,10 @@ EXPORTS = {
                                         c_i32, c_vp, c_vp, c_vp, c_f32, c_vp, c_vp, c_vp, c_size,
                                         c_vp]),
     "fdl_flash_cache_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32]),
+    "flash_cache_step_unfused": (ctypes.c_int, [ctypes.POINTER(KVCacheStruct), c_vp, c_i32, c_vp,
+                                                c_i32, c_i32, c_vp, c_vp, c_vp, c_f32, c_vp, c_vp,
+                                                c_vp, c_size, c_vp]),
+    "fdl_flash_cache_unfused_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32]),
     "scheduled_attention": (ctypes.c_int, [ctypes.POINTER(KVCacheStruct), c_vp, c_i32, c_i32, c_vp,
                                            c_vp, c_i32, c_i32, c_vp, c_f32, c_vp, c_vp, c_i32,
                                            c_vp, c_size, c_vp]),

@@ -67,11 +67,16 @@ int fdl_last_hip_error(void) { return g_last_hip_error; }
 
 const char *fdl_version(void) { return "fdllm 0.1 gfx950"; }
 
-int flash_cache_step(const fdl_kv_cache *cache, const void *x, int32_t hidden, const void *w_qkv,
-                     int32_t batch, int32_t num_rows, const int32_t *cu_rows,
-                     const int32_t *positions, const int32_t *slots, float rope_base,
-                     void *q_out, int64_t *slot_mapping_out, void *workspace,
-                     size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by the fused step and its unfused ablation.
+int flash_cache_common(bool unfused, const fdl_kv_cache *cache, const void *x, int32_t hidden,
+                       const void *w_qkv, int32_t batch, int32_t num_rows,
+                       const int32_t *cu_rows, const int32_t *positions, const int32_t *slots,
+                       float rope_base, void *q_out, int64_t *slot_mapping_out,
+                       void *workspace, size_t workspace_bytes, void *stream) {
   int st = check_cache(cache, true);
   if (st) return st;
   if (batch < 0 || num_rows < 0 || hidden <= 0) return FDL_EINVAL;
@@ -79,8 +84,11 @@ int flash_cache_step(const fdl_kv_cache *cache, const void *x, int32_t hidden, c
   if (hidden % 128 != 0 || hidden > 32768) return FDL_EUNSUPPORTED;
   if (batch == 0 || num_rows == 0) return FDL_OK;
   if (!x || !w_qkv || !cu_rows || !positions || !slots || !q_out) return FDL_EINVAL;
-  const size_t need = fdl::flash_cache_workspace_bytes(num_rows, hidden, cache->num_heads,
-                                                       cache->head_dim);
+  const size_t need =
+      unfused ? fdl::flash_cache_unfused_workspace_bytes(num_rows, hidden, cache->num_heads,
+                                                         cache->head_dim)
+              : fdl::flash_cache_workspace_bytes(num_rows, hidden, cache->num_heads,
+                                                 cache->head_dim);
   if (workspace_bytes < need || (need && !workspace)) return FDL_EWORKSPACE;
   fdl::FlashCacheArgs a;
   a.c = view_of(cache);
@@ -95,8 +103,41 @@ int flash_cache_step(const fdl_kv_cache *cache, const void *x, int32_t hidden, c
   a.log2_base = std::log2((double)rope_base);
   a.q_out = static_cast<uint16_t *>(q_out);
   a.slot_mapping = slot_mapping_out;
-  return hip_status(
-      fdl::launch_flash_cache(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+  a.y_out = nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(unfused ? fdl::launch_flash_cache_unfused(a, workspace, workspace_bytes, s)
+                            : fdl::launch_flash_cache(a, workspace, workspace_bytes, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int flash_cache_step(const fdl_kv_cache *cache, const void *x, int32_t hidden, const void *w_qkv,
+                     int32_t batch, int32_t num_rows, const int32_t *cu_rows,
+                     const int32_t *positions, const int32_t *slots, float rope_base,
+                     void *q_out, int64_t *slot_mapping_out, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+  return flash_cache_common(false, cache, x, hidden, w_qkv, batch, num_rows, cu_rows, positions,
+                            slots, rope_base, q_out, slot_mapping_out, workspace,
+                            workspace_bytes, stream);
+}
+
+int flash_cache_step_unfused(const fdl_kv_cache *cache, const void *x, int32_t hidden,
+                             const void *w_qkv, int32_t batch, int32_t num_rows,
+                             const int32_t *cu_rows, const int32_t *positions,
+                             const int32_t *slots, float rope_base, void *q_out,
+                             int64_t *slot_mapping_out, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  return flash_cache_common(true, cache, x, hidden, w_qkv, batch, num_rows, cu_rows, positions,
+                            slots, rope_base, q_out, slot_mapping_out, workspace,
+                            workspace_bytes, stream);
+}
+
+size_t fdl_flash_cache_unfused_workspace_bytes(int32_t num_rows, int32_t hidden,
+                                               int32_t num_heads, int32_t head_dim) {
+  if (num_rows < 0 || hidden <= 0 || num_heads <= 0 || head_dim <= 0) return 0;
+  return fdl::flash_cache_unfused_workspace_bytes(num_rows, hidden, num_heads, head_dim);
 }
 
 size_t fdl_flash_cache_workspace_bytes(int32_t num_rows, int32_t hidden, int32_t num_heads,

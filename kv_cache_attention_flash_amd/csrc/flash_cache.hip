@@ -53,7 +53,23 @@ __device__ __forceinline__ void rope_cs(int pos, double turns_per_pos, float &c,
   c = __builtin_amdgcn_cosf((float)t);
 }
 
-// Rotate (Q and K parts), round and store one rotary pair of one row.
+// Rotation of one pair (Q and K sections) and bf16 rounding; one helper for
+// the fused epilogue and the unfused rotary kernel, so both round identically.
+__device__ __forceinline__ uint32_t rotate_round(float lo, float hi, int sec, int pos,
+                                                 double turns_per_pos) {
+  if (sec < 2) {
+    float c, s;
+    rope_cs(pos, turns_per_pos, c, s);
+    const float rlo = __builtin_fmaf(lo, c, -(hi * s));
+    const float rhi = __builtin_fmaf(hi, c, lo * s);
+    lo = rlo;
+    hi = rhi;
+  }
+  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+}
+
+// Rotate (Q and K parts), round and store one rotary pair of one row; with
+// y_out set, store the raw fp32 pair instead (the unfused ablation).
 __device__ __forceinline__ void store_pair(const FlashCacheArgs &a, int r, int p, float lo,
                                            float hi, int blk, int off, int pos,
                                            double inv_freq_i) {
@@ -62,14 +78,13 @@ __device__ __forceinline__ void store_pair(const FlashCacheArgs &a, int r, int p
   const int i = p % half;
   const int sec = sh / H;
   const int h = sh % H;
-  if (sec < 2) {
-    float c, s;
-    rope_cs(pos, inv_freq_i, c, s);
-    const float rlo = lo * c - hi * s;
-    const float rhi = hi * c + lo * s;
-    lo = rlo;
-    hi = rhi;
+  if (a.y_out) {
+    float *y = a.y_out + (size_t)r * 3 * H * D + (size_t)sh * D + i;
+    y[0] = lo;
+    y[half] = hi;
+    return;
   }
+  const uint32_t v = rotate_round(lo, hi, sec, pos, inv_freq_i);
   uint16_t *dst;
   if (sec == 0) {
     dst = a.q_out + ((size_t)r * H + h) * D;
@@ -77,8 +92,8 @@ __device__ __forceinline__ void store_pair(const FlashCacheArgs &a, int r, int p
     uint16_t *pool = sec == 1 ? a.c.k : a.c.v;
     dst = pool + (((size_t)blk * H + h) * a.c.bs + off) * D;
   }
-  dst[i] = f32_to_bf16_rne(lo);
-  dst[i + half] = f32_to_bf16_rne(hi);
+  dst[i] = (uint16_t)(v & 0xffffu);
+  dst[i + half] = (uint16_t)(v >> 16);
 }
 
 // Row metadata (physical block, offset, position) of row r; also writes the
@@ -476,6 +491,44 @@ __global__ __launch_bounds__(128 * NWN) void qkv_gemm_kernel(FlashCacheArgs a, i
     }
 }
 
+
+
+// Unfused ablation, stage 2: rotary embedding and bf16 rounding from the fp32
+// projection in HBM; Q to its buffer, K and V rows to staging buffers
+// [rows][H][D].  One thread per (row, rotary pair).
+__global__ __launch_bounds__(256) void rope_round_kernel(FlashCacheArgs a, const float *y,
+                                                          uint16_t *k_stage, uint16_t *v_stage) {
+  const int H = a.c.H, D = a.c.D, half = D >> 1;
+  const int pairs = 3 * H * half;
+  const size_t item = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (item >= (size_t)a.rows * pairs) return;
+  const int r = (int)(item / pairs), p = (int)(item % pairs);
+  const int sh = p / half, i = p % half, sec = sh / H, h = sh % H;
+  const float *yr = y + (size_t)r * 3 * H * D + (size_t)sh * D + i;
+  const uint32_t v = rotate_round(yr[0], yr[half], sec, a.positions[r],
+                                  rope_inv_freq(i, D, a.log2_base));
+  uint16_t *dst = (sec == 0 ? a.q_out : sec == 1 ? k_stage : v_stage) + ((size_t)r * H + h) * D;
+  dst[i] = (uint16_t)(v & 0xffffu);
+  dst[i + half] = (uint16_t)(v >> 16);
+}
+
+// Unfused ablation, stage 3: copy the staged K and V rows into the paged cache
+// and write the slot mapping.  One thread per (row, head, 16-byte chunk).
+__global__ __launch_bounds__(256) void scatter_kv_kernel(FlashCacheArgs a, const uint16_t *k_stage,
+                                                          const uint16_t *v_stage) {
+  const int H = a.c.H, D = a.c.D, ch = D / 8;
+  const size_t item = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (item >= (size_t)a.rows * H * ch) return;
+  const int r = (int)(item / (H * ch)), rem = (int)(item % (H * ch));
+  const int h = rem / ch, c = rem % ch;
+  int blk, off, pos;
+  row_meta(a, r, h == 0 && c == 0, blk, off, pos);
+  const size_t src = ((size_t)r * H + h) * D + c * 8;
+  const size_t dst = (((size_t)blk * H + h) * a.c.bs + off) * D + c * 8;
+  st16(a.c.k + dst, ld16(k_stage + src));
+  st16(a.c.v + dst, ld16(v_stage + src));
+}
+
 }  // namespace
 
 // Tile shape of the split-K projection: NTW 16-feature tiles per wave, NGW
@@ -573,6 +626,42 @@ hipError_t launch_flash_cache(const FlashCacheArgs &a, void *ws, size_t ws_bytes
   const int nrow = (a.rows + BM - 1) / BM, ncol = (total_pairs + BP - 1) / BP;
   hipLaunchKernelGGL((qkv_gemm_kernel<BM, NWN, 2>), dim3(nrow * ncol), dim3(128 * NWN), 0, s, a,
                      nrow, ncol);
+  return hipGetLastError();
+}
+
+size_t flash_cache_unfused_workspace_bytes(int rows, int hidden, int H, int D) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return al(flash_cache_workspace_bytes(rows, hidden, H, D)) +
+         al((size_t)rows * 3 * H * D * sizeof(float)) + 2 * al((size_t)rows * H * D * 2);
+}
+
+// The same step as three launches with the intermediates in HBM: projection
+// (fp32 Y out), rotary + rounding (bf16 staging out), cache scatter.  The
+// projection kernels and the rounding helper are the fused path's own, so the
+// results are bitwise identical; only the memory traffic differs.
+hipError_t launch_flash_cache_unfused(const FlashCacheArgs &a, void *ws, size_t ws_bytes,
+                                      hipStream_t s) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const int H = a.c.H, D = a.c.D;
+  const size_t part = al(flash_cache_workspace_bytes(a.rows, a.hidden, H, D));
+  const size_t ybytes = al((size_t)a.rows * 3 * H * D * sizeof(float));
+  const size_t sbytes = al((size_t)a.rows * H * D * 2);
+  if (ws_bytes < part + ybytes + 2 * sbytes || !ws) return hipErrorInvalidValue;
+  char *base = static_cast<char *>(ws);
+  FlashCacheArgs g = a;
+  g.y_out = reinterpret_cast<float *>(base + part);
+  g.slot_mapping = nullptr;
+  hipError_t e = launch_flash_cache(g, part ? base : nullptr, part, s);
+  if (e != hipSuccess) return e;
+  uint16_t *ks = reinterpret_cast<uint16_t *>(base + part + ybytes);
+  uint16_t *vs = reinterpret_cast<uint16_t *>(base + part + ybytes + sbytes);
+  const size_t n1 = (size_t)a.rows * 3 * H * (D / 2);
+  hipLaunchKernelGGL(rope_round_kernel, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s, a,
+                     g.y_out, ks, vs);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t n2 = (size_t)a.rows * H * (D / 8);
+  hipLaunchKernelGGL(scatter_kv_kernel, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, s, a,
+                     ks, vs);
   return hipGetLastError();
 }
 

@@ -22,10 +22,14 @@ struct FlashCacheArgs {
   double log2_base;
   uint16_t *q_out;
   int64_t *slot_mapping;
+  float *y_out;  // non-null: store the raw fp32 projection [rows][3HD] instead (unfused ablation)
 };
 
 size_t flash_cache_workspace_bytes(int rows, int hidden, int H, int D);
 hipError_t launch_flash_cache(const FlashCacheArgs &a, void *ws, size_t ws_bytes, hipStream_t s);
+size_t flash_cache_unfused_workspace_bytes(int rows, int hidden, int H, int D);
+hipError_t launch_flash_cache_unfused(const FlashCacheArgs &a, void *ws, size_t ws_bytes,
+                                      hipStream_t s);
 
 struct AttnPlan {
   int rows_path;      // 1: row-group kernel (whole cache per workgroup)

@@ -84,8 +84,26 @@ def test_flash_cache_step_validation(lib):
                                 fake, None, fake, ws2 - 1, None) == _lib.FDL_EWORKSPACE
     assert lib.flash_cache_step(ctypes.byref(c2), fake, 1024, fake, 1, 40, fake, fake, fake, 1e4,
                                 fake, None, None, ws2, None) == _lib.FDL_EWORKSPACE
-    assert lib.fdl_flash_cache_workspace_bytes(65, 4096, 32, 128) == 0   # row-strip kernel
+    assert lib.fdl_flash_cache_workspace_bytes(65, 4096, 32, 128) == 0   # tiled kernel
     assert lib.fdl_flash_cache_workspace_bytes(-1, 4096, 32, 128) == 0
+
+
+def test_unfused_ablation_validation(lib):
+    """The unfused ablation validates like the fused step and needs its fp32
+    intermediate and staging buffers in the workspace."""
+    fake = 0x10000
+    r, hid, h, d = 64, 4096, 32, 128
+    ws = lib.fdl_flash_cache_unfused_workspace_bytes(r, hid, h, d)
+    assert ws >= r * 3 * h * d * 4 + 2 * r * h * d * 2      # fp32 Y + bf16 K/V staging
+    assert lib.fdl_flash_cache_unfused_workspace_bytes(-1, hid, h, d) == 0
+    c = _cache(h=h, d=d)
+    call = lambda wsb, wsp=fake, hid_=hid, rows=r: lib.flash_cache_step_unfused(
+        ctypes.byref(c), fake, hid_, fake, 1, rows, fake, fake, fake, 5e5, fake, None, wsp, wsb,
+        None)
+    assert call(ws - 1) == _lib.FDL_EWORKSPACE
+    assert call(ws, wsp=None) == _lib.FDL_EWORKSPACE
+    assert call(ws, hid_=200) == _lib.FDL_EUNSUPPORTED
+    assert call(ws, rows=0) == _lib.FDL_OK
 
 
 def test_attention_validation_and_workspace(lib):

@@ -202,3 +202,26 @@ def test_unused_slots_never_read(name):
         mass = run.mass.cpu().numpy().astype(np.float64)
         assert np.all(np.isfinite(mass))
         G.assert_close(mass, ref["mass"], "mass with NaN past kv_len")
+
+
+@pytest.mark.parametrize("name", ["small_ragged_b5", "small_splitk_h1024", "small_d64_rows150",
+                                  "llada8b_b1_l768", "llada8b_verify_b8"])
+def test_unfused_ablation_is_bitwise_equal(name):
+    """flash_cache_step_unfused (projection -> fp32 Y in HBM -> rotary ->
+    staging -> scatter) gives bitwise the fused step's Q, slot mapping and cache
+    contents: the same projection kernels and rounding helper, only the traffic
+    differs.  Covers the split-K path (with and without a split reduction) and
+    the tiled path."""
+    _banner(f"unfused ablation vs fused: {name}")
+    fd = _fd()
+    dev = "cuda:0"
+    wl = synth.WORKLOADS[name]()
+    outs = []
+    for fn in (fd.flash_cache_step, fd.flash_cache_step_unfused):
+        run = G.GpuRun(wl, dev)
+        q, sm = fn(run.cache, run.x, run.w, run.cu, run.pos, run.slots, wl.rope_base)
+        torch.cuda.synchronize()
+        outs.append((G.bits_of(q), sm.cpu().numpy(), G.bits_of(run.cache.k_cache),
+                     G.bits_of(run.cache.v_cache)))
+    for what, a_, b_ in zip(("q", "slot mapping", "K cache", "V cache"), outs[0], outs[1]):
+        assert np.array_equal(a_, b_), what
