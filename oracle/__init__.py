@@ -15,6 +15,9 @@ Sources (PUBLIC web pages about one preprint; cited by short key):
   tokens.  P4 para 3: Flash-Verify two-view mask and causal-order acceptance).
 * [P2] the arXiv abstract page of the same preprint (abstract).
 
+``reference`` holds one per-layer step; ``loop`` chains such steps into
+a weight-free multi-step loop (planning rules stated in its docstring).
+
 Every function states the passage it follows.  Where the pages are silent the
 function states the reading it takes; the same readings are listed in the
 repository's design notes.
@@ -36,4 +39,12 @@ from .reference import (  # noqa: F401
     top_b,
     accept_length,
     decode_step,
+)
+from .loop import (  # noqa: F401
+    STAGE_UPDATE,
+    STAGE_REFRESH,
+    STAGE_DONE,
+    plan_step,
+    hidden_rows,
+    decode_loop,
 )

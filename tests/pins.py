@@ -374,4 +374,165 @@ def pin_accept_hand():
         assert got == c["expect"], (c, got)
 
 
+# --- multi-step loop: planning, hidden rows, state carried between steps ------------
+
+def pin_decode_plan_hand():
+    """Hand-worked three-step plan of four sequences (refresh and update
+    stages, finished sequences, capped and negative accept lengths, tracked
+    entries inside the window, past the length, repeated)."""
+    gd = golden("decode_plan_hand.json")
+    f = np.array(gd["frontier0"], np.int32)
+    for t, st in enumerate(gd["steps"]):
+        f, stage, cu, pos, slots = O.plan_step(t, gd["kv_len"], gd["window_len"],
+                                               gd["block_size"], gd["refresh_period"],
+                                               st["tracked"], st["accept"], f)
+        assert list(f) == st["frontier"], (t, list(f))
+        assert list(stage) == st["stage"], (t, list(stage))
+        assert list(cu) == st["cu_rows"], (t, list(cu))
+        assert list(pos) == st["positions"], (t, list(pos))
+        assert list(slots) == st["positions"], (t, "slot = position")
+
+
+def _plan_invariants(t, kv_len, w, bs, k, tracked, accept, f_in, plan):
+    f, stage, cu, pos, slots = plan
+    assert cu[0] == 0 and np.all(np.diff(cu) >= 0) and cu[-1] == len(pos)
+    assert np.array_equal(pos, slots)
+    for b, length in enumerate(kv_len):
+        f0 = min(max(int(f_in[b]), 0), length)
+        if t == 0 or f0 >= length:
+            assert f[b] == f0
+        else:
+            assert f[b] == min(length, f0 + max(1, min(max(int(accept[b]), 0), w)))
+        rows = [int(p) for p in pos[cu[b]:cu[b + 1]]]
+        if f[b] >= length:
+            assert rows == [] and stage[b] == O.STAGE_DONE
+            continue
+        refresh = k > 0 and (t + b) % k == 0
+        assert stage[b] == (O.STAGE_REFRESH if refresh else O.STAGE_UPDATE)
+        w0 = rows[0]
+        assert w0 == ((f[b] // bs) * bs if refresh else f[b])
+        nwin = min(w0 + w, length) - w0
+        assert rows[:nwin] == list(range(w0, w0 + nwin))
+        tr = rows[nwin:]
+        assert all(0 <= p < length and not (w0 <= p < w0 + nwin) for p in tr)
+        assert tr == sorted(set(tr)) and len(rows) == len(set(rows))
+        assert len(rows) <= w + len(tracked[b])
+        # every valid tracked entry outside the window, ascending input, is a row
+        srt = sorted(set(int(p) for p in tracked[b]))
+        want = [p for p in srt if 0 <= p < length and not (w0 <= p < w0 + nwin)]
+        if list(tracked[b]) == srt:
+            assert tr == want
+
+
+def pin_decode_plan_invariants(seed=10):
+    """Random states: window placement, commit rule, finished sequences and
+    tracked-row filtering hold for every sequence."""
+    g = np.random.default_rng(seed)
+    for _ in range(200):
+        batch = int(g.integers(1, 7))
+        bs = int(g.choice([4, 8, 32]))
+        w = int(g.integers(1, 12))
+        nb = int(g.integers(1, 6))
+        k = int(g.integers(0, 4))
+        t = int(g.integers(0, 5))
+        kv_len = [int(v) for v in g.integers(0, 40, batch)]
+        f_in = g.integers(-2, 45, batch)
+        accept = g.integers(-3, 15, batch)
+        tracked = np.sort(g.integers(-1, 45, (batch, nb)), axis=1)
+        if g.random() < 0.3:
+            tracked = g.integers(-1, 45, (batch, nb))
+        plan = O.plan_step(t, kv_len, w, bs, k, tracked, accept, f_in)
+        _plan_invariants(t, kv_len, w, bs, k, tracked, accept, f_in, plan)
+
+
+def pin_hidden_rows_marker():
+    """Each row takes the committed-token table's row when its position lies
+    below the frontier, the masked-token table's row otherwise."""
+    batch, max_len, hid = 3, 10, 4
+    com = np.zeros((batch, max_len, hid), np.uint16)
+    msk = np.zeros((batch, max_len, hid), np.uint16)
+    for b in range(batch):
+        for p in range(max_len):
+            com[b, p] = [b, p, 0, 7]
+            msk[b, p] = [b, p, 1, 7]
+    cu = np.array([0, 3, 3, 5], np.int32)
+    pos = np.array([4, 5, 1, 9, 0], np.int32)
+    front = [5, 0, 9]
+    x = O.hidden_rows(com, msk, cu, pos, front)
+    want = [[0, 4, 0, 7], [0, 5, 1, 7], [0, 1, 0, 7], [2, 9, 1, 7], [2, 0, 0, 7]]
+    assert x.tolist() == want, x.tolist()
+
+
+def _tiny_loop_inputs(seed, steps=3):
+    g = np.random.default_rng(seed)
+    h, d, bs, hid, w, nb = 2, 4, 4, 8, 4, 3
+    kv_len = np.array([14, 9, 6], np.int32)
+    nblk = [-(-int(n) // bs) for n in kv_len]
+    perm = g.permutation(sum(nblk))
+    bt = np.zeros((3, max(nblk)), np.int32)
+    o = 0
+    for b, n in enumerate(nblk):
+        bt[b, :n] = perm[o:o + n]
+        o += n
+    def rnd(shape, scale=1.0):
+        return O.f64_to_bf16_bits(g.standard_normal(shape) * scale)
+    kc = rnd((sum(nblk), h, bs, d))
+    vc = rnd((sum(nblk), h, bs, d))
+    wq = rnd((3 * h * d, hid), 0.3)
+    com = rnd((3, 14, hid))
+    msk = rnd((3, 14, hid))
+    draft = g.integers(0, 5, (steps, 3, w)).astype(np.int32)
+    mask = np.where(g.random((steps, 3, w)) < 0.8, draft, draft + 1).astype(np.int32)
+    conf = g.random((steps, 3, w)).astype(np.float32)
+    return dict(w_bits=wq, num_heads=h, head_dim=d, rope_base=100.0, block_table=bt,
+                block_size=bs, k_cache_bits=kc, v_cache_bits=vc, kv_len=kv_len,
+                hidden_committed=com, hidden_masked=msk, frontier0=np.array([3, 2, 6], np.int32),
+                tracked0=np.array([[0, 1, 9], [0, 5, 8], [0, 1, 2]], np.int32), window_len=w,
+                topb=nb, refresh_period=2, draft=draft, mask=mask, conf=conf,
+                threshold=np.float32(0.5))
+
+
+def pin_decode_loop_carries_state(seed=11):
+    """The loop's step t sees the cache as written by steps 0..t (recomposed
+    here from the single-step functions), takes step t-1's top-B set and
+    accept lengths into its plan, and its masses sum to heads x rows."""
+    a = _tiny_loop_inputs(seed)
+    recs, kc_end, vc_end = O.decode_loop(3, **a)
+    kc, vc = a["k_cache_bits"], a["v_cache_bits"]
+    f = a["frontier0"]
+    tracked, accept = a["tracked0"], np.zeros(3, np.int32)
+    for t, rec in enumerate(recs):
+        f, stage, cu, pos, slots = O.plan_step(t, a["kv_len"], a["window_len"], a["block_size"],
+                                               a["refresh_period"], tracked, accept, f)
+        assert np.array_equal(cu, rec["cu_rows"]) and np.array_equal(pos, rec["positions"])
+        x = O.hidden_rows(a["hidden_committed"], a["hidden_masked"], cu, pos, f)
+        q, kc, vc, _ = O.flash_cache_step(x, a["w_bits"], 2, 4, pos, a["rope_base"], cu, slots,
+                                          a["block_table"], 4, kc, vc)
+        o = O.attention(q, kc, vc, a["block_table"], 4, cu, a["kv_len"])
+        assert np.array_equal(o, rec["out"]), t
+        for b in range(3):
+            nrows = int(cu[b + 1] - cu[b])
+            s = rec["mass"][b].sum()
+            assert abs(s - 2 * nrows) <= 1e-12 * max(1.0, 2 * nrows), (t, b, s)
+        tracked = rec["topb"]
+        accept = np.array([O.accept_length(a["draft"][t][b], a["mask"][t][b], a["conf"][t][b],
+                                           a["threshold"]) for b in range(3)], np.int32)
+        assert np.array_equal(accept, rec["accept"])
+    assert np.array_equal(kc, kc_end) and np.array_equal(vc, vc_end)
+
+
+def pin_decode_loop_closed_form_frontier(seed=12):
+    """With every scan position passing, each step commits the whole window
+    (W tokens) until the sequence is finished: f_t = min(L, f_0 + W t)."""
+    a = _tiny_loop_inputs(seed, steps=4)
+    a["mask"] = a["draft"].copy()
+    a["conf"] = np.ones_like(a["conf"])
+    recs, _, _ = O.decode_loop(4, **a)
+    for t, rec in enumerate(recs):
+        want = np.minimum(a["kv_len"], a["frontier0"] + a["window_len"] * t)
+        assert np.array_equal(rec["frontier"], want), (t, rec["frontier"], want)
+        done = want >= a["kv_len"]
+        assert np.array_equal(np.diff(rec["cu_rows"])[done], np.zeros(int(done.sum())))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -5,10 +5,12 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle.loop as LP
 import oracle.reference as R
 from tests import pins
 
 _orig = {name: getattr(R, name) for name in dir(R) if callable(getattr(R, name))}
+_orig_loop = {name: getattr(LP, name) for name in ("plan_step", "hidden_rows", "decode_loop")}
 
 
 def _truncating_bf16(x):
@@ -126,6 +128,87 @@ def _fcs_rotating_v(x_bits, w_bits, num_heads, head_dim, positions, rope_base, c
     return R.f64_to_bf16_bits(q), kc, vc, ps
 
 
+def _plan_variant(kind):
+    def plan(step, kv_len, window_len, block_size, refresh_period, tracked, accept_len, frontier):
+        batch = len(kv_len)
+        w = int(window_len)
+        new_f = np.zeros(batch, np.int32)
+        stage = np.zeros(batch, np.int32)
+        cu, rows = [0], []
+        for b in range(batch):
+            length = max(0, int(kv_len[b]))
+            f = min(max(int(frontier[b]), 0), length)
+            if step > 0 and f < length:
+                acc = max(int(accept_len[b]), 0)
+                if kind != "no_cap":
+                    acc = min(acc, w)
+                f = min(length, f + (acc if kind == "no_min_commit" else max(1, acc)))
+            new_f[b] = f
+            if f >= length:
+                stage[b] = 2
+                cu.append(len(rows))
+                continue
+            refresh = refresh_period > 0 and (step + b) % refresh_period == 0
+            stage[b] = 1 if refresh else 0
+            w0 = (f // block_size) * block_size if refresh and kind != "unaligned" else f
+            w1 = min(w0 + w, length)
+            rows.extend(range(w0, w1))
+            last = -1
+            for t in tracked[b]:
+                t = int(t)
+                inside = w0 <= t < w1 and kind != "window_dupes"
+                if t < 0 or t >= length or inside or t <= last:
+                    continue
+                rows.append(t)
+                last = t
+            cu.append(len(rows))
+        pos = np.array(rows, np.int32)
+        return new_f, stage, np.array(cu, np.int32), pos, pos.copy()
+    return plan
+
+
+def _hidden_le(hidden_committed, hidden_masked, cu_rows, positions, frontier):
+    cu = np.asarray(cu_rows)
+    out = np.zeros((int(cu[-1]), hidden_committed.shape[-1]), np.uint16)
+    for b in range(len(cu) - 1):
+        for r in range(int(cu[b]), int(cu[b + 1])):
+            p = int(positions[r])
+            out[r] = (hidden_committed if p <= int(frontier[b]) else hidden_masked)[b, p]
+    return out
+
+
+def _loop_variant(kind):
+    def loop(steps, w_bits, num_heads, head_dim, rope_base, block_table, block_size,
+             k_cache_bits, v_cache_bits, kv_len, hidden_committed, hidden_masked, frontier0,
+             tracked0, window_len, topb, refresh_period, draft, mask, conf, threshold,
+             mass_stride=None):
+        kc0, vc0 = k_cache_bits, v_cache_bits
+        kc, vc = kc0, vc0
+        frontier = np.asarray(frontier0, np.int32).copy()
+        tracked = np.asarray(tracked0, np.int32).copy()
+        accept = np.zeros(len(kv_len), np.int32)
+        recs = []
+        for t in range(steps):
+            frontier, stage, cu, pos, slots = LP.plan_step(t, kv_len, window_len, block_size,
+                                                           refresh_period, tracked, accept,
+                                                           frontier)
+            x = LP.hidden_rows(hidden_committed, hidden_masked, cu, pos, frontier)
+            res = R.decode_step(x, w_bits, num_heads, head_dim, pos, rope_base, cu, slots,
+                                block_table, block_size, kc, vc, kv_len, topb=topb,
+                                mass_stride=int(max(kv_len)))
+            if kind != "no_carry":
+                kc, vc = res["k_cache"], res["v_cache"]
+            if kind != "stale_tracked":
+                tracked = np.asarray(res["topb"], np.int32)
+            accept = np.array([R.accept_length(draft[t][b], mask[t][b], conf[t][b], threshold)
+                               for b in range(len(kv_len))], np.int32)
+            recs.append(dict(frontier=frontier.copy(), stage=stage, cu_rows=cu, positions=pos,
+                             x=x, q=res["q"], out=res["out"], mass=res["mass"],
+                             topb=np.asarray(res["topb"], np.int32), accept=accept.copy()))
+        return recs, res["k_cache"], res["v_cache"]
+    return loop
+
+
 MUTANTS = {
     "bf16_truncates": ("f64_to_bf16_bits", _truncating_bf16),
     "gemm_drops_term": ("qkv_projection", _gemm_dropped_term),
@@ -142,13 +225,20 @@ MUTANTS = {
     "accept_ge": ("accept_length", _accept_variant("ge")),
     "accept_no_stop": ("accept_length", _accept_variant("nostop")),
     "v_rotated": ("flash_cache_step", _fcs_rotating_v),
+    "plan_no_min_commit": ("plan_step", _plan_variant("no_min_commit")),
+    "plan_no_cap": ("plan_step", _plan_variant("no_cap")),
+    "plan_window_dupes": ("plan_step", _plan_variant("window_dupes")),
+    "plan_refresh_unaligned": ("plan_step", _plan_variant("unaligned")),
+    "hidden_rows_le": ("hidden_rows", _hidden_le),
+    "loop_no_carry": ("decode_loop", _loop_variant("no_carry")),
+    "loop_stale_tracked": ("decode_loop", _loop_variant("stale_tracked")),
 }
 
 
 @pytest.mark.parametrize("mutant", sorted(MUTANTS))
 def test_some_pin_catches(mutant, monkeypatch):
     name, fn = MUTANTS[mutant]
-    monkeypatch.setattr(R, name, fn)
+    monkeypatch.setattr(LP if name in _orig_loop else R, name, fn)
     if hasattr(oracle, name):
         monkeypatch.setattr(oracle, name, fn)
     caught = []
