@@ -93,7 +93,12 @@ typedef struct fdl_two_view {
  *              nn.Linear weight layout); features [0,HD) are Q, [HD,2HD) K,
  *              [2HD,3HD) V; head h owns features h*D .. h*D+D-1 of each part.
  *   cu_rows    device int32 [batch+1]; rows of sequence b are cu_rows[b] ..
- *              cu_rows[b+1]-1 (non-decreasing, cu_rows[batch] == num_rows).
+ *              cu_rows[b+1]-1 (non-decreasing, cu_rows[0] == 0,
+ *              cu_rows[batch] <= num_rows).  Rows cu_rows[batch] .. num_rows-1
+ *              are inactive: nothing is read from positions/slots or written
+ *              to q_out, slot_mapping_out or the cache for them.  num_rows is
+ *              then a capacity, so a row count chosen on the device (see
+ *              decode_plan) needs no host round trip.
  *   positions  device int32 [num_rows], rotary position (0-based) of each row.
  *   slots      device int32 [num_rows], logical cache slot of each row; slots
  *              of one call must map to distinct physical slots.
@@ -144,6 +149,8 @@ size_t fdl_flash_cache_workspace_bytes(int32_t num_rows, int32_t hidden,
  * For sequence b, head h and row r: P = softmax(scale * q_r . k_j) over the
  * visible slots j < kv_len[b] (see fdl_two_view), out_r = sum_j P_j v_j.
  *   q          device bf16 [num_rows][H][D] (as written by flash_cache_step)
+ *   cu_rows    as for flash_cache_step: rows cu_rows[batch] .. num_rows-1 are
+ *              inactive and their `out` rows are not written.
  *   kv_len     device int32 [batch]; max_kv_len >= every kv_len[b] (host bound;
  *              a larger kv_len[b] is read as max_kv_len).
  *   max_rows_per_seq  host upper bound on cu_rows[b+1]-cu_rows[b].
@@ -193,6 +200,61 @@ int track_topb(const float *mass, int32_t mass_stride, const int32_t *kv_len,
 int verify_accept(const int32_t *draft_tok, const int32_t *mask_tok,
                   const float *conf, int32_t batch, int32_t window,
                   float threshold, int32_t *accept_len_out, void *stream);
+
+/* Planning step of a multi-step decoding loop [P4 para 2: each step's query
+ * rows are a sliding unmasking window plus a fixed budget of the most-attended
+ * tokens; P4 para 1: caching (refresh) and update stages alternate within a
+ * batch; P4 para 3: accepted tokens are committed in causal order].  Runs on
+ * the device, so a loop of steps needs no host round trip.  Per sequence b,
+ * with L = kv_len[b] and f = frontier[b] clamped to [0, L] (the first
+ * position not yet committed):
+ *   1. step > 0: f += max(1, min(accept_len[b], window_len)), capped at L
+ *      (at least one token per step; accept_len < 0 reads as 0).
+ *   2. f == L: the sequence is finished and gets no rows (stage 2).
+ *   3. Stage: refresh (1) when refresh_period > 0 and (step + b) %
+ *      refresh_period == 0, else update (0).  The window is [w0, min(w0 +
+ *      window_len, L)) with w0 = f (update) or the block_size boundary at or
+ *      below f (refresh).
+ *   4. Tracked rows: entries of tracked[b] kept when in [0, L), outside the
+ *      window and above every entry kept before them (a track_topb result is
+ *      ascending; this also drops repeats and -1 padding).
+ *   5. Rows: the window positions ascending, then the kept tracked entries;
+ *      slot = position.
+ *   kv_len       device int32 [batch]
+ *   tracked      device int32 [batch][topb]: the previous step's track_topb
+ *                output (the caller's initial set at step 0); may be NULL when
+ *                topb == 0.
+ *   accept_len   device int32 [batch]: the previous step's verify_accept
+ *                output; not read at step 0 (may be NULL then).
+ *   frontier     device int32 [batch], read and then overwritten with the
+ *                new f.
+ *   cu_rows_out  device int32 [batch+1]; positions_out, slots_out device int32
+ *                [row_capacity]; stage_out device int32 [batch] or NULL.
+ *   row_capacity >= batch * (window_len + topb), which bounds every plan.
+ * batch <= 4096 (FDL_EUNSUPPORTED above); window_len >= 1, block_size >= 1,
+ * refresh_period >= 0, step >= 0, topb >= 0 (FDL_EINVAL otherwise).  One
+ * workgroup plans the batch. */
+int decode_plan(int32_t batch, const int32_t *kv_len, int32_t window_len,
+                int32_t block_size, int32_t refresh_period, int32_t step,
+                const int32_t *tracked, int32_t topb, const int32_t *accept_len,
+                int32_t *frontier, int32_t *cu_rows_out, int32_t *positions_out,
+                int32_t *slots_out, int32_t *stage_out, int32_t row_capacity,
+                void *stream);
+
+/* Hidden states of the planned rows for a loop whose model is not given (the
+ * input rows of flash_cache_step): row r of sequence b at position p copies
+ * hidden_committed[b][p] when p < frontier[b] (a committed token), else
+ * hidden_masked[b][p] (a still-masked position).
+ *   cu_rows, positions, frontier  as written by decode_plan
+ *   hidden_committed, hidden_masked  device bf16 [batch][max_len][hidden],
+ *                16-byte aligned; positions are clamped to [0, max_len).
+ *   x_out        device bf16 [row_capacity][hidden], 16-byte aligned; rows
+ *                cu_rows[batch] .. row_capacity-1 are not written.
+ * hidden must be a positive multiple of 8. */
+int gather_hidden(int32_t batch, int32_t row_capacity, const int32_t *cu_rows,
+                  const int32_t *positions, const int32_t *frontier,
+                  const void *hidden_committed, const void *hidden_masked,
+                  int32_t max_len, int32_t hidden, void *x_out, void *stream);
 
 /* Text for a status code (static storage). */
 const char *fdl_status_string(int status);

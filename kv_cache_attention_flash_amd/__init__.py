@@ -10,6 +10,11 @@ Calls (same names as the C ABI):
   scheduled_attention  block-table attention (two-view mask; optional mass)
   track_topb           next tracking set from the attention mass
   verify_accept        Flash-Verify accepted-prefix lengths
+  decode_plan          next loop step's rows, planned on the device
+  gather_hidden        hidden-state rows of the planned rows
+
+DecodeStep binds one step to fixed buffers; DecodeLoop chains steps with the
+planning on the device (no host round trip between steps).
 
 Page key: [P4] "Flash-dLLM: I/O-Aware KV Caching and Parallel Decoding for Fast,
 Memory-Efficient Diffusion LLMs" (ai4snews.wisdomeyes.cn summary), paras 1-3.
@@ -29,7 +34,7 @@ from ._lib import FdlError, KVCacheStruct  # noqa: F401
 __all__ = ["PagedKVCache", "flash_cache_step", "flash_cache_step_unfused", "scheduled_attention",
            "track_topb", "verify_accept", "attention_workspace_bytes",
            "flash_cache_workspace_bytes", "flash_cache_unfused_workspace_bytes", "DecodeStep",
-           "FdlError", "load"]
+           "decode_plan", "gather_hidden", "DecodeLoop", "FdlError", "load"]
 
 
 def load():
@@ -338,3 +343,195 @@ class DecodeStep:
         self.run_attention(s)
         self.run_topb(s)
         self.run_verify(s)
+
+
+def decode_plan(kv_len, frontier, tracked, accept_len, step, window_len, block_size,
+                refresh_period, cu_rows_out=None, positions_out=None, slots_out=None,
+                stage_out=None, stream=None):
+    """Plan loop step ``step`` on the device (rules in include/fdllm.h):
+    commits the previous accept lengths into ``frontier`` (in place) and writes
+    the rows.  Returns (cu_rows int32 [batch+1], positions, slots int32
+    [capacity], stage int32 [batch]) with capacity = batch * (W + topb)."""
+    lib = _lib.load()
+    _need(kv_len, "kv_len", torch.int32, 1)
+    _need(frontier, "frontier", torch.int32, 1)
+    batch = kv_len.numel()
+    if frontier.numel() != batch:
+        raise ValueError("frontier must have one entry per sequence")
+    topb = 0
+    if tracked is not None:
+        _need(tracked, "tracked", torch.int32, 2)
+        if tracked.shape[0] != batch:
+            raise ValueError("tracked must be int32 [batch, topb]")
+        topb = tracked.shape[1]
+    if accept_len is not None:
+        _need(accept_len, "accept_len", torch.int32, 1)
+        if accept_len.numel() != batch:
+            raise ValueError("accept_len must have one entry per sequence")
+    dev = kv_len.device
+    cap = batch * (int(window_len) + topb)
+    if cu_rows_out is None:
+        cu_rows_out = torch.empty((batch + 1,), dtype=torch.int32, device=dev)
+    if positions_out is None:
+        positions_out = torch.empty((max(cap, 1),), dtype=torch.int32, device=dev)
+    if slots_out is None:
+        slots_out = torch.empty((max(cap, 1),), dtype=torch.int32, device=dev)
+    if stage_out is None:
+        stage_out = torch.empty((max(batch, 1),), dtype=torch.int32, device=dev)
+    for t, n in ((cu_rows_out, "cu_rows_out"), (positions_out, "positions_out"),
+                 (slots_out, "slots_out"), (stage_out, "stage_out")):
+        _need(t, n, torch.int32, 1)
+    if positions_out.numel() < cap or slots_out.numel() < cap:
+        raise ValueError(f"positions_out/slots_out need {cap} entries")
+    st = lib.decode_plan(batch, kv_len.data_ptr(), int(window_len), int(block_size),
+                         int(refresh_period), int(step), _ptr(tracked), topb, _ptr(accept_len),
+                         frontier.data_ptr(), cu_rows_out.data_ptr(), positions_out.data_ptr(),
+                         slots_out.data_ptr(), stage_out.data_ptr(), positions_out.numel(),
+                         _stream(stream, dev))
+    _lib.check("decode_plan", st)
+    return cu_rows_out, positions_out, slots_out, stage_out
+
+
+def gather_hidden(cu_rows, positions, frontier, hidden_committed, hidden_masked, x_out=None,
+                  stream=None):
+    """Hidden-state rows of the planned rows: the committed-token table's row
+    for positions below the frontier, the masked-token table's otherwise
+    (tables bf16 [batch, max_len, hidden]).  Returns x_out bf16 [capacity, hidden]."""
+    lib = _lib.load()
+    _need(cu_rows, "cu_rows", torch.int32, 1)
+    _need(positions, "positions", torch.int32, 1)
+    _need(frontier, "frontier", torch.int32, 1)
+    _need(hidden_committed, "hidden_committed", torch.bfloat16, 3)
+    _need(hidden_masked, "hidden_masked", torch.bfloat16, 3)
+    if hidden_committed.shape != hidden_masked.shape:
+        raise ValueError("the two hidden-state tables must have the same shape")
+    batch, max_len, hid = hidden_committed.shape
+    if cu_rows.numel() != batch + 1 or frontier.numel() != batch:
+        raise ValueError("cu_rows/frontier do not match the tables' batch")
+    cap = positions.numel()
+    if x_out is None:
+        x_out = torch.empty((cap, hid), dtype=torch.bfloat16, device=positions.device)
+    _need(x_out, "x_out", torch.bfloat16, 2)
+    if x_out.shape[1] != hid or x_out.shape[0] < cap:
+        raise ValueError(f"x_out must be [>= {cap}, {hid}]")
+    st = lib.gather_hidden(batch, cap, cu_rows.data_ptr(), positions.data_ptr(),
+                           frontier.data_ptr(), hidden_committed.data_ptr(),
+                           hidden_masked.data_ptr(), max_len, hid, x_out.data_ptr(),
+                           _stream(stream, positions.device))
+    _lib.check("gather_hidden", st)
+    return x_out
+
+
+class DecodeLoop:
+    """A multi-step decoding loop of one layer whose every step runs on the
+    device: decode_plan -> gather_hidden -> flash_cache_step ->
+    scheduled_attention (+ mass) -> track_topb -> verify_accept.
+
+    Step t plans from step t-1's top-B set (``tracked``) and accept lengths;
+    the rows' count is chosen on the device, so the projection and attention
+    launch over the row capacity batch * (W + topb) and skip the inactive tail.
+    ``scan`` = (draft, mask, conf, threshold) with [steps, batch, W'] tensors
+    gives each step's accept-scan inputs; without it every step commits one
+    token.  Nothing synchronises the host inside ``step``."""
+
+    def __init__(self, cache: PagedKVCache, w_qkv, hidden_committed, hidden_masked, kv_len,
+                 frontier0, tracked0, window_len, rope_base, refresh_period, max_kv_len,
+                 scan=None, softmax_scale=0.0):
+        self.lib = _lib.load()
+        dev = w_qkv.device
+        _need(tracked0, "tracked0", torch.int32, 2)
+        self.cache, self.w = cache, w_qkv
+        self.hc, self.hm = hidden_committed, hidden_masked
+        self.kv_len = kv_len
+        self.batch = kv_len.numel()
+        self.window = int(window_len)
+        self.topb = tracked0.shape[1]
+        self.refresh_period = int(refresh_period)
+        self.cap = self.batch * (self.window + self.topb)
+        h, d = cache.num_heads, cache.head_dim
+        hid = hidden_committed.shape[2]
+        self.frontier = frontier0.clone()
+        self.tracked = tracked0.clone()
+        self.accept = torch.zeros((self.batch,), dtype=torch.int32, device=dev)
+        self.cu_rows = torch.empty((self.batch + 1,), dtype=torch.int32, device=dev)
+        self.positions = torch.empty((self.cap,), dtype=torch.int32, device=dev)
+        self.slots = torch.empty((self.cap,), dtype=torch.int32, device=dev)
+        self.stage = torch.empty((self.batch,), dtype=torch.int32, device=dev)
+        self.x = torch.empty((self.cap, hid), dtype=torch.bfloat16, device=dev)
+        self.q = torch.empty((self.cap, h, d), dtype=torch.bfloat16, device=dev)
+        self.slot_mapping = torch.empty((self.cap,), dtype=torch.int64, device=dev)
+        self.out = torch.empty((self.cap, h, d), dtype=torch.float32, device=dev)
+        self.max_kv_len = int(max_kv_len)
+        self.mass = torch.empty((self.batch, self.max_kv_len), dtype=torch.float32, device=dev)
+        need = attention_workspace_bytes(self.batch, self.cap, h, d, self.max_kv_len,
+                                         self.window + self.topb, self.max_kv_len)
+        self.workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+        fneed = flash_cache_workspace_bytes(self.cap, hid, h, d)
+        self.fc_workspace = torch.empty((max(fneed, 1),), dtype=torch.uint8, device=dev)
+        self.cs = cache.struct()
+        self._plan = (self.batch, kv_len.data_ptr(), self.window, cache.block_size,
+                      self.refresh_period)
+        self._plan_tail = (self.tracked.data_ptr(), self.topb, self.accept.data_ptr(),
+                           self.frontier.data_ptr(), self.cu_rows.data_ptr(),
+                           self.positions.data_ptr(), self.slots.data_ptr(),
+                           self.stage.data_ptr(), self.cap)
+        self._gather = (self.batch, self.cap, self.cu_rows.data_ptr(), self.positions.data_ptr(),
+                        self.frontier.data_ptr(), hidden_committed.data_ptr(),
+                        hidden_masked.data_ptr(), hidden_committed.shape[1], hid,
+                        self.x.data_ptr())
+        self._fcs = (ctypes.byref(self.cs), self.x.data_ptr(), hid, w_qkv.data_ptr(), self.batch,
+                     self.cap, self.cu_rows.data_ptr(), self.positions.data_ptr(),
+                     self.slots.data_ptr(), float(rope_base), self.q.data_ptr(),
+                     self.slot_mapping.data_ptr(), self.fc_workspace.data_ptr(), fneed)
+        self._att = (ctypes.byref(self.cs), self.q.data_ptr(), self.batch, self.cap,
+                     self.cu_rows.data_ptr(), kv_len.data_ptr(), self.max_kv_len,
+                     self.window + self.topb, None, float(softmax_scale), self.out.data_ptr(),
+                     self.mass.data_ptr(), self.max_kv_len, self.workspace.data_ptr(),
+                     self.workspace.numel())
+        self._top = (self.mass.data_ptr(), self.max_kv_len, kv_len.data_ptr(), self.batch,
+                     self.topb, self.tracked.data_ptr())
+        self.scan = None
+        if scan is not None:
+            dr, mk, cf, thr = scan
+            _need(dr, "draft", torch.int32, 3)
+            _need(mk, "mask", torch.int32, 3)
+            _need(cf, "conf", torch.float32, 3)
+            if dr.shape != mk.shape or dr.shape != cf.shape or dr.shape[1] != self.batch:
+                raise ValueError("scan tensors must be [steps, batch, W] alike")
+            self.scan = (dr, mk, cf, float(thr))
+
+    def run_plan(self, t: int, stream: int):
+        _lib.check("decode_plan", self.lib.decode_plan(*self._plan, int(t), *self._plan_tail,
+                                                       stream))
+
+    def run_gather(self, stream: int):
+        _lib.check("gather_hidden", self.lib.gather_hidden(*self._gather, stream))
+
+    def run_flash_cache(self, stream: int):
+        _lib.check("flash_cache_step", self.lib.flash_cache_step(*self._fcs, stream))
+
+    def run_attention(self, stream: int):
+        _lib.check("scheduled_attention", self.lib.scheduled_attention(*self._att, stream))
+
+    def run_topb(self, stream: int):
+        if self.topb:
+            _lib.check("track_topb", self.lib.track_topb(*self._top, stream))
+
+    def run_verify(self, t: int, stream: int):
+        if self.scan is None:
+            return
+        dr, mk, cf, thr = self.scan
+        if t >= dr.shape[0]:
+            raise ValueError(f"no scan inputs for step {t}")
+        _lib.check("verify_accept", self.lib.verify_accept(
+            dr[t].data_ptr(), mk[t].data_ptr(), cf[t].data_ptr(), self.batch, dr.shape[2],
+            ctypes.c_float(thr), self.accept.data_ptr(), stream))
+
+    def step(self, t: int, stream=None):
+        s = _stream(stream, self.w.device) if not isinstance(stream, int) else stream
+        self.run_plan(t, s)
+        self.run_gather(s)
+        self.run_flash_cache(s)
+        self.run_attention(s)
+        self.run_topb(s)
+        self.run_verify(t, s)

@@ -41,6 +41,10 @@ EXPORTS = {
     "fdl_attention_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "track_topb": (ctypes.c_int, [c_vp, c_i32, c_vp, c_i32, c_i32, c_vp, c_vp]),
     "verify_accept": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i32, c_i32, c_f32, c_vp, c_vp]),
+    "decode_plan": (ctypes.c_int, [c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp,
+                                   c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp]),
+    "gather_hidden": (ctypes.c_int, [c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
+                                     c_vp, c_vp]),
     "fdl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fdl_last_hip_error": (ctypes.c_int, []),
     "fdl_version": (ctypes.c_char_p, []),

@@ -219,4 +219,63 @@ int verify_accept(const int32_t *draft_tok, const int32_t *mask_tok, const float
                                        accept_len_out, static_cast<hipStream_t>(stream)));
 }
 
+int decode_plan(int32_t batch, const int32_t *kv_len, int32_t window_len, int32_t block_size,
+                int32_t refresh_period, int32_t step, const int32_t *tracked, int32_t topb,
+                const int32_t *accept_len, int32_t *frontier, int32_t *cu_rows_out,
+                int32_t *positions_out, int32_t *slots_out, int32_t *stage_out,
+                int32_t row_capacity, void *stream) {
+  if (batch < 0 || window_len < 1 || block_size < 1 || refresh_period < 0 || step < 0 ||
+      topb < 0 || row_capacity < 0)
+    return FDL_EINVAL;
+  if (batch > fdl::kPlanMaxBatch) return FDL_EUNSUPPORTED;
+  if ((int64_t)row_capacity < (int64_t)batch * ((int64_t)window_len + topb)) return FDL_EINVAL;
+  if (batch == 0) return FDL_OK;
+  if (!kv_len || !frontier || !cu_rows_out || !positions_out || !slots_out) return FDL_EINVAL;
+  if (topb > 0 && !tracked) return FDL_EINVAL;
+  if (step > 0 && !accept_len) return FDL_EINVAL;
+  fdl::PlanArgs a;
+  a.batch = batch;
+  a.window = window_len;
+  a.block_size = block_size;
+  a.refresh_period = refresh_period;
+  a.step = step;
+  a.topb = topb;
+  a.kv_len = kv_len;
+  a.tracked = tracked;
+  a.accept_len = accept_len;
+  a.frontier = frontier;
+  a.frontier_out = frontier;
+  a.cu_rows = cu_rows_out;
+  a.positions = positions_out;
+  a.slots = slots_out;
+  a.stage = stage_out;
+  return hip_status(fdl::launch_plan(a, static_cast<hipStream_t>(stream)));
+}
+
+int gather_hidden(int32_t batch, int32_t row_capacity, const int32_t *cu_rows,
+                  const int32_t *positions, const int32_t *frontier,
+                  const void *hidden_committed, const void *hidden_masked, int32_t max_len,
+                  int32_t hidden, void *x_out, void *stream) {
+  if (batch < 0 || row_capacity < 0 || max_len < 1 || hidden <= 0 || hidden % 8 != 0)
+    return FDL_EINVAL;
+  if (batch == 0 || row_capacity == 0) return FDL_OK;
+  if (!cu_rows || !positions || !frontier || !hidden_committed || !hidden_masked || !x_out)
+    return FDL_EINVAL;
+  auto misaligned = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
+  if (misaligned(hidden_committed) || misaligned(hidden_masked) || misaligned(x_out))
+    return FDL_EINVAL;
+  fdl::GatherArgs a;
+  a.batch = batch;
+  a.rows = row_capacity;
+  a.max_len = max_len;
+  a.hidden = hidden;
+  a.cu_rows = cu_rows;
+  a.positions = positions;
+  a.frontier = frontier;
+  a.committed = static_cast<const uint16_t *>(hidden_committed);
+  a.masked = static_cast<const uint16_t *>(hidden_masked);
+  a.x_out = static_cast<uint16_t *>(x_out);
+  return hip_status(fdl::launch_gather_hidden(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -62,6 +62,12 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnArgs &a, int b) {
   return si;
 }
 
+// Rows at or past cu_rows[batch] are inactive (num_rows is then a capacity):
+// no output is written for them.
+__device__ __forceinline__ int active_rows(const AttnArgs &a) {
+  return max(0, min(a.rows, a.cu_rows[a.batch]));
+}
+
 // The slots local row t of a sequence may see, as intervals: slot j is visible
 // iff (j < lim and not x0 <= j < x1) or y0 <= j <= y1.
 //   plain row:        [0, L)
@@ -442,7 +448,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, AttnPlan p)
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t rh = idx / (D / 4);
   const int d4 = (int)(idx % (D / 4)) * 4;
-  if (rh >= (size_t)a.rows * a.c.H) return;
+  if (rh >= (size_t)active_rows(a) * a.c.H) return;
   merge_row<4>(a, p, rh, D, d4, a.out);
 }
 
@@ -585,7 +591,7 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnArgs a, AttnPlan p
     const size_t idx = (size_t)(blockIdx.x - nb_mass) * blockDim.x + threadIdx.x;
     const size_t rh = idx / (D / 4);
     const int d4 = (int)(idx % (D / 4)) * 4;
-    if (rh < (size_t)a.rows * a.c.H) merge_row<4>(a, p, rh, D, d4, a.out);
+    if (rh < (size_t)active_rows(a) * a.c.H) merge_row<4>(a, p, rh, D, d4, a.out);
     return;
   }
   const int per_b = (a.mass_stride + 255) / 256;

@@ -37,6 +37,12 @@ __device__ __forceinline__ int row_to_seq(const int32_t *cu_rows, int batch, int
   return lo;
 }
 
+// Rows at or past cu_rows[batch] are inactive (num_rows is then a capacity):
+// nothing is written for them.
+__device__ __forceinline__ int active_rows(const FlashCacheArgs &a) {
+  return max(0, min(a.rows, a.cu_rows[a.batch]));
+}
+
 // Rotary frequency base^(-2i/D), in turns (revolutions) per position, fp64.
 __device__ __forceinline__ double rope_inv_freq(int i, int D, double log2_base) {
   return exp2(-(2.0 * (double)i / (double)D) * log2_base) * kInvTwoPi;
@@ -184,7 +190,8 @@ __global__ __launch_bounds__(NW * 64) void qkv_splitk_kernel(FlashCacheArgs a, S
     }
   }
 
-  if (sp.S == 1 && tid < ROWS && tid < a.rows) {
+  const int act = active_rows(a);
+  if (sp.S == 1 && tid < ROWS && tid < act) {
     int blk, off, pos;
     row_meta(a, tid, idx == 0, blk, off, pos);
     s_blk[tid] = blk;
@@ -309,7 +316,7 @@ __global__ __launch_bounds__(NW * 64) void qkv_splitk_kernel(FlashCacheArgs a, S
   for (int item = tid; item < ROWS * PW; item += NW * 64) {
     const int rl = item / PW, pl = item % PW;
     const int p = pair0 + pl;
-    if (rl >= a.rows || p >= total_pairs) continue;
+    if (rl >= act || p >= total_pairs) continue;
     const int clo = 16 * (pl >> 3) + (pl & 7);
     store_pair(a, rl, p, Y[rl * YS + clo], Y[rl * YS + clo + 8], s_blk[rl], s_off[rl], s_pos[rl],
                s_freq[p % half]);
@@ -329,7 +336,7 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(FlashCacheArgs a, Split
   const int grp = item / per_group;
   const int rl = (item % per_group) / PW, pl = item % PW;
   const int p = grp * PW + pl;
-  if (p >= total_pairs) return;
+  if (p >= total_pairs || rl >= active_rows(a)) return;
   const int clo = 16 * (pl >> 3) + (pl & 7);
   const size_t split_stride = (size_t)64 * CW;
   const float *base = sp.partials + (size_t)grp * sp.S * split_stride + rl * CW + clo;
@@ -383,9 +390,10 @@ __global__ __launch_bounds__(128 * NWN) void qkv_gemm_kernel(FlashCacheArgs a, i
   const int ct = idx / nrow_tiles, rtile = idx % nrow_tiles;
   const int row0 = rtile * BM, pair0 = ct * BP;
 
+  const int act = active_rows(a);
   for (int rl = tid; rl < BM; rl += NT) {
     const int r = row0 + rl;
-    if (r < a.rows) {
+    if (r < act) {
       int blk, off, pos;
       row_meta(a, r, ct == 0, blk, off, pos);
       s_blk[rl] = blk;
@@ -485,7 +493,7 @@ __global__ __launch_bounds__(128 * NWN) void qkv_gemm_kernel(FlashCacheArgs a, i
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int rl = wm * (BM / 2) + 32 * mt + 8 * (e / 4) + 4 * hi + (e % 4);
-      if (row0 + rl >= a.rows) continue;
+      if (row0 + rl >= act) continue;
       store_pair(a, row0 + rl, p, acc[mt][0][e], acc[mt][1][e], s_blk[rl], s_off[rl], s_pos[rl],
                  freq);
     }
@@ -503,6 +511,7 @@ __global__ __launch_bounds__(256) void rope_round_kernel(FlashCacheArgs a, const
   const size_t item = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (item >= (size_t)a.rows * pairs) return;
   const int r = (int)(item / pairs), p = (int)(item % pairs);
+  if (r >= active_rows(a)) return;
   const int sh = p / half, i = p % half, sec = sh / H, h = sh % H;
   const float *yr = y + (size_t)r * 3 * H * D + (size_t)sh * D + i;
   const uint32_t v = rotate_round(yr[0], yr[half], sec, a.positions[r],
@@ -520,6 +529,7 @@ __global__ __launch_bounds__(256) void scatter_kv_kernel(FlashCacheArgs a, const
   const size_t item = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (item >= (size_t)a.rows * H * ch) return;
   const int r = (int)(item / (H * ch)), rem = (int)(item % (H * ch));
+  if (r >= active_rows(a)) return;
   const int h = rem / ch, c = rem % ch;
   int blk, off, pos;
   row_meta(a, r, h == 0 && c == 0, blk, off, pos);

@@ -64,4 +64,25 @@ hipError_t launch_topb(const float *mass, int stride, const int32_t *kv_len, int
 hipError_t launch_verify(const int32_t *draft, const int32_t *mask, const float *conf,
                          int batch, int window, float thr, int32_t *out, hipStream_t s);
 
+// Multi-step loop planning (loop.hip).
+constexpr int kStageUpdate = 0, kStageRefresh = 1, kStageDone = 2;
+constexpr int kPlanMaxBatch = 4096;
+
+struct PlanArgs {
+  int batch, window, block_size, refresh_period, step, topb;
+  const int32_t *kv_len, *tracked, *accept_len, *frontier;
+  int32_t *frontier_out, *cu_rows, *positions, *slots, *stage;
+};
+
+hipError_t launch_plan(const PlanArgs &a, hipStream_t s);
+
+struct GatherArgs {
+  int batch, rows, max_len, hidden;  // rows = capacity of x_out
+  const int32_t *cu_rows, *positions, *frontier;
+  const uint16_t *committed, *masked;
+  uint16_t *x_out;
+};
+
+hipError_t launch_gather_hidden(const GatherArgs &a, hipStream_t s);
+
 }  // namespace fdl

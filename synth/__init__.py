@@ -8,7 +8,9 @@ it without sharing any computation.
 Recipe: every stream is ``numpy.random.default_rng([workload_id, layer, stream])``
 with streams 0 X, 1 W, 2 K cache, 3 V cache, 4 window/tracked positions,
 5 block permutation, 6 lengths, 8 draft tokens, 9 agreement, 10 replacement
-tokens, 11 confidences.  Real values are drawn as standard normals in fp32
+tokens, 11 confidences, 12 and 13 the committed- and masked-token hidden-state
+tables of a multi-step loop (whose per-step scan draws use the step as the
+``layer`` key).  Real values are drawn as standard normals in fp32
 (the weight scaled by 0.02 in fp32) and rounded to bf16 by torch's CPU cast.
 The large 32-layer stack draws its tensors on the GPU with torch's seeded
 generator instead (host generation of ~19 G values would take minutes); those
@@ -27,6 +29,7 @@ import numpy as np
 
 STREAM_X, STREAM_W, STREAM_K, STREAM_V, STREAM_POS, STREAM_PERM, STREAM_LEN = 0, 1, 2, 3, 4, 5, 6
 STREAM_DRAFT, STREAM_AGREE, STREAM_REPL, STREAM_CONF = 8, 9, 10, 11
+STREAM_HID_COMMITTED, STREAM_HID_MASKED = 12, 13
 
 
 def rng(workload_id: int, layer: int, stream: int) -> np.random.Generator:
@@ -369,6 +372,174 @@ def small_long(materialize=True) -> Workload:
              SeqSpec(kv_len=1100, window=(1050, 16), tracked=distinct(g, 0, 1050, 8))]
     return build("small_long_l1500", 15, 256, 2, 64, 32, 1.0e4, specs, topb=8,
                  materialize=materialize)
+
+
+# ---------------------------------------------------------------------------
+# Multi-step loop workloads
+# ---------------------------------------------------------------------------
+
+
+@dataclasses.dataclass
+class LoopWorkload:
+    """Initial state and inputs of a multi-step decoding loop of one layer.
+
+    ``frontier0`` [batch] is each sequence's first uncommitted position,
+    ``tracked0`` [batch, topb] the initial tracking set (ascending, -1 padded).
+    Hidden states come from two tables bf16 [batch, max_len, hid]: a
+    committed-token row and a masked-token row per position.  ``scan`` holds
+    each step's accept-scan inputs, [steps, batch, W] draft and mask-view
+    tokens and fp32 confidences, and the threshold 0.9f.
+    """
+    name: str
+    workload_id: int
+    hid: int
+    num_heads: int
+    head_dim: int
+    block_size: int
+    rope_base: float
+    kv_len: np.ndarray
+    block_table: np.ndarray
+    num_blocks: int
+    frontier0: np.ndarray
+    tracked0: np.ndarray
+    window_len: int
+    topb: int
+    refresh_period: int
+    steps: int
+    scan: dict
+    w: Optional[np.ndarray] = None
+    k_cache: Optional[np.ndarray] = None
+    v_cache: Optional[np.ndarray] = None
+    hidden_committed: Optional[np.ndarray] = None
+    hidden_masked: Optional[np.ndarray] = None
+
+    @property
+    def batch(self) -> int:
+        return len(self.kv_len)
+
+    @property
+    def max_len(self) -> int:
+        return int(self.kv_len.max())
+
+
+def loop_scan_inputs(workload_id: int, steps: int, batch: int, window: int):
+    """Per-step accept-scan inputs: draft tokens U{0..2^20-1}; the mask-view
+    argmax agrees with probability 0.98 (else a different token); confidences
+    0.885 + 0.115 U(0,1) in fp32; threshold 0.9f.  A position then passes with
+    probability about 0.85, so about 5.7 tokens are accepted per step, the
+    figure the pages report for Flash-Verify."""
+    v = 1 << 20
+    shape = (batch, window)
+    draft, mask, conf = [], [], []
+    for t in range(steps):
+        d = rng(workload_id, t, STREAM_DRAFT).integers(0, v, size=shape).astype(np.int32)
+        agree = rng(workload_id, t, STREAM_AGREE).random(size=shape) < 0.98
+        repl = rng(workload_id, t, STREAM_REPL).integers(0, v - 1, size=shape)
+        m = np.where(agree, d, (d.astype(np.int64) + 1 + repl) % v).astype(np.int32)
+        u = rng(workload_id, t, STREAM_CONF).random(size=shape, dtype=np.float32)
+        c = (np.float32(0.885) + np.float32(0.115) * u).astype(np.float32)
+        draft.append(d); mask.append(m); conf.append(c)
+    return dict(draft=np.stack(draft), mask=np.stack(mask), conf=np.stack(conf),
+                threshold=np.float32(0.9))
+
+
+def build_loop(name, workload_id, hid, num_heads, head_dim, block_size, rope_base, kv_len,
+               frontier0, tracked0, window_len, topb, refresh_period, steps,
+               materialize=True) -> LoopWorkload:
+    specs = [SeqSpec(kv_len=int(n)) for n in kv_len]
+    kvl, _, _, _, bt, nb, _ = layout(workload_id, specs, block_size)
+    tr = np.full((len(kv_len), topb), -1, np.int32)
+    for b, t in enumerate(tracked0):
+        t = sorted(int(v) for v in t)[:topb]
+        tr[b, :len(t)] = t
+    wl = LoopWorkload(name, workload_id, hid, num_heads, head_dim, block_size, rope_base, kvl,
+                      bt, nb, np.array(frontier0, np.int32), tr, window_len, topb,
+                      refresh_period, steps,
+                      loop_scan_inputs(workload_id, steps, len(kv_len), window_len))
+    if materialize:
+        hd = num_heads * head_dim
+        wl.w = normal_bf16(workload_id, 0, STREAM_W, (3 * hd, hid), scale=0.02)
+        shape = (nb, num_heads, block_size, head_dim)
+        wl.k_cache = normal_bf16(workload_id, 0, STREAM_K, shape)
+        wl.v_cache = normal_bf16(workload_id, 0, STREAM_V, shape)
+        tshape = (len(kv_len), wl.max_len, hid)
+        wl.hidden_committed = normal_bf16(workload_id, 0, STREAM_HID_COMMITTED, tshape)
+        wl.hidden_masked = normal_bf16(workload_id, 0, STREAM_HID_MASKED, tshape)
+    return wl
+
+
+def small_loop_b4(materialize=True) -> LoopWorkload:
+    """Loop on a narrow layer (hidden 256, 2 x 64): batch 4, cache lengths
+    150, 77, 40, 200; one sequence finished from the start, one finishing
+    within two steps; window 16, budget 8, refresh every third step, 6 steps."""
+    g = rng(21, 0, STREAM_POS)
+    f0 = [60, 70, 40, 100]
+    tracked = [distinct(g, 0, f, 8) for f in f0]
+    return build_loop("small_loop_b4", 21, 256, 2, 64, 32, 1.0e4, [150, 77, 40, 200], f0,
+                      tracked, 16, 8, 3, 6, materialize)
+
+
+def small_loop_d128(materialize=True) -> LoopWorkload:
+    """Loop with head_dim 128 (hidden 512, 4 x 128): batch 3, lengths 300, 129,
+    64, one sequence starting at position 0 with an empty tracking set, one
+    finishing within the run; window 32, budget 16, refresh every other step,
+    5 steps."""
+    g = rng(22, 0, STREAM_POS)
+    f0 = [40, 118, 0]
+    tracked = [distinct(g, 0, f, 16) for f in f0]
+    return build_loop("small_loop_d128", 22, 512, 4, 128, 32, 5.0e5, [300, 129, 64], f0,
+                      tracked, 32, 16, 2, 5, materialize)
+
+
+def llada8b_loop_b32(materialize=False) -> LoopWorkload:
+    """The batch-32 ragged layer (hidden 4096, 32 x 128, lengths U{512..1024})
+    run as a 16-step loop: each sequence starts at its window start with its
+    32 tracked rows; window 32, budget 32, refresh every fourth step (stages
+    staggered across the batch).  Tensors are drawn on the GPU
+    (``loop_tensors``)."""
+    base = llada8b_ragged_b32(materialize=False)
+    f0, tracked = [], []
+    cu = base.cu_rows
+    for b in range(base.batch):
+        rows = base.positions[cu[b]:cu[b + 1]]
+        f0.append(int(rows[0]))
+        tracked.append([int(p) for p in rows[32:]])
+    return build_loop("llada8b_loop_b32", 23, 4096, 32, 128, 32, 5.0e5,
+                      [int(n) for n in base.kv_len], f0, tracked, 32, 32, 4, 16, materialize)
+
+
+def loop_tensors(wl: LoopWorkload, device):
+    """torch bf16 tensors of a loop workload on ``device``: host draws when the
+    workload is materialized, else torch's seeded generator on the device
+    (seed = workload*1e6 + stream) for W, the cache pools and both tables."""
+    import torch
+    if wl.w is not None:
+        def dev(a):
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        return (dev(wl.w), dev(wl.k_cache), dev(wl.v_cache), dev(wl.hidden_committed),
+                dev(wl.hidden_masked))
+    hd = wl.num_heads * wl.head_dim
+    cshape = (wl.num_blocks, wl.num_heads, wl.block_size, wl.head_dim)
+    tshape = (wl.batch, wl.max_len, wl.hid)
+    out = []
+    for stream, shape, scale in ((STREAM_W, (3 * hd, wl.hid), 0.02), (STREAM_K, cshape, 1.0),
+                                 (STREAM_V, cshape, 1.0), (STREAM_HID_COMMITTED, tshape, 1.0),
+                                 (STREAM_HID_MASKED, tshape, 1.0)):
+        g = torch.Generator(device=device)
+        g.manual_seed(wl.workload_id * 1_000_000 + stream)
+        t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if scale != 1.0:
+            t.mul_(scale)
+        out.append(t.to(torch.bfloat16))
+        del t
+    return tuple(out)
+
+
+LOOP_WORKLOADS = {
+    "small_loop_b4": small_loop_b4,
+    "small_loop_d128": small_loop_d128,
+    "llada8b_loop_b32": llada8b_loop_b32,
+}
 
 
 WORKLOADS = {

@@ -138,3 +138,43 @@ def test_topb_and_verify_validation(lib):
     assert lib.verify_accept(None, fake, fake, 2, 4, 0.9, fake, None) == _lib.FDL_EINVAL
     assert lib.verify_accept(fake, fake, fake, 2, 4, 0.9, None, None) == _lib.FDL_EINVAL
     assert lib.verify_accept(fake, fake, fake, 0, 4, 0.9, fake, None) == _lib.FDL_OK
+
+
+def test_decode_plan_validation(lib):
+    fake = 0x10000
+    def plan(batch=2, w=16, bs=32, k=2, step=1, tracked=fake, topb=8, acc=fake, front=fake,
+             cu=fake, pos=fake, slots=fake, cap=None):
+        cap = batch * (w + topb) if cap is None else cap
+        return lib.decode_plan(batch, fake, w, bs, k, step, tracked, topb, acc, front, cu, pos,
+                               slots, None, cap, None)
+    assert plan(w=0) == _lib.FDL_EINVAL
+    assert plan(bs=0) == _lib.FDL_EINVAL
+    assert plan(k=-1) == _lib.FDL_EINVAL
+    assert plan(step=-1) == _lib.FDL_EINVAL
+    assert plan(topb=-1) == _lib.FDL_EINVAL
+    assert plan(batch=-1) == _lib.FDL_EINVAL
+    assert plan(cap=2 * 24 - 1) == _lib.FDL_EINVAL          # capacity below batch * (W + topb)
+    assert plan(batch=4097) == _lib.FDL_EUNSUPPORTED        # one workgroup plans at most 4096
+    assert plan(tracked=None) == _lib.FDL_EINVAL            # topb > 0 needs the tracked set
+    assert plan(acc=None) == _lib.FDL_EINVAL                # step > 0 reads accept lengths
+    assert plan(front=None) == _lib.FDL_EINVAL
+    assert plan(cu=None) == _lib.FDL_EINVAL
+    assert plan(pos=None) == _lib.FDL_EINVAL
+    assert plan(slots=None) == _lib.FDL_EINVAL
+    assert plan(batch=0) == _lib.FDL_OK
+
+
+def test_gather_hidden_validation(lib):
+    fake = 0x10000
+    def gather(batch=2, cap=10, max_len=64, hid=256, hc=fake, hm=fake, x=fake, cu=fake):
+        return lib.gather_hidden(batch, cap, cu, fake, fake, hc, hm, max_len, hid, x, None)
+    assert gather(hid=100) == _lib.FDL_EINVAL               # not a multiple of 8
+    assert gather(hid=0) == _lib.FDL_EINVAL
+    assert gather(max_len=0) == _lib.FDL_EINVAL
+    assert gather(batch=-1) == _lib.FDL_EINVAL
+    assert gather(hc=None) == _lib.FDL_EINVAL
+    assert gather(cu=None) == _lib.FDL_EINVAL
+    assert gather(hm=fake + 8) == _lib.FDL_EINVAL           # tables must be 16-byte aligned
+    assert gather(x=fake + 2) == _lib.FDL_EINVAL
+    assert gather(batch=0) == _lib.FDL_OK
+    assert gather(cap=0) == _lib.FDL_OK
