@@ -257,6 +257,171 @@ def roofline_entry(call, wl, ms, workload):
     return e
 
 
+LOOP_METRIC = "decode-loop steps/s (one layer, batch 32, every step planned on the device)"
+LOOP_WORKLOAD = ("llada8b_loop_b32: hidden 4096, 32x128 MHA, batch 32, cache U{512..1024}; per "
+                 "step decode_plan (window 32 + up to 32 tracked rows, refresh every 4th step "
+                 "staggered across the batch, commit max(1, accepted)) -> gather_hidden -> "
+                 "flash_cache_step -> scheduled_attention(+mass) -> track_topb -> verify_accept "
+                 "(synthetic scan, ~5.7 accepted per step)")
+
+
+def run_loop(args):
+    """The multi-step loop: steps/s of the whole batch with every step planned
+    on the device.  An untimed pass from the same initial state records each
+    step's active rows and frontiers (copies that would otherwise sit inside
+    the timed region); the timed pass then runs the same steps with nothing
+    added, and its final frontiers must equal the untimed pass's."""
+    import numpy as np
+    import torch
+
+    import kv_cache_attention_flash_amd as fd
+    import synth
+
+    steps_k = args.steps if args.steps is not None else 32
+    warmup = args.warmup if args.warmup is not None else 4
+    fd.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.llada8b_loop_b32(steps=warmup + steps_k)
+    w, k, v, hc, hm = synth.loop_tensors(wl, dev)
+    k0, v0 = k.clone(), v.clone()
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    sc = wl.scan
+    scan = (i32(sc["draft"]), i32(sc["mask"]), torch.from_numpy(sc["conf"]).to(dev),
+            float(sc["threshold"]))
+    kv = i32(wl.kv_len)
+    cache = fd.PagedKVCache(k, v, i32(wl.block_table))
+    loop = fd.DecodeLoop(cache, w, hc, hm, kv, i32(wl.frontier0), i32(wl.tracked0),
+                         wl.window_len, wl.rope_base, wl.refresh_period, wl.max_len, scan=scan)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    log(f"loop {wl.name}: batch {wl.batch}, row capacity {loop.cap}, "
+        f"{warmup} + {steps_k} steps, resident {torch.cuda.memory_allocated(dev) / 1e9:.2f} GB")
+
+    def reset():
+        k.copy_(k0)
+        v.copy_(v0)
+        loop.frontier.copy_(i32(wl.frontier0))
+        loop.tracked.copy_(i32(wl.tracked0))
+        loop.accept.zero_()
+        torch.cuda.synchronize()
+
+    rows, fronts = [], []
+    for t in range(warmup + steps_k):
+        loop.step(t, sh)
+        rows.append(int(loop.cu_rows[-1].item()))
+        fronts.append(loop.frontier.cpu().numpy().astype(np.int64))
+    reset()
+    for t in range(warmup):
+        loop.step(t, sh)
+    torch.cuda.synchronize()
+    ht = HipTimer()
+    names = ["decode_plan", "gather_hidden", "flash_cache_step", "scheduled_attention",
+             "track_topb", "verify_accept"]
+    ev = [[ht.event() for _ in range(len(names) + 1)] for _ in range(steps_k)]
+    start, end = ht.event(), ht.event()
+    ht.record(start, sh)
+    for i in range(steps_k):
+        t, e = warmup + i, ev[i]
+        ht.record(e[0], sh)
+        loop.run_plan(t, sh)
+        ht.record(e[1], sh)
+        loop.run_gather(sh)
+        ht.record(e[2], sh)
+        loop.run_flash_cache(sh)
+        ht.record(e[3], sh)
+        loop.run_attention(sh)
+        ht.record(e[4], sh)
+        loop.run_topb(sh)
+        ht.record(e[5], sh)
+        loop.run_verify(t, sh)
+        ht.record(e[6], sh)
+    ht.record(end, sh)
+    torch.cuda.synchronize()
+    total_ms = ht.ms(start, end)
+    same = bool(np.array_equal(loop.frontier.cpu().numpy(), fronts[-1]))
+    per_call = {n: float(np.mean([ht.ms(e[j], e[j + 1]) for e in ev])) for j, n in enumerate(names)}
+    timed_rows = rows[warmup:]
+    committed = int(fronts[-1].sum() - fronts[warmup - 1].sum()) if warmup else \
+        int(fronts[-1].sum() - wl.frontier0.astype(np.int64).sum())
+    ms_per_step = total_ms / steps_k
+    r_avg = float(np.mean(timed_rows))
+    hd = wl.num_heads * wl.head_dim
+    fc_flops = 2 * r_avg * wl.hid * 3 * hd
+    fc_ms = per_call["flash_cache_step"]
+    ridge = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    fc_bytes = 2 * 3 * hd * wl.hid + r_avg * (2 * wl.hid + 2 * 3 * hd + 16)
+    if fc_flops / fc_bytes >= ridge:
+        ach = fc_flops / (fc_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFS, 4)}
+    else:
+        ach = fc_bytes / (fc_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": None, "kernel": "flash_cache_step (row capacity "
+                 f"{loop.cap}, {r_avg:.0f} active rows on average)",
+                 "algorithmic_flops": int(fc_flops), "avg_launch_us": round(fc_ms * 1e3, 2)})
+    log(f"loop step {ms_per_step * 1e3:.1f} us; " +
+        ", ".join(f"{n} {per_call[n] * 1e3:.1f} us" for n in names) +
+        f"; frontiers reproduced: {same}")
+
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = loop_cpu_baseline(wl, w, k0, v0, hc, hm, args.cpu_budget)
+        log(f"cpu oracle loop {cpu['value']:.3f} steps/s (extrapolated)")
+    line = {
+        "metric": LOOP_METRIC, "value": round(1e3 / ms_per_step, 1), "unit": "steps/s",
+        "n_gpus": 1, "steps": steps_k, "warmup": warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": LOOP_WORKLOAD, "batch": wl.batch, "row_capacity": loop.cap,
+                   "hidden": wl.hid, "heads": wl.num_heads, "head_dim": wl.head_dim},
+        "active_rows_per_s": round(sum(timed_rows) / (total_ms / 1e3), 1),
+        "committed_tokens_per_s": round(committed / (total_ms / 1e3), 1),
+        "active_rows_per_step": round(r_avg, 1),
+        "committed_tokens_per_step": round(committed / steps_k, 2),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "step_breakdown_us": {n: round(per_call[n] * 1e3, 2) for n in names},
+        "frontiers_reproduced": same,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def loop_cpu_baseline(wl, w, k0, v0, hc, hm, budget_s):
+    """The oracle loop over the whole batch from the same initial state, for
+    one step (more if the budget allows a second): steps/s measured, not
+    extrapolated (the oracle's per-step costs are not linear in the
+    sequences: it widens the whole weight each step)."""
+    import numpy as np
+    import torch
+    import oracle as O
+
+    def host(t):
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    w_h, k_h, v_h, hc_h, hm_h = host(w), host(k0), host(v0), host(hc), host(hm)
+    sc = wl.scan
+
+    def run(n):
+        t0 = time.perf_counter()
+        O.decode_loop(n, w_h, wl.num_heads, wl.head_dim, wl.rope_base, wl.block_table,
+                      wl.block_size, k_h, v_h, wl.kv_len, hc_h, hm_h, wl.frontier0, wl.tracked0,
+                      wl.window_len, wl.topb, wl.refresh_period, sc["draft"], sc["mask"],
+                      sc["conf"], sc["threshold"], mass_stride=wl.max_len)
+        return time.perf_counter() - t0
+    n_steps, el = 1, run(1)
+    if 3 * el < budget_s:
+        n_steps = min(wl.steps, int(budget_s / el))
+        el = run(n_steps)
+    return {"value": n_steps / el, "unit": "steps/s", "cores": int(_threads()), "kind": "oracle",
+            "sample": f"oracle loop over the whole batch ({wl.batch} sequences) for {n_steps} "
+                      f"step(s) from the same initial state ({el:.1f} s, fp64 numpy)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -275,11 +440,17 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 100 MiB device-to-device copy before timing (a dispatch of "
                          "known size that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--loop", action="store_true",
+                    help="time the multi-step decode loop (batch 32, planned on the device) and "
+                         "report steps/s instead of the single-step metric")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.loop:
+        run_loop(args)
+        return
     stack = args.workload == "llada8b_stack32_b16_l4096"
     steps_k = args.steps if args.steps is not None else (5 if stack else 200)
     warmup = args.warmup if args.warmup is not None else (1 if stack else 20)

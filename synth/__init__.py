@@ -491,9 +491,10 @@ def small_loop_d128(materialize=True) -> LoopWorkload:
                       tracked, 32, 16, 2, 5, materialize)
 
 
-def llada8b_loop_b32(materialize=False) -> LoopWorkload:
+def llada8b_loop_b32(materialize=False, steps=16) -> LoopWorkload:
     """The batch-32 ragged layer (hidden 4096, 32 x 128, lengths U{512..1024})
-    run as a 16-step loop: each sequence starts at its window start with its
+    run as a loop (16 steps unless ``steps`` says otherwise): each sequence
+    starts at its window start with its
     32 tracked rows; window 32, budget 32, refresh every fourth step (stages
     staggered across the batch).  Tensors are drawn on the GPU
     (``loop_tensors``)."""
@@ -505,7 +506,7 @@ def llada8b_loop_b32(materialize=False) -> LoopWorkload:
         f0.append(int(rows[0]))
         tracked.append([int(p) for p in rows[32:]])
     return build_loop("llada8b_loop_b32", 23, 4096, 32, 128, 32, 5.0e5,
-                      [int(n) for n in base.kv_len], f0, tracked, 32, 32, 4, 16, materialize)
+                      [int(n) for n in base.kv_len], f0, tracked, 32, 32, 4, steps, materialize)
 
 
 def loop_tensors(wl: LoopWorkload, device):
