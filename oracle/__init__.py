@@ -16,7 +16,8 @@ Sources (PUBLIC web pages about one preprint; cited by short key):
 * [P2] the arXiv abstract page of the same preprint (abstract).
 
 ``reference`` holds one per-layer step; ``loop`` chains such steps into
-a weight-free multi-step loop (planning rules stated in its docstring).
+a weight-free multi-step loop (planning rules stated in its docstring);
+``lm_head`` is the mask-view confidence producer that feeds the accept scan.
 
 Every function states the passage it follows.  Where the pages are silent the
 function states the reading it takes; the same readings are listed in the
@@ -47,4 +48,8 @@ from .loop import (  # noqa: F401
     plan_step,
     hidden_rows,
     decode_loop,
+)
+from .lm_head import (  # noqa: F401
+    lm_head_confidence,
+    verify_chain,
 )

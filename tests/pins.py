@@ -535,4 +535,76 @@ def pin_decode_loop_closed_form_frontier(seed=12):
         assert np.array_equal(np.diff(rec["cu_rows"])[done], np.zeros(int(done.sum())))
 
 
+# --- mask-view confidence producer (LM head) ----------------------------------------
+
+def _one_hot_head(columns):
+    """Hidden rows e_0 and a weight whose column 0 holds each row's logits: the
+    logits of row r are exactly columns[r] (bf16-exact values)."""
+    cols = np.asarray(columns, np.float64)  # [rows, vocab]
+    rows, vocab = cols.shape
+    hid = rows + 2
+    w = np.zeros((vocab, hid))
+    h = np.zeros((rows, hid))
+    for r in range(rows):
+        w[:, r] = cols[r]
+        h[r, r] = 1.0
+    return bits(h), bits(w)
+
+
+def pin_lm_head_hand():
+    """Hand-worked tokens and confidences: a dominant logit, tied maxima (lower
+    id), uniform logits (1/V), logits past exp's range, the maximum last."""
+    gd = golden("lm_head_hand.json")
+    for c in gd["cases"]:
+        h, w = _one_hot_head([c["logits"]])
+        tok, conf, _ = O.lm_head_confidence(h, w)
+        want = eval(c["conf"], {"__builtins__": {}}, {"exp": math.exp})
+        assert int(tok[0]) == c["token"], (c, tok)
+        assert abs(conf[0] - want) <= 1e-12 * want, (c, conf[0], want)
+
+
+def pin_lm_head_brute(seed=13):
+    """Tiny random heads against pure-Python logits, argmax and softmax."""
+    g = np.random.default_rng(seed)
+    for _ in range(20):
+        rows, vocab, hid = int(g.integers(1, 5)), int(g.integers(1, 9)), int(g.integers(1, 6))
+        h = bits(np.round(g.standard_normal((rows, hid)) * 8) / 8)
+        w = bits(np.round(g.standard_normal((vocab, hid)) * 8) / 8)
+        tok, conf, _ = O.lm_head_confidence(h, w)
+        hf, wf = O.bf16_bits_to_f64(h), O.bf16_bits_to_f64(w)
+        for r in range(rows):
+            z = [sum(float(hf[r, k]) * float(wf[v, k]) for k in range(hid)) for v in range(vocab)]
+            best = max(range(vocab), key=lambda v: (z[v], -v))
+            p = math.exp(z[best]) / sum(math.exp(zv) for zv in z)
+            assert int(tok[r]) == best and abs(conf[r] - p) <= 1e-12, (r, z, tok[r], conf[r], p)
+
+
+def pin_verify_chain_hand():
+    """Draft tokens from the draft rows, tokens and confidences from the mask
+    rows, then the accept scan (hand-worked in the fixture)."""
+    gd = golden("lm_head_hand.json")["chain"]
+    # vocab 4; logits built so the argmax and the confidence are known:
+    # confidence c for token t with the other three logits at 0 needs
+    # exp(a) / (3 + exp(a)) = c, i.e. a = ln(3c / (1 - c)); rounded to bf16 the
+    # probability moves a little but stays on the same side of 0.5.
+    def row(t, c):
+        a = math.log(3 * c / (1 - c))
+        z = [0.0] * 4
+        z[t] = float(O.bf16_bits_to_f64(O.f64_to_bf16_bits(a)))
+        return z
+    draft = [row(1, 0.9), row(2, 0.9), row(0, 0.9), row(3, 0.9), row(3, 0.9), row(1, 0.9)]
+    mask = [row(1, 0.8), row(2, 0.6), row(1, 0.9), row(3, 0.9), row(3, 0.4), row(1, 0.9)]
+    hd, w_d = _one_hot_head(draft)
+    hm, w_m = _one_hot_head(mask)
+    # one head for both views: stack the two weights' columns
+    w = np.concatenate([O.bf16_bits_to_f64(w_d), O.bf16_bits_to_f64(w_m)], axis=1)
+    hdd = np.concatenate([O.bf16_bits_to_f64(hd), np.zeros_like(O.bf16_bits_to_f64(hm))], axis=1)
+    hmm = np.concatenate([np.zeros_like(O.bf16_bits_to_f64(hd)), O.bf16_bits_to_f64(hm)], axis=1)
+    dtok, mtok, conf, acc = O.verify_chain(bits(hdd), bits(hmm), bits(w), 2, 3,
+                                           np.float32(gd["threshold"]))
+    assert dtok.tolist() == [[1, 2, 0], [3, 3, 1]], dtok
+    assert mtok.tolist() == [[1, 2, 1], [3, 3, 1]], mtok
+    assert acc.tolist() == gd["expect_accept"], acc
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -5,12 +5,14 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle.lm_head as LH
 import oracle.loop as LP
 import oracle.reference as R
 from tests import pins
 
 _orig = {name: getattr(R, name) for name in dir(R) if callable(getattr(R, name))}
 _orig_loop = {name: getattr(LP, name) for name in ("plan_step", "hidden_rows", "decode_loop")}
+_orig_lm = {name: getattr(LH, name) for name in ("lm_head_confidence", "verify_chain")}
 
 
 def _truncating_bf16(x):
@@ -209,6 +211,34 @@ def _loop_variant(kind):
     return loop
 
 
+def _lm_variant(kind):
+    def lm(h_bits, w_bits):
+        z = R.bf16_bits_to_f64(h_bits) @ R.bf16_bits_to_f64(w_bits).T
+        if kind == "hi_ties":
+            tok = (z.shape[1] - 1 - np.argmax(z[:, ::-1], axis=1)).astype(np.int32)
+        else:
+            tok = np.argmax(z, axis=1).astype(np.int32)
+        zmax = z[np.arange(z.shape[0]), tok]
+        if kind == "no_shift":
+            with np.errstate(over="ignore", invalid="ignore"):
+                conf = np.exp(zmax) / np.exp(z).sum(axis=1)
+        elif kind == "max_logit":
+            conf = 1.0 / (1.0 + np.exp(-zmax))
+        else:
+            conf = 1.0 / np.exp(z - zmax[:, None]).sum(axis=1)
+        return tok, conf, z
+    return lm
+
+
+def _chain_draft_conf(h_draft_bits, h_mask_bits, w_bits, batch, window, threshold):
+    dtok, dconf, _ = LH.lm_head_confidence(h_draft_bits, w_bits)
+    mtok, _, _ = LH.lm_head_confidence(h_mask_bits, w_bits)
+    dtok, mtok, conf = (a.reshape(batch, window) for a in (dtok, mtok, dconf))
+    acc = np.array([R.accept_length(dtok[b], mtok[b], conf[b], threshold) for b in range(batch)],
+                   np.int32)
+    return dtok, mtok, conf, acc
+
+
 MUTANTS = {
     "bf16_truncates": ("f64_to_bf16_bits", _truncating_bf16),
     "gemm_drops_term": ("qkv_projection", _gemm_dropped_term),
@@ -232,13 +262,18 @@ MUTANTS = {
     "hidden_rows_le": ("hidden_rows", _hidden_le),
     "loop_no_carry": ("decode_loop", _loop_variant("no_carry")),
     "loop_stale_tracked": ("decode_loop", _loop_variant("stale_tracked")),
+    "lm_head_high_ties": ("lm_head_confidence", _lm_variant("hi_ties")),
+    "lm_head_unshifted_softmax": ("lm_head_confidence", _lm_variant("no_shift")),
+    "lm_head_sigmoid_conf": ("lm_head_confidence", _lm_variant("max_logit")),
+    "chain_draft_confidence": ("verify_chain", _chain_draft_conf),
 }
 
 
 @pytest.mark.parametrize("mutant", sorted(MUTANTS))
 def test_some_pin_catches(mutant, monkeypatch):
     name, fn = MUTANTS[mutant]
-    monkeypatch.setattr(LP if name in _orig_loop else R, name, fn)
+    mod = LP if name in _orig_loop else LH if name in _orig_lm else R
+    monkeypatch.setattr(mod, name, fn)
     if hasattr(oracle, name):
         monkeypatch.setattr(oracle, name, fn)
     caught = []
