@@ -256,6 +256,30 @@ int gather_hidden(int32_t batch, int32_t row_capacity, const int32_t *cu_rows,
                   const void *hidden_committed, const void *hidden_masked,
                   int32_t max_len, int32_t hidden, void *x_out, void *stream);
 
+/* Mask-view confidence producer [P4 para 3: a position is accepted when the
+ * two views agree and the mask-view confidence exceeds the threshold].
+ * Reading: the LM head maps each row's final hidden state to vocabulary
+ * logits z = h . W^T (bf16 inputs, fp32 accumulate); the row's token is the
+ * argmax (equal logits go to the lower id) and its confidence the softmax
+ * probability of that token, 1 / sum_v exp(z_v - z_max).  The logits never
+ * reach memory.  Applied to the draft rows it gives the draft tokens, to the
+ * mask rows the tokens and confidences that verify_accept compares.
+ *   hidden_states  device bf16 [rows][hidden]
+ *   w_lm           device bf16 [vocab][hidden] (the nn.Linear weight; no bias)
+ *   token_out      device int32 [rows]; conf_out device fp32 [rows]
+ *   workspace      device scratch of fdl_lm_head_workspace_bytes(rows, vocab)
+ *                  bytes (per-tile partial maxima, sums and ids).
+ * hidden must be a multiple of 32 and at most 65536 (FDL_EUNSUPPORTED);
+ * rows == 0 is a no-op.  Results are bitwise reproducible (fixed-order
+ * reductions). */
+int lm_head_confidence(const void *hidden_states, const void *w_lm, int32_t rows,
+                       int32_t vocab, int32_t hidden, int32_t *token_out,
+                       float *conf_out, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* Workspace bytes lm_head_confidence needs (0 for invalid sizes). */
+size_t fdl_lm_head_workspace_bytes(int32_t rows, int32_t vocab);
+
 /* Text for a status code (static storage). */
 const char *fdl_status_string(int status);
 

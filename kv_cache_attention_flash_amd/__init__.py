@@ -12,6 +12,7 @@ Calls (same names as the C ABI):
   verify_accept        Flash-Verify accepted-prefix lengths
   decode_plan          next loop step's rows, planned on the device
   gather_hidden        hidden-state rows of the planned rows
+  lm_head_confidence   argmax token and softmax confidence of each row (LM head)
 
 DecodeStep binds one step to fixed buffers; DecodeLoop chains steps with the
 planning on the device (no host round trip between steps).
@@ -34,7 +35,8 @@ from ._lib import FdlError, KVCacheStruct  # noqa: F401
 __all__ = ["PagedKVCache", "flash_cache_step", "flash_cache_step_unfused", "scheduled_attention",
            "track_topb", "verify_accept", "attention_workspace_bytes",
            "flash_cache_workspace_bytes", "flash_cache_unfused_workspace_bytes", "DecodeStep",
-           "decode_plan", "gather_hidden", "DecodeLoop", "FdlError", "load"]
+           "decode_plan", "gather_hidden", "DecodeLoop", "lm_head_confidence",
+           "lm_head_workspace_bytes", "FdlError", "load"]
 
 
 def load():
@@ -535,3 +537,39 @@ class DecodeLoop:
         self.run_attention(s)
         self.run_topb(s)
         self.run_verify(t, s)
+
+
+def lm_head_workspace_bytes(rows, vocab) -> int:
+    return int(_lib.load().fdl_lm_head_workspace_bytes(int(rows), int(vocab)))
+
+
+def lm_head_confidence(hidden_states, w_lm, token_out=None, conf_out=None, workspace=None,
+                       stream=None):
+    """Per row of ``hidden_states`` (bf16 [rows, hidden]) the argmax token of
+    the logits h . w_lm^T (w_lm bf16 [vocab, hidden]; equal logits go to the
+    lower id) and its softmax probability.  Returns (token int32 [rows],
+    conf fp32 [rows])."""
+    lib = _lib.load()
+    _need(hidden_states, "hidden_states", torch.bfloat16, 2)
+    _need(w_lm, "w_lm", torch.bfloat16, 2)
+    rows, hid = hidden_states.shape
+    vocab = w_lm.shape[0]
+    if w_lm.shape[1] != hid:
+        raise ValueError(f"w_lm must be [vocab, {hid}], got {tuple(w_lm.shape)}")
+    dev = hidden_states.device
+    if token_out is None:
+        token_out = torch.empty((rows,), dtype=torch.int32, device=dev)
+    if conf_out is None:
+        conf_out = torch.empty((rows,), dtype=torch.float32, device=dev)
+    _need(token_out, "token_out", torch.int32, 1)
+    _need(conf_out, "conf_out", torch.float32, 1)
+    if token_out.numel() < rows or conf_out.numel() < rows:
+        raise ValueError("token_out/conf_out need one entry per row")
+    need = lm_head_workspace_bytes(rows, vocab)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    st = lib.lm_head_confidence(hidden_states.data_ptr(), w_lm.data_ptr(), rows, vocab, hid,
+                                token_out.data_ptr(), conf_out.data_ptr(),
+                                workspace.data_ptr(), workspace.numel(), _stream(stream, dev))
+    _lib.check("lm_head_confidence", st)
+    return token_out, conf_out

@@ -45,6 +45,9 @@ EXPORTS = {
                                    c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp]),
     "gather_hidden": (ctypes.c_int, [c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
                                      c_vp, c_vp]),
+    "lm_head_confidence": (ctypes.c_int, [c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,
+                                          c_size, c_vp]),
+    "fdl_lm_head_workspace_bytes": (c_size, [c_i32, c_i32]),
     "fdl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fdl_last_hip_error": (ctypes.c_int, []),
     "fdl_version": (ctypes.c_char_p, []),

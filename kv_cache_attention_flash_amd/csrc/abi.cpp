@@ -278,4 +278,31 @@ int gather_hidden(int32_t batch, int32_t row_capacity, const int32_t *cu_rows,
   return hip_status(fdl::launch_gather_hidden(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t fdl_lm_head_workspace_bytes(int32_t rows, int32_t vocab) {
+  if (rows < 0 || vocab <= 0) return 0;
+  return fdl::lm_head_workspace_bytes(rows, vocab);
+}
+
+int lm_head_confidence(const void *hidden_states, const void *w_lm, int32_t rows, int32_t vocab,
+                       int32_t hidden, int32_t *token_out, float *conf_out, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+  if (rows < 0 || vocab <= 0 || hidden <= 0) return FDL_EINVAL;
+  if (hidden % 32 != 0 || hidden > 65536) return FDL_EUNSUPPORTED;
+  if (rows == 0) return FDL_OK;
+  if (!hidden_states || !w_lm || !token_out || !conf_out) return FDL_EINVAL;
+  const size_t need = fdl::lm_head_workspace_bytes(rows, vocab);
+  if (workspace_bytes < need || !workspace) return FDL_EWORKSPACE;
+  fdl::LmHeadArgs a;
+  a.h = static_cast<const uint16_t *>(hidden_states);
+  a.w = static_cast<const uint16_t *>(w_lm);
+  a.rows = rows;
+  a.vocab = vocab;
+  a.hidden = hidden;
+  a.token = token_out;
+  a.conf = conf_out;
+  a.part_ml = nullptr;
+  a.part_idx = nullptr;
+  return hip_status(fdl::launch_lm_head(a, workspace, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -85,4 +85,18 @@ struct GatherArgs {
 
 hipError_t launch_gather_hidden(const GatherArgs &a, hipStream_t s);
 
+// Mask-view confidence producer (lm_head.hip).
+struct LmHeadArgs {
+  const uint16_t *h, *w;  // bf16 [rows][hidden], [vocab][hidden]
+  int rows, vocab, hidden;
+  int32_t *token;
+  float *conf;
+  float *part_ml;     // workspace: [rows][col tiles][2] (max, sum of exp)
+  int32_t *part_idx;  // workspace: [rows][col tiles]
+};
+
+int lm_head_col_tiles(int vocab);
+size_t lm_head_workspace_bytes(int rows, int vocab);
+hipError_t launch_lm_head(LmHeadArgs a, void *ws, hipStream_t s);
+
 }  // namespace fdl

@@ -10,7 +10,8 @@ with streams 0 X, 1 W, 2 K cache, 3 V cache, 4 window/tracked positions,
 5 block permutation, 6 lengths, 8 draft tokens, 9 agreement, 10 replacement
 tokens, 11 confidences, 12 and 13 the committed- and masked-token hidden-state
 tables of a multi-step loop (whose per-step scan draws use the step as the
-``layer`` key).  Real values are drawn as standard normals in fp32
+``layer`` key), 14 the LM-head weight, 15 the mask rows' final hidden states,
+16 the draft rows' perturbation.  Real values are drawn as standard normals in fp32
 (the weight scaled by 0.02 in fp32) and rounded to bf16 by torch's CPU cast.
 The large 32-layer stack draws its tensors on the GPU with torch's seeded
 generator instead (host generation of ~19 G values would take minutes); those
@@ -30,6 +31,7 @@ import numpy as np
 STREAM_X, STREAM_W, STREAM_K, STREAM_V, STREAM_POS, STREAM_PERM, STREAM_LEN = 0, 1, 2, 3, 4, 5, 6
 STREAM_DRAFT, STREAM_AGREE, STREAM_REPL, STREAM_CONF = 8, 9, 10, 11
 STREAM_HID_COMMITTED, STREAM_HID_MASKED = 12, 13
+STREAM_LM_W, STREAM_LM_H, STREAM_LM_NOISE = 14, 15, 16
 
 
 def rng(workload_id: int, layer: int, stream: int) -> np.random.Generator:
@@ -534,6 +536,102 @@ def loop_tensors(wl: LoopWorkload, device):
         out.append(t.to(torch.bfloat16))
         del t
     return tuple(out)
+
+
+# ---------------------------------------------------------------------------
+# Mask-view confidence producer workloads (LM head)
+# ---------------------------------------------------------------------------
+
+
+@dataclasses.dataclass
+class LmHeadWorkload:
+    """Final hidden states of the window rows of a two-view step and an LM head.
+
+    ``h_mask`` bf16 [batch*window, hid] are the mask rows; the draft rows
+    ``h_draft`` are the same states plus ``noise`` x N(0,1) (drawn in fp32,
+    then rounded), so the two views mostly agree.  ``w`` bf16 [vocab, hid] is
+    N(0,1) x ``w_std``: with w_std = 16 / sqrt(hid) the logits have standard
+    deviation about 16; over the 126464-token vocabulary the top token's
+    probability then spreads over (0, 1) with a median near 0.87, so the 0.9f
+    threshold splits the positions (a draft noise of 0.1 leaves about 3 in 4
+    argmaxes unchanged).
+    """
+    name: str
+    workload_id: int
+    hid: int
+    vocab: int
+    batch: int
+    window: int
+    w_std: float
+    noise: float
+    threshold: np.float32 = np.float32(0.9)
+    w: Optional[np.ndarray] = None
+    h_mask: Optional[np.ndarray] = None
+    h_draft: Optional[np.ndarray] = None
+
+    @property
+    def rows(self) -> int:
+        return self.batch * self.window
+
+
+def build_lm_head(name, workload_id, hid, vocab, batch, window, materialize=True):
+    wl = LmHeadWorkload(name, workload_id, hid, vocab, batch, window,
+                        w_std=16.0 / float(np.sqrt(hid)), noise=0.1)
+    if materialize:
+        wl.w = normal_bf16(workload_id, 0, STREAM_LM_W, (vocab, hid), scale=wl.w_std)
+        base = rng(workload_id, 0, STREAM_LM_H).standard_normal((wl.rows, hid), dtype=np.float32)
+        noise = rng(workload_id, 0, STREAM_LM_NOISE).standard_normal((wl.rows, hid),
+                                                                     dtype=np.float32)
+        wl.h_mask = to_bf16_bits(base)
+        wl.h_draft = to_bf16_bits(base + np.float32(wl.noise) * noise)
+    return wl
+
+
+def tiny_lm_head(materialize=True) -> LmHeadWorkload:
+    """Vocabulary 77 (less than one column tile), hidden 64, 2 sequences x 3 rows."""
+    return build_lm_head("tiny_lmhead_v77", 31, 64, 77, 2, 3, materialize)
+
+
+def small_lm_head(materialize=True) -> LmHeadWorkload:
+    """Vocabulary 1000 (a ragged last column tile), hidden 256, 3 sequences x
+    16 window rows (48 draft + 48 mask rows: a ragged row tile)."""
+    return build_lm_head("small_lmhead_v1000", 32, 256, 1000, 3, 16, materialize)
+
+
+def llada8b_lm_head_b8(materialize=False) -> LmHeadWorkload:
+    """The two-view batch-8 step's window rows through an LLaDA-8B-class head:
+    vocabulary 126464, hidden 4096, 8 sequences x 32 rows per view (256 draft
+    + 256 mask rows).  Tensors are drawn on the GPU (``lm_head_tensors``)."""
+    return build_lm_head("llada8b_lmhead_b8", 33, 4096, 126464, 8, 32, materialize)
+
+
+def lm_head_tensors(wl: LmHeadWorkload, device):
+    """(w, h_draft, h_mask) as torch bf16 tensors on ``device``: host draws when
+    materialized, else torch's seeded generator on the device (seed =
+    workload*1e6 + stream), the draft rows being the mask rows plus the noise."""
+    import torch
+    if wl.w is not None:
+        def dev(a):
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        return dev(wl.w), dev(wl.h_draft), dev(wl.h_mask)
+
+    def draw(stream, shape):
+        g = torch.Generator(device=device)
+        g.manual_seed(wl.workload_id * 1_000_000 + stream)
+        return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    w = draw(STREAM_LM_W, (wl.vocab, wl.hid)).mul_(wl.w_std).to(torch.bfloat16)
+    base = draw(STREAM_LM_H, (wl.rows, wl.hid))
+    noise = draw(STREAM_LM_NOISE, (wl.rows, wl.hid))
+    h_mask = base.to(torch.bfloat16)
+    h_draft = base.add_(noise.mul_(wl.noise)).to(torch.bfloat16)
+    return w, h_draft, h_mask
+
+
+LM_HEAD_WORKLOADS = {
+    "tiny_lmhead_v77": tiny_lm_head,
+    "small_lmhead_v1000": small_lm_head,
+    "llada8b_lmhead_b8": llada8b_lm_head_b8,
+}
 
 
 LOOP_WORKLOADS = {

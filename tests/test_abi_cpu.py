@@ -178,3 +178,20 @@ def test_gather_hidden_validation(lib):
     assert gather(x=fake + 2) == _lib.FDL_EINVAL
     assert gather(batch=0) == _lib.FDL_OK
     assert gather(cap=0) == _lib.FDL_OK
+
+
+def test_lm_head_validation(lib):
+    fake = 0x10000
+    ws = lib.fdl_lm_head_workspace_bytes(4, 1000)
+    assert ws > 0 and lib.fdl_lm_head_workspace_bytes(-1, 10) == 0
+    def call(rows=4, vocab=1000, hid=256, h=fake, w=fake, tok=fake, conf=fake, wsp=fake, wsb=ws):
+        return lib.lm_head_confidence(h, w, rows, vocab, hid, tok, conf, wsp, wsb, None)
+    assert call(hid=100) == _lib.FDL_EUNSUPPORTED            # not a multiple of 32
+    assert call(hid=65536 + 32) == _lib.FDL_EUNSUPPORTED
+    assert call(vocab=0) == _lib.FDL_EINVAL
+    assert call(rows=-1) == _lib.FDL_EINVAL
+    assert call(h=None) == _lib.FDL_EINVAL
+    assert call(conf=None) == _lib.FDL_EINVAL
+    assert call(wsb=ws - 1) == _lib.FDL_EWORKSPACE
+    assert call(wsp=None) == _lib.FDL_EWORKSPACE
+    assert call(rows=0) == _lib.FDL_OK
