@@ -532,6 +532,9 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 100 MiB device-to-device copy before timing (a dispatch of "
                          "known size that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--fused", action="store_true",
+                    help="time flash_cache_attention_step (projection, attention and mass in one "
+                         "launch) in place of the two calls")
     ap.add_argument("--loop", action="store_true",
                     help="time the multi-step decode loop (batch 32, planned on the device) and "
                          "report steps/s instead of the single-step metric")
@@ -591,7 +594,7 @@ def main():
     def make_step(cache, x, w):
         return fd.DecodeStep(cache, x, w, cu, pos, slots, kv, wl.rope_base, wl.max_kv_len,
                              max_rows, views=views, topb=wl.topb, verify=verify,
-                             unfused=args.unfused)
+                             unfused=args.unfused, fused=args.fused)
 
     # units[i % len(units)] = the per-layer steps that make up logical step i
     units = []
@@ -634,9 +637,13 @@ def main():
     for i in range(K):
         for st, e in zip(units[i % len(units)], ev[i]):
             ht.record(e[0], sh)
-            st.run_flash_cache(sh)
+            if args.fused:
+                st.run_fused(sh)  # one launch: its time is booked to the first bracket
+            else:
+                st.run_flash_cache(sh)
             ht.record(e[1], sh)
-            st.run_attention(sh)
+            if not args.fused:
+                st.run_attention(sh)
             ht.record(e[2], sh)
             st.run_topb(sh)
             st.run_verify(sh)
@@ -652,6 +659,16 @@ def main():
     rf_fc = roofline_entry(fc_call, wl, fcs_ms, args.workload)
     rf_att = roofline_entry("scheduled_attention", wl, att_ms, args.workload)
     dominant, other = (rf_fc, rf_att) if fcs_ms >= att_ms else (rf_att, rf_fc)
+    if args.fused:
+        # one launch: its algorithmic bytes are both calls' (HBM-bound at this AI)
+        nb_f = flash_cache_bytes(wl) + attention_bytes(wl)
+        ach = nb_f / (fcs_ms / 1e3) / 1e9
+        dominant = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "flash_cache_attention_step", "algorithmic_bytes": nb_f,
+                    "algorithmic_flops": flash_cache_flops(wl) + attention_flops(wl),
+                    "avg_launch_us": round(fcs_ms * 1e3, 2)}
+        other = None
     log(f"step {ms_per_step * 1e3:.1f} us ({layers_per_step} layer(s)); flash_cache_step "
         f"{fcs_ms * 1e3:.1f} us ({rf_fc['achieved']} {rf_fc['unit']}); scheduled_attention "
         f"{att_ms * 1e3:.1f} us ({rf_att['achieved']} {rf_att['unit']})")
@@ -682,6 +699,9 @@ def main():
     tail = (" + scheduled_attention(+mass) + track_topb" if wl.topb else " + scheduled_attention")
     if args.unfused:
         tail += " [ablation: flash_cache_step_unfused, three launches with HBM intermediates]"
+    if args.fused:
+        tail += (" [flash_cache_attention_step: projection, attention and mass in one launch; "
+                 "its whole time is in the flash_cache_step bracket]")
     tail += " + verify_accept" if verify is not None else ""
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s/layer", "n_gpus": 1,

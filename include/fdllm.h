@@ -201,6 +201,41 @@ int verify_accept(const int32_t *draft_tok, const int32_t *mask_tok,
                   const float *conf, int32_t batch, int32_t window,
                   float threshold, int32_t *accept_len_out, void *stream);
 
+/* Single-launch step [P4 para 1: the fused cache kernel combined with
+ * scheduled attention]: flash_cache_step followed by scheduled_attention with
+ * the mass, as one persistent launch.  Arguments as for those two calls (the
+ * attention reads the q_out this call writes); mass must not be NULL.
+ * Results are bitwise those of the two separate calls: each phase runs the
+ * same workgroup code.  The launch is cooperative (every workgroup resident):
+ * the attention phase starts when every projection workgroup has finished,
+ * the mass phase when every attention workgroup has; hand-offs between
+ * workgroups use device-scope release/acquire on counters in the workspace.
+ *   workspace  fdl_fused_step_workspace_bytes(...) bytes.  Its first 256
+ *              bytes hold the counters and an error word: they must be zero
+ *              before the first call (for example a zero-filled allocation);
+ *              each call leaves the counters zero.  The error word (int32 at
+ *              byte 12) becomes 1 if a phase wait ever timed out, which a
+ *              cooperative launch rules out; results are then invalid.  Calls
+ *              sharing a workspace must not run at the same time.
+ * Supported: the shapes whose separate calls take a one-launch projection (no
+ * split reduction) and the row-group attention path (few sequences x heads,
+ * caches up to 1024 keys); otherwise FDL_EUNSUPPORTED and nothing launched. */
+int flash_cache_attention_step(const fdl_kv_cache *cache, const void *x, int32_t hidden,
+                               const void *w_qkv, int32_t batch, int32_t num_rows,
+                               const int32_t *cu_rows, const int32_t *positions,
+                               const int32_t *slots, float rope_base, void *q_out,
+                               int64_t *slot_mapping_out, const int32_t *kv_len,
+                               int32_t max_kv_len, int32_t max_rows_per_seq,
+                               const fdl_two_view *views, float softmax_scale, float *out,
+                               float *mass, int32_t mass_stride, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* Workspace bytes flash_cache_attention_step needs (0 for invalid sizes;
+ * mass_stride > 0). */
+size_t fdl_fused_step_workspace_bytes(int32_t batch, int32_t num_rows, int32_t num_heads,
+                                      int32_t head_dim, int32_t max_kv_len,
+                                      int32_t max_rows_per_seq, int32_t mass_stride);
+
 /* Planning step of a multi-step decoding loop [P4 para 2: each step's query
  * rows are a sliding unmasking window plus a fixed budget of the most-attended
  * tokens; P4 para 1: caching (refresh) and update stages alternate within a

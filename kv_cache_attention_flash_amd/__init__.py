@@ -13,6 +13,7 @@ Calls (same names as the C ABI):
   decode_plan          next loop step's rows, planned on the device
   gather_hidden        hidden-state rows of the planned rows
   lm_head_confidence   argmax token and softmax confidence of each row (LM head)
+  flash_cache_attention_step  flash_cache_step + scheduled_attention (+ mass) in one launch
 
 DecodeStep binds one step to fixed buffers; DecodeLoop chains steps with the
 planning on the device (no host round trip between steps).
@@ -36,7 +37,8 @@ __all__ = ["PagedKVCache", "flash_cache_step", "flash_cache_step_unfused", "sche
            "track_topb", "verify_accept", "attention_workspace_bytes",
            "flash_cache_workspace_bytes", "flash_cache_unfused_workspace_bytes", "DecodeStep",
            "decode_plan", "gather_hidden", "DecodeLoop", "lm_head_confidence",
-           "lm_head_workspace_bytes", "FdlError", "load"]
+           "lm_head_workspace_bytes", "flash_cache_attention_step", "fused_step_workspace_bytes",
+           "FdlError", "load"]
 
 
 def load():
@@ -273,7 +275,7 @@ class DecodeStep:
 
     def __init__(self, cache: PagedKVCache, x, w_qkv, cu_rows, positions, slots, kv_len,
                  rope_base, max_kv_len, max_rows_per_seq, views=None, topb=0,
-                 softmax_scale=0.0, verify=None, unfused=False):
+                 softmax_scale=0.0, verify=None, unfused=False, fused=False):
         self.lib = _lib.load()
         dev = x.device
         r = x.shape[0]
@@ -313,6 +315,22 @@ class DecodeStep:
                      self.workspace.data_ptr(), self.workspace.numel())
         self._top = ((self.mass.data_ptr(), self.mass_stride, kv_len.data_ptr(), self.batch,
                       self.topb, self.idx.data_ptr()) if self.topb else None)
+        # fused: flash_cache_attention_step in place of the two calls (needs the mass).
+        self._fus = None
+        if fused:
+            if not self.topb:
+                raise ValueError("the single-launch step forms the mass: topb must be > 0")
+            fus_need = fused_step_workspace_bytes(self.batch, r, h, d, int(max_kv_len),
+                                                  int(max_rows_per_seq), self.mass_stride)
+            self.fused_workspace = torch.zeros((max(fus_need, 256),), dtype=torch.uint8,
+                                               device=dev)
+            self._fus = (ctypes.byref(self.cs), x.data_ptr(), x.shape[1], w_qkv.data_ptr(),
+                         self.batch, r, cu_rows.data_ptr(), positions.data_ptr(),
+                         slots.data_ptr(), float(rope_base), self.q.data_ptr(),
+                         self.slot_mapping.data_ptr(), kv_len.data_ptr(), int(max_kv_len),
+                         int(max_rows_per_seq), _ptr(views), float(softmax_scale),
+                         self.out.data_ptr(), self.mass.data_ptr(), self.mass_stride,
+                         self.fused_workspace.data_ptr(), self.fused_workspace.numel())
         # Optional accept scan after the step: (draft, mask, conf, threshold).
         self._ver = None
         if verify is not None:
@@ -328,6 +346,10 @@ class DecodeStep:
     def run_flash_cache(self, stream: int):
         _lib.check(self._fc_name, self._fc_fn(*self._fcs, stream))
 
+    def run_fused(self, stream: int):
+        _lib.check("flash_cache_attention_step",
+                   self.lib.flash_cache_attention_step(*self._fus, stream))
+
     def run_attention(self, stream: int):
         _lib.check("scheduled_attention", self.lib.scheduled_attention(*self._att, stream))
 
@@ -341,8 +363,11 @@ class DecodeStep:
 
     def run(self, stream: Optional[int] = None):
         s = _stream(stream, self.x.device) if not isinstance(stream, int) else stream
-        self.run_flash_cache(s)
-        self.run_attention(s)
+        if self._fus is not None:
+            self.run_fused(s)
+        else:
+            self.run_flash_cache(s)
+            self.run_attention(s)
         self.run_topb(s)
         self.run_verify(s)
 
@@ -573,3 +598,80 @@ def lm_head_confidence(hidden_states, w_lm, token_out=None, conf_out=None, works
                                 workspace.data_ptr(), workspace.numel(), _stream(stream, dev))
     _lib.check("lm_head_confidence", st)
     return token_out, conf_out
+
+
+def fused_step_workspace_bytes(batch, num_rows, num_heads, head_dim, max_kv_len, max_rows_per_seq,
+                               mass_stride) -> int:
+    return int(_lib.load().fdl_fused_step_workspace_bytes(batch, num_rows, num_heads, head_dim,
+                                                          max_kv_len, max_rows_per_seq,
+                                                          mass_stride))
+
+
+_FUSED_WS = {}
+
+
+def _fused_workspace(device, stream_handle: int, nbytes: int):
+    """Zero-filled workspace per (device, stream): its first 256 bytes are the
+    single-launch step's counters, which every call leaves at zero."""
+    key = (device.index if device.index is not None else torch.cuda.current_device(), stream_handle)
+    ws = _FUSED_WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros((max(nbytes, 256),), dtype=torch.uint8, device=device)
+        _FUSED_WS[key] = ws
+    return ws
+
+
+def flash_cache_attention_step(cache: PagedKVCache, x, w_qkv, cu_rows, positions, slots,
+                               rope_base, kv_len, max_kv_len, max_rows_per_seq, views=None,
+                               softmax_scale=0.0, mass_stride=None, q_out=None,
+                               slot_mapping_out=None, out=None, mass=None, workspace=None,
+                               stream=None):
+    """flash_cache_step then scheduled_attention with the mass, as one launch
+    (bitwise the same results).  ``workspace``, if given, must be zero-filled
+    before its first use.  Returns (q_out, slot_mapping, out, mass)."""
+    lib = _lib.load()
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w_qkv, "w_qkv", torch.bfloat16, 2)
+    for t, n in ((cu_rows, "cu_rows"), (positions, "positions"), (slots, "slots"),
+                 (kv_len, "kv_len")):
+        _need(t, n, torch.int32, 1)
+    r, hid = x.shape
+    h, d = cache.num_heads, cache.head_dim
+    batch = kv_len.numel()
+    if cu_rows.numel() != batch + 1:
+        raise ValueError("cu_rows must have batch + 1 entries")
+    if tuple(w_qkv.shape) != (3 * h * d, hid):
+        raise ValueError(f"w_qkv must be [{3 * h * d}, {hid}], got {tuple(w_qkv.shape)}")
+    if positions.numel() != r or slots.numel() != r:
+        raise ValueError("positions/slots must have one entry per row")
+    if views is not None:
+        _need(views, "views", torch.int32, 2)
+    dev = x.device
+    if q_out is None:
+        q_out = torch.empty((r, h, d), dtype=torch.bfloat16, device=dev)
+    if slot_mapping_out is None:
+        slot_mapping_out = torch.empty((r,), dtype=torch.int64, device=dev)
+    if out is None:
+        out = torch.empty((r, h, d), dtype=torch.float32, device=dev)
+    if mass_stride is None:
+        mass_stride = mass.shape[1] if mass is not None else int(max_kv_len)
+    if mass is None:
+        mass = torch.empty((batch, int(mass_stride)), dtype=torch.float32, device=dev)
+    _need(q_out, "q_out", torch.bfloat16, 3)
+    _need(slot_mapping_out, "slot_mapping_out", torch.int64, 1)
+    _need(out, "out", torch.float32, 3)
+    _need(mass, "mass", torch.float32, 2)
+    sh = _stream(stream, dev)
+    need = fused_step_workspace_bytes(batch, r, h, d, int(max_kv_len), int(max_rows_per_seq),
+                                      int(mass_stride))
+    if workspace is None:
+        workspace = _fused_workspace(dev, sh, need)
+    cs = cache.struct()
+    st = lib.flash_cache_attention_step(
+        ctypes.byref(cs), x.data_ptr(), hid, w_qkv.data_ptr(), batch, r, cu_rows.data_ptr(),
+        positions.data_ptr(), slots.data_ptr(), float(rope_base), q_out.data_ptr(),
+        slot_mapping_out.data_ptr(), kv_len.data_ptr(), int(max_kv_len), int(max_rows_per_seq),
+        _ptr(views), float(softmax_scale), out.data_ptr(), mass.data_ptr(), int(mass_stride),
+        workspace.data_ptr(), workspace.numel(), sh)
+    _lib.check("flash_cache_attention_step", st)
+    return q_out, slot_mapping_out, out, mass

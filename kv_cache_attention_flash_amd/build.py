@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libfdllm.so")
 OBJ_DIR = os.path.join(HERE, "_build")
-SOURCES = ["flash_cache.hip", "attention.hip", "select.hip", "loop.hip", "lm_head.hip", "abi.cpp"]
+SOURCES = ["flash_cache.hip", "attention.hip", "select.hip", "loop.hip", "lm_head.hip", "fused.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -71,26 +71,23 @@ const char *fdl_version(void) { return "fdllm 0.1 gfx950"; }
 
 namespace {
 
-// Validation and launch shared by the fused step and its unfused ablation.
-int flash_cache_common(bool unfused, const fdl_kv_cache *cache, const void *x, int32_t hidden,
-                       const void *w_qkv, int32_t batch, int32_t num_rows,
-                       const int32_t *cu_rows, const int32_t *positions, const int32_t *slots,
-                       float rope_base, void *q_out, int64_t *slot_mapping_out,
-                       void *workspace, size_t workspace_bytes, void *stream) {
+// Host validation of flash_cache_step's arguments into launch arguments.
+// Returns a status; empty is set when the call has nothing to do.
+int fc_args(const fdl_kv_cache *cache, const void *x, int32_t hidden, const void *w_qkv,
+            int32_t batch, int32_t num_rows, const int32_t *cu_rows, const int32_t *positions,
+            const int32_t *slots, float rope_base, void *q_out, int64_t *slot_mapping_out,
+            fdl::FlashCacheArgs &a, bool &empty) {
+  empty = false;
   int st = check_cache(cache, true);
   if (st) return st;
   if (batch < 0 || num_rows < 0 || hidden <= 0) return FDL_EINVAL;
   if (!(rope_base > 0.f) || !std::isfinite(rope_base)) return FDL_EINVAL;
   if (hidden % 128 != 0 || hidden > 32768) return FDL_EUNSUPPORTED;
-  if (batch == 0 || num_rows == 0) return FDL_OK;
+  if (batch == 0 || num_rows == 0) {
+    empty = true;
+    return FDL_OK;
+  }
   if (!x || !w_qkv || !cu_rows || !positions || !slots || !q_out) return FDL_EINVAL;
-  const size_t need =
-      unfused ? fdl::flash_cache_unfused_workspace_bytes(num_rows, hidden, cache->num_heads,
-                                                         cache->head_dim)
-              : fdl::flash_cache_workspace_bytes(num_rows, hidden, cache->num_heads,
-                                                 cache->head_dim);
-  if (workspace_bytes < need || (need && !workspace)) return FDL_EWORKSPACE;
-  fdl::FlashCacheArgs a;
   a.c = view_of(cache);
   a.x = static_cast<const uint16_t *>(x);
   a.w = static_cast<const uint16_t *>(w_qkv);
@@ -104,10 +101,79 @@ int flash_cache_common(bool unfused, const fdl_kv_cache *cache, const void *x, i
   a.q_out = static_cast<uint16_t *>(q_out);
   a.slot_mapping = slot_mapping_out;
   a.y_out = nullptr;
+  return FDL_OK;
+}
+
+// Validation and launch shared by the fused step and its unfused ablation.
+int flash_cache_common(bool unfused, const fdl_kv_cache *cache, const void *x, int32_t hidden,
+                       const void *w_qkv, int32_t batch, int32_t num_rows,
+                       const int32_t *cu_rows, const int32_t *positions, const int32_t *slots,
+                       float rope_base, void *q_out, int64_t *slot_mapping_out,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+  fdl::FlashCacheArgs a;
+  bool empty;
+  int st = fc_args(cache, x, hidden, w_qkv, batch, num_rows, cu_rows, positions, slots, rope_base,
+                   q_out, slot_mapping_out, a, empty);
+  if (st || empty) return st;
+  const size_t need =
+      unfused ? fdl::flash_cache_unfused_workspace_bytes(num_rows, hidden, cache->num_heads,
+                                                         cache->head_dim)
+              : fdl::flash_cache_workspace_bytes(num_rows, hidden, cache->num_heads,
+                                                 cache->head_dim);
+  if (workspace_bytes < need || (need && !workspace)) return FDL_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(unfused ? fdl::launch_flash_cache_unfused(a, workspace, workspace_bytes, s)
                             : fdl::launch_flash_cache(a, workspace, workspace_bytes, s));
 }
+
+// Host validation of scheduled_attention's arguments (workspace aside) into
+// launch arguments and the plan.  empty: 1 = no sequences (nothing to check
+// further), 2 = no rows and no mass (nothing to launch once the workspace
+// is checked), 0 = launch.
+int attn_args(const fdl_kv_cache *cache, const void *q, int32_t batch, int32_t num_rows,
+              const int32_t *cu_rows, const int32_t *kv_len, int32_t max_kv_len,
+              int32_t max_rows_per_seq, const fdl_two_view *views, float softmax_scale,
+              float *out, float *mass, int32_t mass_stride, fdl::AttnArgs &a, fdl::AttnPlan &plan,
+              int &empty) {
+  empty = 0;
+  int st = check_cache(cache, true);
+  if (st) return st;
+  if (batch < 0 || num_rows < 0 || max_kv_len < 0 || max_rows_per_seq < 0) return FDL_EINVAL;
+  if (!(softmax_scale >= 0.f) || !std::isfinite(softmax_scale)) return FDL_EINVAL;
+  if ((long)max_kv_len > (long)cache->max_blocks_per_seq * cache->block_size) return FDL_EINVAL;
+  if ((max_kv_len + cache->block_size - 1) / cache->block_size > 1024) return FDL_EUNSUPPORTED;
+  if (mass && mass_stride < max_kv_len) return FDL_EINVAL;
+  if (mass && mass_stride <= 0) return FDL_EINVAL;
+  const int ms = mass ? mass_stride : 0;
+  plan = fdl::plan_attention(batch, num_rows, cache->num_heads, cache->head_dim, max_kv_len,
+                             max_rows_per_seq, ms);
+  if (batch == 0) {
+    empty = 1;
+    return FDL_OK;
+  }
+  if (!cu_rows || !kv_len) return FDL_EINVAL;
+  if (num_rows > 0 && (!q || !out)) return FDL_EINVAL;
+  if (num_rows > 0 && max_rows_per_seq == 0) return FDL_EINVAL;
+  if (num_rows == 0 && !mass) empty = 2;
+  a.c = view_of(cache);
+  a.q = static_cast<const uint16_t *>(q);
+  a.batch = batch;
+  a.rows = num_rows;
+  a.cu_rows = cu_rows;
+  a.kv_len = kv_len;
+  a.max_kv_len = max_kv_len;
+  a.views = reinterpret_cast<const int32_t *>(views);
+  const double scale = softmax_scale > 0.f ? (double)softmax_scale
+                                            : 1.0 / std::sqrt((double)cache->head_dim);
+  a.scale_log2 = (float)(scale * 1.4426950408889634073599246810019);
+  a.out = out;
+  a.mass = mass;
+  a.mass_stride = ms;
+  a.ws = nullptr;
+  return FDL_OK;
+}
+
+constexpr size_t kFusedSyncBytes = 256;  // 4 counters / flags, padded
 
 }  // namespace
 
@@ -162,41 +228,61 @@ int scheduled_attention(const fdl_kv_cache *cache, const void *q, int32_t batch,
                         int32_t max_kv_len, int32_t max_rows_per_seq, const fdl_two_view *views,
                         float softmax_scale, float *out, float *mass, int32_t mass_stride,
                         void *workspace, size_t workspace_bytes, void *stream) {
-  int st = check_cache(cache, true);
-  if (st) return st;
-  if (batch < 0 || num_rows < 0 || max_kv_len < 0 || max_rows_per_seq < 0) return FDL_EINVAL;
-  if (!(softmax_scale >= 0.f) || !std::isfinite(softmax_scale)) return FDL_EINVAL;
-  if ((long)max_kv_len > (long)cache->max_blocks_per_seq * cache->block_size) return FDL_EINVAL;
-  if ((max_kv_len + cache->block_size - 1) / cache->block_size > 1024) return FDL_EUNSUPPORTED;
-  if (mass && mass_stride < max_kv_len) return FDL_EINVAL;
-  if (mass && mass_stride <= 0) return FDL_EINVAL;
-  if (batch == 0) return FDL_OK;
-  if (!cu_rows || !kv_len) return FDL_EINVAL;
-  if (num_rows > 0 && (!q || !out)) return FDL_EINVAL;
-  if (num_rows > 0 && max_rows_per_seq == 0) return FDL_EINVAL;
-  const int ms = mass ? mass_stride : 0;
-  fdl::AttnPlan plan = fdl::plan_attention(batch, num_rows, cache->num_heads, cache->head_dim,
-                                           max_kv_len, max_rows_per_seq, ms);
-  if (plan.bytes > workspace_bytes) return FDL_EWORKSPACE;
-  if (plan.bytes && !workspace) return FDL_EWORKSPACE;
-  if (num_rows == 0 && !mass) return FDL_OK;
   fdl::AttnArgs a;
-  a.c = view_of(cache);
-  a.q = static_cast<const uint16_t *>(q);
-  a.batch = batch;
-  a.rows = num_rows;
-  a.cu_rows = cu_rows;
-  a.kv_len = kv_len;
-  a.max_kv_len = max_kv_len;
-  a.views = reinterpret_cast<const int32_t *>(views);
-  const double scale = softmax_scale > 0.f ? (double)softmax_scale
-                                            : 1.0 / std::sqrt((double)cache->head_dim);
-  a.scale_log2 = (float)(scale * 1.4426950408889634073599246810019);
-  a.out = out;
-  a.mass = mass;
-  a.mass_stride = ms;
+  fdl::AttnPlan plan;
+  int empty;
+  int st = attn_args(cache, q, batch, num_rows, cu_rows, kv_len, max_kv_len, max_rows_per_seq,
+                     views, softmax_scale, out, mass, mass_stride, a, plan, empty);
+  if (st || empty == 1) return st;
+  if (plan.bytes > workspace_bytes || (plan.bytes && !workspace)) return FDL_EWORKSPACE;
+  if (empty) return FDL_OK;
   a.ws = static_cast<char *>(workspace);
   return hip_status(fdl::launch_attention(a, plan, static_cast<hipStream_t>(stream)));
+}
+
+size_t fdl_fused_step_workspace_bytes(int32_t batch, int32_t num_rows, int32_t num_heads,
+                                      int32_t head_dim, int32_t max_kv_len,
+                                      int32_t max_rows_per_seq, int32_t mass_stride) {
+  if (batch < 0 || num_rows < 0 || num_heads <= 0 || head_dim <= 0 || max_kv_len < 0 ||
+      max_rows_per_seq < 0 || mass_stride <= 0)
+    return 0;
+  return kFusedSyncBytes + fdl::plan_attention(batch, num_rows, num_heads, head_dim, max_kv_len,
+                                               max_rows_per_seq, mass_stride)
+                               .bytes;
+}
+
+int flash_cache_attention_step(const fdl_kv_cache *cache, const void *x, int32_t hidden,
+                               const void *w_qkv, int32_t batch, int32_t num_rows,
+                               const int32_t *cu_rows, const int32_t *positions,
+                               const int32_t *slots, float rope_base, void *q_out,
+                               int64_t *slot_mapping_out, const int32_t *kv_len,
+                               int32_t max_kv_len, int32_t max_rows_per_seq,
+                               const fdl_two_view *views, float softmax_scale, float *out,
+                               float *mass, int32_t mass_stride, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  fdl::FlashCacheArgs fa;
+  fdl::AttnArgs aa;
+  fdl::AttnPlan plan;
+  bool empty_fc;
+  int empty_at;
+  int st = fc_args(cache, x, hidden, w_qkv, batch, num_rows, cu_rows, positions, slots,
+                   rope_base, q_out, slot_mapping_out, fa, empty_fc);
+  if (st) return st;
+  st = attn_args(cache, q_out, batch, num_rows, cu_rows, kv_len, max_kv_len, max_rows_per_seq,
+                 views, softmax_scale, out, mass, mass_stride, aa, plan, empty_at);
+  if (st || empty_at == 1) return st;
+  if (!mass) return FDL_EINVAL;
+  if (workspace_bytes < kFusedSyncBytes + plan.bytes || !workspace) return FDL_EWORKSPACE;
+  if (empty_fc) {
+    // No rows to project: what remains is the attention call's (with the
+    // mass asked for, it writes zeros).
+    aa.ws = static_cast<char *>(workspace) + kFusedSyncBytes;
+    return hip_status(fdl::launch_attention(aa, plan, static_cast<hipStream_t>(stream)));
+  }
+  if (!fdl::fused_step_supported(fa, plan, true)) return FDL_EUNSUPPORTED;
+  aa.ws = static_cast<char *>(workspace) + kFusedSyncBytes;
+  return hip_status(fdl::launch_fused_step(fa, aa, plan, static_cast<int *>(workspace),
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int track_topb(const float *mass, int32_t mass_stride, const int32_t *kv_len, int32_t batch,

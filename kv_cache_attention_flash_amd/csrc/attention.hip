@@ -630,23 +630,34 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnArgs a, AttnPlan p
 // and normalisers, sums exp2(s - LSE) over its 16 rows for each of its keys.
 constexpr int kRowWaves = 8;
 
+// LDS of one row-group workgroup.
+template <int D>
+struct RowsLds {
+  uint16_t vbuf[kRowWaves][KT][kVPad<D>];
+  int s_page[kMaxPages];
+  float s_ml[kRowWaves][16][2];
+  float s_inv[16];
+};
+
+// The workgroup body: item bid of nb (LDS from the caller, so a fused kernel
+// can share one buffer across phases).
 template <int D, int MAXT, bool MASS>
-__global__ __launch_bounds__(512) void attn_rows_kernel(AttnArgs a, AttnPlan p) {
+__device__ __forceinline__ void attn_rows_body(const AttnArgs &a, const AttnPlan &p, int bid,
+                                               int nb, RowsLds<D> &L) {
   constexpr int KS = D / 32;            // MFMA k-steps per key row
   constexpr int CH = D / 8;             // 16-byte chunks per key row
   constexpr int VLD = KT * CH / 64;     // V chunks per lane per tile
   constexpr int NST = 2;                // tiles in flight per wave
   static_assert(kRowWaves * 16 * D * 4 <= kRowWaves * KT * kVPad<D> * 2, "merge scratch");
-  __shared__ uint16_t vbuf[kRowWaves][KT][kVPad<D>];
-  __shared__ int s_page[kMaxPages];
-  __shared__ float s_ml[kRowWaves][16][2];
-  __shared__ float s_inv[16];
+  auto &vbuf = L.vbuf;
+  auto &s_page = L.s_page;
+  auto &s_ml = L.s_ml;
+  auto &s_inv = L.s_inv;
 
   // Blocks are dealt to the 8 XCDs round-robin; map them so that the row
   // groups of one (sequence, head) run on one XCD and share its L2.
-  const int nb = gridDim.x;
-  int u = blockIdx.x;
-  if ((nb & 7) == 0) u = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
+  int u = bid;
+  if ((nb & 7) == 0) u = (bid & 7) * (nb >> 3) + (bid >> 3);
   const int rg = u % p.rgroups;
   u /= p.rgroups;
   const int h = u % a.c.H;
@@ -829,16 +840,25 @@ __global__ __launch_bounds__(512) void attn_rows_kernel(AttnArgs a, AttnPlan p) 
   }
 }
 
+template <int D, int MAXT, bool MASS>
+__global__ __launch_bounds__(512) void attn_rows_kernel(AttnArgs a, AttnPlan p) {
+  __shared__ RowsLds<D> lds;
+  attn_rows_body<D, MAXT, MASS>(a, p, blockIdx.x, gridDim.x, lds);
+}
+
 // Mass of the row-group path: mass[b][j] = sum over heads and row groups of the
 // partial sums, zero from kv_len to the stride.  A block covers 32 keys with
 // 8 lanes per key: lane group g adds partials g, g + 8, g + 16, ... in order,
 // then the 8 group sums are added in group order (a fixed order throughout).
-__global__ __launch_bounds__(256) void attn_rows_mass_kernel(AttnArgs a, AttnPlan p) {
-  __shared__ float part[8][32];
+// Body for 256 threads (tid = thread index in the 256, item bid).  With
+// valid false the body only takes part in the barrier (a fused caller runs
+// two items per 512-thread workgroup and one half may have none).
+__device__ __forceinline__ void attn_rows_mass_body(const AttnArgs &a, const AttnPlan &p, int bid,
+                                                    int tid, bool valid, float (*part)[32]) {
   const int per_b = (a.mass_stride + 31) / 32;
-  const int b = blockIdx.x / per_b;
-  const int k = threadIdx.x & 31, grp = threadIdx.x >> 5;
-  const int jj = (blockIdx.x % per_b) * 32 + k;
+  const int b = valid ? bid / per_b : 0;
+  const int k = tid & 31, grp = tid >> 5;
+  const int jj = valid ? (bid % per_b) * 32 + k : a.mass_stride;
   // Partial loads are issued with the length loads (every entry read lies in
   // the workspace; entries no workgroup wrote are selected away, not added).
   const int jc = min(jj, a.mass_stride - 1);
@@ -872,10 +892,18 @@ __global__ __launch_bounds__(256) void attn_rows_mass_kernel(AttnArgs a, AttnPla
   }
 }
 
+__global__ __launch_bounds__(256) void attn_rows_mass_kernel(AttnArgs a, AttnPlan p) {
+  __shared__ float part[8][32];
+  attn_rows_mass_body(a, p, blockIdx.x, threadIdx.x, true, part);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+// The externally visible launchers (left out of a unit that compiles this
+// file only for its device bodies: FDL_DEVICE_ONLY).
+#ifndef FDL_DEVICE_ONLY
 // Row-group path only when the split path cannot fill the GPU (few
 // sequences x heads) and the mass is asked for: there it saves the split
 // merge and the second pass over K, which at that size cost more than the
@@ -992,5 +1020,7 @@ hipError_t launch_attention(const AttnArgs &a, const AttnPlan &p, hipStream_t s)
   }
   return hipSuccess;
 }
+
+#endif  // FDL_DEVICE_ONLY
 
 }  // namespace fdl

@@ -138,8 +138,20 @@ struct SplitPlan {
   float *partials;  // [G][S][64][CW]
 };
 
+// LDS of one split-K workgroup.
+template <int NTW, int NGW, int KC>
+struct SplitLds {
+  static constexpr int CW = 16 * NTW * NGW, ROWS = 64, PIECES = KC / 8, TROWS = ROWS + CW;
+  u32x4 lds[2][TROWS * PIECES];
+  int s_blk[ROWS], s_off[ROWS], s_pos[ROWS];
+  double s_freq[64];
+};
+
+// The workgroup body (item bid of the grid; LDS from the caller, so a fused
+// kernel can share one buffer across phases).
 template <int NTW, int NGW, int NST, int NCH, int NW, int KC>
-__global__ __launch_bounds__(NW * 64) void qkv_splitk_kernel(FlashCacheArgs a, SplitPlan sp) {
+__device__ __forceinline__ void qkv_splitk_body(const FlashCacheArgs &a, const SplitPlan &sp,
+                                                int bid, SplitLds<NTW, NGW, KC> &L) {
   constexpr int NKQ = NW / NGW;
   constexpr int CW = 16 * NTW * NGW;
   constexpr int PW = CW / 2;
@@ -150,9 +162,11 @@ __global__ __launch_bounds__(NW * 64) void qkv_splitk_kernel(FlashCacheArgs a, S
   constexpr int LOADS = TROWS * PIECES / (NW * 64);
   static_assert(TROWS * PIECES % (NW * 64) == 0, "chunk must split evenly");
   static_assert(KSTEPS % NKQ == 0, "k-steps per chunk must split over the quarters");
-  __shared__ u32x4 lds[2][TROWS * PIECES];
-  __shared__ int s_blk[ROWS], s_off[ROWS], s_pos[ROWS];
-  __shared__ double s_freq[64];
+  auto &lds = L.lds;
+  auto &s_blk = L.s_blk;
+  auto &s_off = L.s_off;
+  auto &s_pos = L.s_pos;
+  auto &s_freq = L.s_freq;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.c.H, D = a.c.D, half = D >> 1;
@@ -163,8 +177,8 @@ __global__ __launch_bounds__(NW * 64) void qkv_splitk_kernel(FlashCacheArgs a, S
   // Block -> (group, split) so that the S splits of a group run on one XCD
   // (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
   const int nb = sp.G * sp.S;
-  int idx = blockIdx.x;
-  if (nb % 8 == 0) idx = (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8;
+  int idx = bid;
+  if (nb % 8 == 0) idx = (bid % 8) * (nb / 8) + bid / 8;
   const int grp = idx / sp.S, split = idx % sp.S;
   const int pair0 = grp * PW;
   const int k_begin = split * sp.ks;
@@ -323,6 +337,12 @@ __global__ __launch_bounds__(NW * 64) void qkv_splitk_kernel(FlashCacheArgs a, S
   }
 }
 
+template <int NTW, int NGW, int NST, int NCH, int NW, int KC>
+__global__ __launch_bounds__(NW * 64) void qkv_splitk_kernel(FlashCacheArgs a, SplitPlan sp) {
+  __shared__ SplitLds<NTW, NGW, KC> lds;
+  qkv_splitk_body<NTW, NGW, NST, NCH, NW, KC>(a, sp, blockIdx.x, lds);
+}
+
 // Adds the S split partials of qkv_splitk_kernel in split order and runs the
 // epilogue.  One thread per (row, rotary pair); consecutive threads read
 // consecutive partial columns.
@@ -366,9 +386,17 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(FlashCacheArgs a, Split
 // (clamped past the end) so the compiler waits for exactly one stage.
 // Workgroups of one feature tile are dealt to one XCD so the weight tile is
 // shared through its L2.
+// LDS of one tiled-projection workgroup.
+template <int BM, int NWN>
+struct GemmLds {
+  static constexpr int TR = BM + 64 * NWN, PIECES = 4;
+  u32x4 lds[2][TR * PIECES];
+  int s_blk[BM], s_off[BM], s_pos[BM];
+};
+
 template <int BM, int NWN, int NREG>
-__global__ __launch_bounds__(128 * NWN) void qkv_gemm_kernel(FlashCacheArgs a, int nrow_tiles,
-                                                              int ncol_tiles) {
+__device__ __forceinline__ void qkv_gemm_body(const FlashCacheArgs &a, int nrow_tiles,
+                                              int ncol_tiles, int bid, GemmLds<BM, NWN> &L) {
   constexpr int NT = 128 * NWN;                        // threads
   constexpr int BP = 32 * NWN;                         // pairs per tile
   constexpr int BN = 2 * BP;                           // output features per tile
@@ -377,16 +405,18 @@ __global__ __launch_bounds__(128 * NWN) void qkv_gemm_kernel(FlashCacheArgs a, i
   constexpr int TR = BM + BN;                          // staged rows per step
   constexpr int LD = TR * PIECES / NT;                 // 16-byte loads per thread per step
   static_assert(TR * PIECES % NT == 0, "step must split evenly over the threads");
-  __shared__ u32x4 lds[2][TR * PIECES];
-  __shared__ int s_blk[BM], s_off[BM], s_pos[BM];
+  auto &lds = L.lds;
+  auto &s_blk = L.s_blk;
+  auto &s_off = L.s_off;
+  auto &s_pos = L.s_pos;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.c.H, D = a.c.D, half = D >> 1;
   const int total_pairs = 3 * H * half;
   const int hidden = a.hidden;
   const int nb = nrow_tiles * ncol_tiles;
-  int idx = blockIdx.x;
-  if (nb % 8 == 0) idx = (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8;
+  int idx = bid;
+  if (nb % 8 == 0) idx = (bid % 8) * (nb / 8) + bid / 8;
   const int ct = idx / nrow_tiles, rtile = idx % nrow_tiles;
   const int row0 = rtile * BM, pair0 = ct * BP;
 
@@ -501,6 +531,13 @@ __global__ __launch_bounds__(128 * NWN) void qkv_gemm_kernel(FlashCacheArgs a, i
 
 
 
+template <int BM, int NWN, int NREG>
+__global__ __launch_bounds__(128 * NWN) void qkv_gemm_kernel(FlashCacheArgs a, int nrow_tiles,
+                                                              int ncol_tiles) {
+  __shared__ GemmLds<BM, NWN> lds;
+  qkv_gemm_body<BM, NWN, NREG>(a, nrow_tiles, ncol_tiles, blockIdx.x, lds);
+}
+
 // Unfused ablation, stage 2: rotary embedding and bf16 rounding from the fp32
 // projection in HBM; Q to its buffer, K and V rows to staging buffers
 // [rows][H][D].  One thread per (row, rotary pair).
@@ -586,6 +623,9 @@ FcPlan plan_fc(int rows, int hidden, int H, int D) {
 }
 }  // namespace
 
+// The externally visible launchers; a unit that compiles this file only for
+// its device bodies (the fused step) defines FDL_DEVICE_ONLY and leaves them out.
+#ifndef FDL_DEVICE_ONLY
 size_t flash_cache_workspace_bytes(int rows, int hidden, int H, int D) {
   return plan_fc(rows, hidden, H, D).bytes;
 }
@@ -674,6 +714,8 @@ hipError_t launch_flash_cache_unfused(const FlashCacheArgs &a, void *ws, size_t 
                      ks, vs);
   return hipGetLastError();
 }
+
+#endif  // FDL_DEVICE_ONLY
 
 }  // namespace fdl
 
