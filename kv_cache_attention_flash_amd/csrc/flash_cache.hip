@@ -59,13 +59,11 @@ __device__ __forceinline__ void rope_cs(int pos, double turns_per_pos, float &c,
   c = __builtin_amdgcn_cosf((float)t);
 }
 
-// Rotation of one pair (Q and K sections) and bf16 rounding; one helper for
-// the fused epilogue and the unfused rotary kernel, so both round identically.
-__device__ __forceinline__ uint32_t rotate_round(float lo, float hi, int sec, int pos,
-                                                 double turns_per_pos) {
-  if (sec < 2) {
-    float c, s;
-    rope_cs(pos, turns_per_pos, c, s);
+// Rotation of one pair by the angle with cosine c and sine s (Q and K
+// sections only) and bf16 rounding.
+__device__ __forceinline__ uint32_t rotate_round_cs(float lo, float hi, bool rotate, float c,
+                                                    float s) {
+  if (rotate) {
     const float rlo = __builtin_fmaf(lo, c, -(hi * s));
     const float rhi = __builtin_fmaf(hi, c, lo * s);
     lo = rlo;
@@ -74,32 +72,56 @@ __device__ __forceinline__ uint32_t rotate_round(float lo, float hi, int sec, in
   return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
 }
 
-// Rotate (Q and K parts), round and store one rotary pair of one row; with
-// y_out set, store the raw fp32 pair instead (the unfused ablation).
-__device__ __forceinline__ void store_pair(const FlashCacheArgs &a, int r, int p, float lo,
-                                           float hi, int blk, int off, int pos,
-                                           double inv_freq_i) {
+// The same with the angle formed here; one helper for every epilogue and the
+// unfused rotary kernel, so all of them round identically.
+__device__ __forceinline__ uint32_t rotate_round(float lo, float hi, int sec, int pos,
+                                                 double turns_per_pos) {
+  float c = 1.f, s = 0.f;
+  if (sec < 2) rope_cs(pos, turns_per_pos, c, s);
+  return rotate_round_cs(lo, hi, sec < 2, c, s);
+}
+
+// The raw fp32 pair of row r, rotary pair p (the unfused ablation's output).
+__device__ __forceinline__ void store_raw_pair(const FlashCacheArgs &a, int r, int p, float lo,
+                                               float hi) {
+  const int H = a.c.H, D = a.c.D, half = D >> 1;
+  float *y = a.y_out + (size_t)r * 3 * H * D + (size_t)(p / half) * D + p % half;
+  y[0] = lo;
+  y[half] = hi;
+}
+
+// Where element i of rotary pair p (i, i + D/2) of row r goes: Q to its
+// buffer, K and V into the cache (physical block blk, offset off).
+__device__ __forceinline__ uint16_t *pair_dst(const FlashCacheArgs &a, int r, int p, int blk,
+                                              int off) {
   const int H = a.c.H, D = a.c.D, half = D >> 1;
   const int sh = p / half;  // section * H + head
   const int i = p % half;
   const int sec = sh / H;
   const int h = sh % H;
+  if (sec == 0) return a.q_out + ((size_t)r * H + h) * D + i;
+  uint16_t *pool = sec == 1 ? a.c.k : a.c.v;
+  return pool + (((size_t)blk * H + h) * a.c.bs + off) * D + i;
+}
+
+// Stores the rounded pair word v (low half: element i, high half: i + D/2).
+__device__ __forceinline__ void store_word(uint16_t *dst, int half, uint32_t v) {
+  dst[0] = (uint16_t)(v & 0xffffu);
+  dst[half] = (uint16_t)(v >> 16);
+}
+
+// Rotate (Q and K parts), round and store one rotary pair of one row; with
+// y_out set, store the raw fp32 pair instead (the unfused ablation).
+__device__ __forceinline__ void store_pair(const FlashCacheArgs &a, int r, int p, float lo,
+                                           float hi, int blk, int off, int pos,
+                                           double inv_freq_i) {
   if (a.y_out) {
-    float *y = a.y_out + (size_t)r * 3 * H * D + (size_t)sh * D + i;
-    y[0] = lo;
-    y[half] = hi;
+    store_raw_pair(a, r, p, lo, hi);
     return;
   }
-  const uint32_t v = rotate_round(lo, hi, sec, pos, inv_freq_i);
-  uint16_t *dst;
-  if (sec == 0) {
-    dst = a.q_out + ((size_t)r * H + h) * D;
-  } else {
-    uint16_t *pool = sec == 1 ? a.c.k : a.c.v;
-    dst = pool + (((size_t)blk * H + h) * a.c.bs + off) * D;
-  }
-  dst[i] = (uint16_t)(v & 0xffffu);
-  dst[i + half] = (uint16_t)(v >> 16);
+  const int sec = p / (a.c.D >> 1) / a.c.H;
+  store_word(pair_dst(a, r, p, blk, off), a.c.D >> 1,
+             rotate_round(lo, hi, sec, pos, inv_freq_i));
 }
 
 // Row metadata (physical block, offset, position) of row r; also writes the
@@ -172,7 +194,6 @@ __device__ __forceinline__ void qkv_splitk_body(const FlashCacheArgs &a, const S
   const int H = a.c.H, D = a.c.D, half = D >> 1;
   const int total_pairs = 3 * H * half;
   const int hidden = a.hidden;
-  if (sp.S == 1 && tid < half) s_freq[tid] = rope_inv_freq(tid, D, a.log2_base);
 
   // Block -> (group, split) so that the S splits of a group run on one XCD
   // (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
@@ -182,6 +203,38 @@ __device__ __forceinline__ void qkv_splitk_body(const FlashCacheArgs &a, const S
   const int grp = idx / sp.S, split = idx % sp.S;
   const int pair0 = grp * PW;
   const int k_begin = split * sp.ks;
+
+  // Row metadata for the epilogue (S == 1), in three steps.  Every wave
+  // computes it for row `lane` (identical values; wave 0 parks them in LDS),
+  // so no step sits in a branch.  Step 0 (slot, position, sequence) is issued
+  // before the first chunk loads and is complete once chunk 0 is; step 1 (the
+  // block-table entry) goes out behind chunk 2's loads; step 2 uses it one
+  // chunk later.  A wait on a load is a wait on
+  // every load issued before it, so no step waits ahead of the chunk loads it
+  // would hold back.
+  const bool epi = sp.S == 1;
+  const int mrow = max(0, min(lane, a.rows - 1));
+  int act = 0, m_end = 0, m_seq = 0, m_slot = 0, m_pos = 0, m_blk = 0;
+  auto meta = [&](int step) {
+    if (step == 0) {  // unconditional: a value merged from two paths would be waited for here
+      m_end = a.cu_rows[a.batch];  // used in step 1 (a use here would wait for it)
+      m_slot = a.slots[mrow];
+      m_pos = a.positions[mrow];
+      m_seq = row_to_seq(a.cu_rows, a.batch, mrow);
+    } else if (!epi) {
+      return;
+    } else if (step == 1) {
+      act = max(0, min(a.rows, m_end));  // the active-row count
+      // rows past the active count may hold anything: they read entry 0
+      const size_t e = lane < act ? (size_t)m_seq * a.c.max_blocks + m_slot / a.c.bs : 0;
+      m_blk = a.c.block_table[e];
+    } else if (wave == 0 && lane < act) {
+      s_blk[lane] = m_blk;
+      s_off[lane] = m_slot % a.c.bs;
+      s_pos[lane] = m_pos;
+    }
+  };
+  meta(0);
 
   // Global rows this thread stages: row t/16 + 32*i of the chunk tile, piece t%16.
   const int piece = tid % PIECES;
@@ -199,18 +252,10 @@ __device__ __forceinline__ void qkv_splitk_body(const FlashCacheArgs &a, const S
       const int c = tr - ROWS;  // column in the group: tile c/16, lane col c%16
       int p = pair0 + 8 * (c / 16) + (c & 7);
       p = p < total_pairs ? p : total_pairs - 1;
-      const int feat = (p / half) * D + (p % half) + ((c & 8) ? half : 0);
+      const int lh = D == 128 ? 6 : 5;  // log2(D / 2): D is 64 or 128
+      const int feat = (p >> lh) * D + (p & (half - 1)) + ((c & 8) ? half : 0);
       src[i] = a.w + (size_t)feat * hidden + k_begin + piece * 8;
     }
-  }
-
-  const int act = active_rows(a);
-  if (sp.S == 1 && tid < ROWS && tid < act) {
-    int blk, off, pos;
-    row_meta(a, tid, idx == 0, blk, off, pos);
-    s_blk[tid] = blk;
-    s_off[tid] = off;
-    s_pos[tid] = pos;
   }
 
   const int g = lane >> 4, j = lane & 15;
@@ -257,12 +302,35 @@ __device__ __forceinline__ void qkv_splitk_body(const FlashCacheArgs &a, const S
     for (int i = 0; i < LOADS; ++i) buf[dst_slot[i]] = reg[i];
   };
 
+  // This thread's epilogue items (rows and pairs are fixed per thread): their
+  // rotation angles, destinations and flags (bit k: item k is stored; bit
+  // NIT + k: it is rotated), formed while chunks are still streaming in, so
+  // the tail after the last chunk only adds, rotates and stores.  Items the
+  // epilogue skips get an unused angle and destination.
+  constexpr int NIT = ROWS * PW / (NW * 64);
+  static_assert(ROWS * PW % (NW * 64) == 0, "epilogue items must split evenly");
+  float ec[NIT], es[NIT];
+  uint16_t *edst[NIT];
+  unsigned eflags = 0;
+  auto angles = [&]() {
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+      const int item = tid + NW * 64 * k;
+      const int rl = max(0, min(item / PW, act - 1)), p = pair0 + item % PW;
+      rope_cs(s_pos[rl], s_freq[p % half], ec[k], es[k]);
+      edst[k] = pair_dst(a, rl, min(p, total_pairs - 1), s_blk[rl], s_off[rl]);
+      if (item / PW < act && p < total_pairs) eflags |= 1u << k;
+      if (p / half < 2 * H) eflags |= 1u << (NIT + k);
+    }
+  };
+
   // NST register stages and two LDS buffers: while chunk c is multiplied out
   // of one LDS buffer, chunk c + 1 moves from registers into the other and
   // chunks c + 2 .. c + NST are in flight from HBM.  With a compile-time chunk
   // count (NCH > 0) the loop is fully unrolled, so the compiler knows exactly
   // which loads each LDS store waits for; scheduling barriers keep the load
   // groups in issue order.  Loads past the last chunk re-read it (clamped).
+  static_assert(NCH == 0 || NCH >= 4, "the metadata steps need four chunks");
   const int nchunks = NCH > 0 ? NCH : sp.ks / KC;
   u32x4 r[NST][LOADS];
 #pragma unroll
@@ -270,8 +338,11 @@ __device__ __forceinline__ void qkv_splitk_body(const FlashCacheArgs &a, const S
     load(r[t], min(t, nchunks - 1));
     __builtin_amdgcn_sched_barrier(0);
   }
+  if (epi && tid < half) s_freq[tid] = rope_inv_freq(tid, D, a.log2_base);
   store(lds[0], r[0]);
   load(r[0], min(NST, nchunks - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  meta(1);
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
   if constexpr (NCH > 0) {
@@ -281,6 +352,9 @@ __device__ __forceinline__ void qkv_splitk_body(const FlashCacheArgs &a, const S
       if (c + 1 < NCH) {
         store(lds[(c + 1) & 1], r[(c + 1) % NST]);
         if (c + 1 + NST < NCH) load(r[(c + 1) % NST], c + 1 + NST);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c == 1) meta(2);
+        if (c == 2 && epi) angles();
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
       }
@@ -297,43 +371,55 @@ __device__ __forceinline__ void qkv_splitk_body(const FlashCacheArgs &a, const S
         __syncthreads();
       }
     }
+    meta(2);
   }
   __syncthreads();
+  if (NCH == 0 && epi) angles();
 
-  // Reduce the NKQ reduction quarters into Y[64][CW] (fp32, reusing the LDS).
+  // Every wave parks its reduction share's partial tile Y_q[64][CW] (fp32,
+  // reusing the LDS); the shares are then added in the fixed order
+  // q = NKQ-1 .. 0, whichever wave finished first.
   float *Y = reinterpret_cast<float *>(&lds[0][0]);
-  constexpr int YS = CW + 4;  // padded row stride
-  static_assert(ROWS * YS * 4 <= (int)sizeof(lds), "LDS reuse");
-  for (int q = NKQ - 1; q >= 0; --q) {
-    if (kq == q) {
+  constexpr int YS = CW + 4;       // padded row stride
+  constexpr int YQ = ROWS * YS;    // floats per share
+  static_assert(NKQ * YQ * 4 <= (int)sizeof(lds), "LDS reuse");
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int t = 0; t < NTW; ++t)
+    for (int t = 0; t < NTW; ++t)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float *y = &Y[(16 * mt + 4 * g + e) * YS + 16 * (ng * NTW + t) + j];
-            *y = (q == NKQ - 1) ? acc[mt][t][e] : acc[mt][t][e] + *y;
-          }
-    }
-    __syncthreads();
-  }
+      for (int e = 0; e < 4; ++e)
+        Y[kq * YQ + (16 * mt + 4 * g + e) * YS + 16 * (ng * NTW + t) + j] = acc[mt][t][e];
+  __syncthreads();
+  auto ysum = [&](int at) {
+    float v = Y[(NKQ - 1) * YQ + at];
+#pragma unroll
+    for (int q = NKQ - 2; q >= 0; --q) v = Y[q * YQ + at] + v;
+    return v;
+  };
 
-  if (sp.S > 1) {
+  if (!epi) {
     float *part = sp.partials + ((size_t)grp * sp.S + split) * ROWS * CW;
     for (int e = tid; e < ROWS * CW / 4; e += NW * 64) {
-      const int row = (4 * e) / CW, col = (4 * e) % CW;
-      *reinterpret_cast<f32x4 *>(part + 4 * e) = *reinterpret_cast<const f32x4 *>(&Y[row * YS + col]);
+      const int row = (4 * e) / CW, col = (4 * e) % CW, at = row * YS + col;
+      *reinterpret_cast<f32x4 *>(part + 4 * e) =
+          f32x4{ysum(at), ysum(at + 1), ysum(at + 2), ysum(at + 3)};
     }
     return;
   }
-  for (int item = tid; item < ROWS * PW; item += NW * 64) {
+  if (idx == 0 && wave == 0 && lane < act && a.slot_mapping)
+    a.slot_mapping[lane] = (int64_t)m_blk * a.c.bs + m_slot % a.c.bs;
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) {
+    const int item = tid + NW * 64 * k;
     const int rl = item / PW, pl = item % PW;
-    const int p = pair0 + pl;
-    if (rl >= act || p >= total_pairs) continue;
+    if (!(eflags >> k & 1u)) continue;
     const int clo = 16 * (pl >> 3) + (pl & 7);
-    store_pair(a, rl, p, Y[rl * YS + clo], Y[rl * YS + clo + 8], s_blk[rl], s_off[rl], s_pos[rl],
-               s_freq[p % half]);
+    const float lo = ysum(rl * YS + clo), hi = ysum(rl * YS + clo + 8);
+    if (a.y_out)
+      store_raw_pair(a, rl, pair0 + pl, lo, hi);
+    else
+      store_word(edst[k], half, rotate_round_cs(lo, hi, eflags >> (NIT + k) & 1u, ec[k], es[k]));
   }
 }
 
