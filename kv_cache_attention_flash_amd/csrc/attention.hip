@@ -751,10 +751,12 @@ __device__ __forceinline__ void attn_rows_body(const AttnArgs &a, const AttnPlan
 #pragma unroll
     for (int i = 0; i < NST; ++i) issue(st[i], i);
     if constexpr (MASS) {
+      // No wave has more than MAXT tiles: loads for tiles past it would only
+      // be waited for (before their registers are reused) at the merge.
 #pragma unroll
       for (int kk = 0; kk < MAXT; ++kk) {
         if (kk < n_w) process(st[kk % NST], kk, sc[kk]);
-        issue(st[kk % NST], kk + NST);
+        if (kk + NST < MAXT) issue(st[kk % NST], kk + NST);
       }
     } else {
       for (int kk0 = 0; kk0 < n_w; kk0 += NST) {
@@ -774,14 +776,20 @@ __device__ __forceinline__ void attn_rows_body(const AttnArgs &a, const AttnPlan
     s_ml[w][j][1] = l;
   }
   lds_barrier();
+  float mws[kRowWaves], lws[kRowWaves];  // read once, then combined without branches
+#pragma unroll
+  for (int ww = 0; ww < kRowWaves; ++ww) {
+    mws[ww] = s_ml[ww][j][0];
+    lws[ww] = s_ml[ww][j][1];
+  }
   float mx = kNegInf;
 #pragma unroll
-  for (int ww = 0; ww < kRowWaves; ++ww) mx = fmaxf(mx, s_ml[ww][j][0]);
+  for (int ww = 0; ww < kRowWaves; ++ww) mx = fmaxf(mx, mws[ww]);
   float lsum = 0.f;
 #pragma unroll
   for (int ww = 0; ww < kRowWaves; ++ww) {
-    const float mw = s_ml[ww][j][0];
-    lsum += mw == kNegInf ? 0.f : s_ml[ww][j][1] * exp2f(mw - mx);
+    const float e = exp2f(mws[ww] - mx);
+    lsum += mws[ww] == kNegInf ? 0.f : lws[ww] * e;
   }
   const float fself = m == kNegInf ? 0.f : exp2f(m - mx);
   const float lse = lsum > 0.f ? mx + log2f(lsum) : kNegInf;

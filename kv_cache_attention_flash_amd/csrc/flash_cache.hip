@@ -472,6 +472,11 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(FlashCacheArgs a, Split
 // (clamped past the end) so the compiler waits for exactly one stage.
 // Workgroups of one feature tile are dealt to one XCD so the weight tile is
 // shared through its L2.
+// 16-byte slot swizzle of a staged row (four slots per row): a 16-byte LDS
+// access is served 16 lanes at a time, and 16 consecutive rows then cover all
+// 16 slots of the 64 banks (no bank conflicts; checked with the LDS counters).
+__device__ __forceinline__ int gemm_swz(int row) { return (row >> 2) & 3; }
+
 // LDS of one tiled-projection workgroup.
 template <int BM, int NWN>
 struct GemmLds {
@@ -535,7 +540,7 @@ __device__ __forceinline__ void qkv_gemm_body(const FlashCacheArgs &a, int nrow_
       const int feat = (p / half) * D + (p % half) + (c >= BP ? half : 0);
       src[i] = a.w + (size_t)feat * hidden + piece * 8;
     }
-    slot[i] = tr * PIECES + (piece ^ ((tr >> 2) & 3));
+    slot[i] = tr * PIECES + (piece ^ gemm_swz(tr));
   }
   const int nk = hidden / BK;
   u32x4 rg[NREG][LD];
@@ -582,12 +587,12 @@ __device__ __forceinline__ void qkv_gemm_body(const FlashCacheArgs &a, int nrow_
 #pragma unroll
           for (int mt = 0; mt < MTW; ++mt) {
             const int row = wm * (BM / 2) + 32 * mt + l32;
-            af[mt] = buf[row * PIECES + (pc ^ ((row >> 2) & 3))];
+            af[mt] = buf[row * PIECES + (pc ^ gemm_swz(row))];
           }
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             const int row = BM + BP * c + 32 * wn + l32;
-            bfr[c] = buf[row * PIECES + (pc ^ ((row >> 2) & 3))];
+            bfr[c] = buf[row * PIECES + (pc ^ gemm_swz(row))];
           }
 #pragma unroll
           for (int mt = 0; mt < MTW; ++mt)
@@ -758,10 +763,16 @@ hipError_t launch_flash_cache(const FlashCacheArgs &a, void *ws, size_t ws_bytes
   // More than 64 rows (or a hidden size the chunking does not divide): the
   // tiled MFMA kernel, 128 rows x 128 rotary pairs per workgroup.
   const int total_pairs = 3 * a.c.H * (a.c.D / 2);
-  constexpr int BM = 128, NWN = 4, BP = 32 * NWN;
+#ifndef FDL_FC_GBM
+#define FDL_FC_GBM 128
+#endif
+#ifndef FDL_FC_GNREG
+#define FDL_FC_GNREG 2
+#endif
+  constexpr int BM = FDL_FC_GBM, NWN = 4, BP = 32 * NWN;
   const int nrow = (a.rows + BM - 1) / BM, ncol = (total_pairs + BP - 1) / BP;
-  hipLaunchKernelGGL((qkv_gemm_kernel<BM, NWN, 2>), dim3(nrow * ncol), dim3(128 * NWN), 0, s, a,
-                     nrow, ncol);
+  hipLaunchKernelGGL((qkv_gemm_kernel<BM, NWN, FDL_FC_GNREG>), dim3(nrow * ncol), dim3(128 * NWN),
+                     0, s, a, nrow, ncol);
   return hipGetLastError();
 }
 

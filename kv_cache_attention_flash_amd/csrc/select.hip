@@ -13,122 +13,116 @@ namespace fdl {
 
 namespace {
 
-// Exclusive prefix count of `flag` over the block (in thread order) and the
-// block total; NW waves.
-template <int NW>
-__device__ __forceinline__ int block_excl_count(bool flag, int &total, int *sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const unsigned long long bal = __ballot(flag);
-  const int in_wave = __popcll(bal & ((1ull << lane) - 1ull));
-  if (lane == 0) sh[wave] = __popcll(bal);
-  __syncthreads();
-  int before = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int c = sh[w];
-    before += w < wave ? c : 0;
-    total += c;
-  }
-  __syncthreads();
-  return before + in_wave;
-}
-
-// Inclusive prefix sum over the block's threads (thread order); NW waves.
-template <int NW>
-__device__ __forceinline__ unsigned block_incl_sum(unsigned v, unsigned *sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const unsigned u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
-  if (lane == 63) sh[wave] = v;
-  __syncthreads();
-  unsigned before = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) before += w < wave ? sh[w] : 0u;
-  __syncthreads();
-  return v + before;
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (ALU
+// latency, no LDS round trips): shifts by 1, 2, 4, 8 inside each row of 16
+// lanes, then row 0's total into row 1 and row 2's into row 3 (broadcast of
+// lane 15), then lane 31's running total into rows 2 and 3.
+__device__ __forceinline__ unsigned wave_incl_scan(unsigned v) {
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
 }
 
 // One workgroup of NT threads per sequence (1024 for long rows, so a few
 // sequences still keep many waves busy).  Masses are non-negative, so their
 // fp32 bit patterns order like the values: a 4-pass radix select over 8-bit
-// digits (LDS histogram, then a parallel scan from the top digit down over
-// the first 256 threads) finds the bit pattern T of the B-th largest mass;
-// every key above T is taken, and keys equal to T are taken in index order
-// until B are chosen.  A final in-order scan writes the chosen indices
-// ascending.  Rows of up to kCached keys (by stride) are held in LDS across
-// the passes.
+// digits finds the bit pattern T of the B-th largest mass; every key above T
+// is taken, and keys equal to T are taken in index order until B are chosen.
+// Each pass costs one barrier: the four LDS histograms are zeroed up front,
+// and after a pass every wave reads the whole histogram (four bins a lane,
+// from the top digit down) and finds the digit with a DPP wave scan of its
+// own.  Wave 0 then writes the chosen indices in ascending order, 64 keys at
+// a time, placing them with ballots.  Rows of up to kCached keys (by stride)
+// are held in LDS across the passes.
 constexpr int kCached = 8192;
 
 template <int NT>
 __global__ __launch_bounds__(NT) void topb_kernel(const float *mass, int stride,
                                                   const int32_t *kv_len, int topb,
                                                   int32_t *out) {
-  constexpr int NW = NT / 64;
-  static_assert(NT >= 256, "the digit scan needs one thread per bin");
-  __shared__ unsigned hist[256];
-  __shared__ unsigned s_digit, s_remaining;
-  __shared__ unsigned shs[NW];
-  __shared__ int sh[NW];
+  static_assert(NT >= 256 && NT % 64 == 0, "whole waves, 256+ threads");
+  __shared__ unsigned hist[4][256];
   __shared__ uint32_t cache[kCached];
   const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const uint32_t *mb = reinterpret_cast<const uint32_t *>(mass + (size_t)b * stride);
   // The row's loads go out with the length's (the stride bounds them).
   const bool cached = stride <= kCached;
   if (cached)
-    for (int k = threadIdx.x; k < stride; k += NT) cache[k] = mb[k];
+    for (int k = tid; k < stride; k += NT) cache[k] = mb[k];
+  for (int i = tid; i < 4 * 256; i += NT) (&hist[0][0])[i] = 0u;
   const int L = min(kv_len[b], stride);  // a length past the row stride is clamped
   int32_t *ob = out + (size_t)b * topb;
 
   if (L <= topb) {
-    for (int k = threadIdx.x; k < topb; k += NT) ob[k] = k < L ? k : -1;
+    for (int k = tid; k < topb; k += NT) ob[k] = k < L ? k : -1;
     return;
   }
   auto key = [&](int k) -> uint32_t { return cached ? cache[k] : mb[k]; };
+  __syncthreads();
 
   uint32_t prefix = 0, pmask = 0;
-  unsigned remaining = (unsigned)topb;
+  unsigned remaining = (unsigned)topb;  // keys still to take below the digits fixed so far
+#pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    if (threadIdx.x < 256) hist[threadIdx.x] = 0;
-    __syncthreads();
-    for (int k = threadIdx.x; k < L; k += NT) {
+    for (int k = tid; k < L; k += NT) {
       const uint32_t u = key(k);
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+      if ((u & pmask) == prefix) atomicAdd(&hist[pass][(u >> shift) & 255u], 1u);
     }
     __syncthreads();
-    // Thread t < 256 looks at digit 255 - t; cum = candidates with digit >= it.
-    const unsigned c = threadIdx.x < 256 ? hist[255 - threadIdx.x] : 0u;
-    const unsigned cum = block_incl_sum<NW>(c, shs);
-    if (c > 0 && cum >= remaining && cum - c < remaining) {
-      s_digit = 255u - threadIdx.x;
-      s_remaining = remaining - (cum - c);
+    // Lane l holds digits 255-4l .. 252-4l; `incl` counts candidates with a
+    // digit at or above its lowest one.  The digit holding the remaining-th
+    // largest candidate lies in the one lane where the count crosses.
+    unsigned c[4], lsum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[i] = hist[pass][255 - 4 * lane - i];
+      lsum += c[i];
     }
-    __syncthreads();
-    prefix |= s_digit << shift;
+    const unsigned incl = wave_incl_scan(lsum);
+    const unsigned excl = incl - lsum;
+    const int src = __ffsll((long long)__ballot(excl < remaining && incl >= remaining)) - 1;
+    unsigned digit = 0, rem = 0, cum = excl;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!found && cum + c[i] >= remaining) {
+        digit = 255u - 4u * lane - i;
+        rem = remaining - cum;
+        found = true;
+      }
+      cum += c[i];
+    }
+    digit = (unsigned)__builtin_amdgcn_readlane((int)digit, src);
+    rem = (unsigned)__builtin_amdgcn_readlane((int)rem, src);
+    prefix |= digit << shift;
     pmask |= 255u << shift;
-    remaining = s_remaining;
-    __syncthreads();
+    remaining = rem;
   }
   const uint32_t T = prefix;
-  // `remaining` keys equal to T are needed (after all keys above T).
-  int base_sel = 0, base_eq = 0;
-  for (int c0 = 0; c0 < L; c0 += NT) {
-    const int k = c0 + threadIdx.x;
+
+  // `remaining` keys equal to T are taken (lowest indices first) after every
+  // key above T; wave 0 places them, 64 keys at a time.
+  if (tid >= 64) return;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  unsigned eq_seen = 0;
+  int sel_seen = 0;
+  for (int c0 = 0; c0 < L && sel_seen < topb; c0 += 64) {
+    const int k = c0 + lane;
     const uint32_t u = k < L ? key(k) : 0u;
-    const bool gt = k < L && u > T;
     const bool eq = k < L && u == T;
-    int eq_total, sel_total;
-    const int eq_rank = base_eq + block_excl_count<NW>(eq, eq_total, sh);
-    const bool sel = gt || (eq && eq_rank < (int)remaining);
-    const int pos = base_sel + block_excl_count<NW>(sel, sel_total, sh);
+    const unsigned long long beq = __ballot(eq);
+    const bool sel = (k < L && u > T) || (eq && eq_seen + __popcll(beq & below) < remaining);
+    const unsigned long long bsel = __ballot(sel);
+    const int pos = sel_seen + __popcll(bsel & below);
     if (sel && pos < topb) ob[pos] = k;
-    base_eq += eq_total;
-    base_sel += sel_total;
-    if (base_sel >= topb) break;
+    eq_seen += __popcll(beq);
+    sel_seen += __popcll(bsel);
   }
 }
 
