@@ -156,6 +156,38 @@ def test_topb_crafted_masses():
                 assert np.array_equal(got[i], want), (width, b_, i)
 
 
+def test_topb_uncached_rows_and_low_digits():
+    """Rows longer than the LDS-cached 8192 keys (read from HBM in every pass),
+    keys that differ only in their lowest byte (decided by the fourth digit
+    pass), and threshold ties spread over many 64-key output chunks."""
+    fd = _fd()
+    dev = "cuda:0"
+    rng = np.random.default_rng(11)
+    width = 9000
+    low = (np.uint32(0x3F800000) + rng.integers(0, 256, width).astype(np.uint32)).view(np.float32)
+    ties = np.full(width, 0.25, np.float32)
+    ties[rng.choice(width, 300, replace=False)] = 2.0   # 300 keys at the threshold value
+    ties[rng.choice(width, 10, replace=False)] = 3.0    # ten above it
+    flat = np.ones(width, np.float32)                    # every key ties
+    rows = [rng.random(width, dtype=np.float32), low, ties, flat]
+    lens = [width, 8999, width, 8193]
+    mass = torch.from_numpy(np.ascontiguousarray(np.stack(rows))).to(dev)
+    kv = G.i32(lens, dev)
+    for b_ in (1, 32, 64, 150):
+        got = fd.track_topb(mass, kv, b_).cpu().numpy()
+        for i, L in enumerate(lens):
+            want = O.top_b(rows[i].astype(np.float64), L, b_)
+            assert np.array_equal(got[i], want), (b_, i)
+    # the same rows cut to 2048 keys (the 256-thread workgroup, LDS-cached)
+    mass2 = torch.from_numpy(np.ascontiguousarray(np.stack(rows)[:, :2048])).to(dev)
+    kv2 = G.i32([2048, 2047, 2048, 1500], dev)
+    for b_ in (32, 150):
+        got = fd.track_topb(mass2, kv2, b_).cpu().numpy()
+        for i, L in enumerate([2048, 2047, 2048, 1500]):
+            want = O.top_b(rows[i][:2048].astype(np.float64), L, b_)
+            assert np.array_equal(got[i], want), ("cached", b_, i)
+
+
 def test_verify_long_window():
     """Windows longer than one wavefront; crafted prefixes."""
     fd = _fd()
