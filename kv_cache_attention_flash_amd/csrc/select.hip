@@ -35,17 +35,20 @@ __device__ __forceinline__ unsigned wave_incl_scan(unsigned v) {
 // Each pass costs one barrier: the four LDS histograms are zeroed up front,
 // and after a pass every wave reads the whole histogram (four bins a lane,
 // from the top digit down) and finds the digit with a DPP wave scan of its
-// own.  Wave 0 then writes the chosen indices in ascending order, 64 keys at
-// a time, placing them with ballots.  Rows of up to kCached keys (by stride)
-// are held in LDS across the passes.
+// own.  The chosen indices are written in ascending order: each wave counts
+// its segment's keys, one barrier shares the counts, and each wave places its
+// segment's keys 64 at a time with ballots.  Rows of up to kCached keys (by
+// stride) are held in LDS across the passes.
 constexpr int kCached = 8192;
 
 template <int NT>
 __global__ __launch_bounds__(NT) void topb_kernel(const float *mass, int stride,
                                                   const int32_t *kv_len, int topb,
                                                   int32_t *out) {
+  constexpr int NW = NT / 64;
   static_assert(NT >= 256 && NT % 64 == 0, "whole waves, 256+ threads");
   __shared__ unsigned hist[4][256];
+  __shared__ unsigned seg_eq[NW], seg_gt[NW];
   __shared__ uint32_t cache[kCached];
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -107,17 +110,37 @@ __global__ __launch_bounds__(NT) void topb_kernel(const float *mass, int stride,
   const uint32_t T = prefix;
 
   // `remaining` keys equal to T are taken (lowest indices first) after every
-  // key above T; wave 0 places them, 64 keys at a time.
-  if (tid >= 64) return;
-  const unsigned long long below = (1ull << lane) - 1ull;
-  unsigned eq_seen = 0;
-  int sel_seen = 0;
-  for (int c0 = 0; c0 < L && sel_seen < topb; c0 += 64) {
+  // key above T.  Wave w owns a contiguous segment of keys: it counts its
+  // keys above and equal to T, the counts of the waves before it give its
+  // first output position, and it places its chosen keys 64 at a time.
+  const int w = tid >> 6;
+  const int seg = (L + NW * 64 - 1) / (NW * 64) * 64;
+  const int s0 = min(w * seg, L), s1 = min(s0 + seg, L);
+  unsigned weq = 0, wgt = 0;
+  for (int c0 = s0; c0 < s1; c0 += 64) {
     const int k = c0 + lane;
-    const uint32_t u = k < L ? key(k) : 0u;
-    const bool eq = k < L && u == T;
+    const uint32_t u = k < s1 ? key(k) : 0u;
+    weq += __popcll(__ballot(k < s1 && u == T));
+    wgt += __popcll(__ballot(k < s1 && u > T));
+  }
+  if (lane == 0) {
+    seg_eq[w] = weq;
+    seg_gt[w] = wgt;
+  }
+  __syncthreads();
+  unsigned eq_seen = 0, gt_before = 0;
+  for (int ww = 0; ww < w; ++ww) {
+    eq_seen += seg_eq[ww];
+    gt_before += seg_gt[ww];
+  }
+  int sel_seen = (int)(gt_before + min(eq_seen, remaining));
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int c0 = s0; c0 < s1 && sel_seen < topb; c0 += 64) {
+    const int k = c0 + lane;
+    const uint32_t u = k < s1 ? key(k) : 0u;
+    const bool eq = k < s1 && u == T;
     const unsigned long long beq = __ballot(eq);
-    const bool sel = (k < L && u > T) || (eq && eq_seen + __popcll(beq & below) < remaining);
+    const bool sel = (k < s1 && u > T) || (eq && eq_seen + __popcll(beq & below) < remaining);
     const unsigned long long bsel = __ballot(sel);
     const int pos = sel_seen + __popcll(bsel & below);
     if (sel && pos < topb) ob[pos] = k;
