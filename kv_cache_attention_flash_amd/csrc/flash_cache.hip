@@ -782,17 +782,24 @@ hipError_t launch_flash_cache(const FlashCacheArgs &a, void *ws, size_t ws_bytes
   // More than 64 rows (or a hidden size the chunking does not divide): the
   // tiled MFMA kernel, 128 rows x 128 rotary pairs per workgroup.  A grid
   // that fits one workgroup per CU takes K in steps of 64 with one register
-  // stage (each workgroup owns its CU; half the barriers per MFMA); larger
-  // grids take steps of 32 with two stages, two workgroups per CU, whose
-  // loads in flight hide more of the weight stream's latency (measured on
-  // the bench: 85.6 against 94.5 us at 512 rows, 241.3 against 254.3 us at
-  // 2048).  The accumulation order is the same, so are the results.
+  // stage (each workgroup owns its CU; half the barriers per MFMA); failing
+  // that, 256-row tiles in steps of 64 if their grid fits (one workgroup per
+  // CU again, twice the reuse of each weight tile); larger grids take 128-row
+  // tiles in steps of 32 with two stages, two workgroups per CU, whose loads
+  // in flight hide more of the weight stream's latency.  Measured on the
+  // bench: 85.6 against 94.5 us at 512 rows, 141.9 against 157.3 us at 1024,
+  // 241.3 against 254.3 us at 2048.  Every form accumulates in the same order,
+  // so the results are the same.
   const int total_pairs = 3 * a.c.H * (a.c.D / 2);
   constexpr int BM = 128, NWN = 4, BP = 32 * NWN;
   const int nrow = (a.rows + BM - 1) / BM, ncol = (total_pairs + BP - 1) / BP;
+  const int nrow2 = (a.rows + 2 * BM - 1) / (2 * BM);  // with 256-row tiles
   if (nrow * ncol <= device_cus())
     hipLaunchKernelGGL((qkv_gemm_kernel<BM, NWN, 1, 64>), dim3(nrow * ncol), dim3(128 * NWN), 0,
                        s, a, nrow, ncol);
+  else if (nrow2 * ncol <= device_cus())
+    hipLaunchKernelGGL((qkv_gemm_kernel<2 * BM, NWN, 1, 64>), dim3(nrow2 * ncol), dim3(128 * NWN),
+                       0, s, a, nrow2, ncol);
   else
     hipLaunchKernelGGL((qkv_gemm_kernel<BM, NWN, 2, 32>), dim3(nrow * ncol), dim3(128 * NWN), 0,
                        s, a, nrow, ncol);

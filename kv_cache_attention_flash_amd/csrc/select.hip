@@ -89,7 +89,10 @@ __global__ __launch_bounds__(NT) void topb_kernel(const float *mass, int stride,
     }
     const unsigned incl = wave_incl_scan(lsum);
     const unsigned excl = incl - lsum;
-    const int src = __ffsll((long long)__ballot(excl < remaining && incl >= remaining)) - 1;
+    // Exactly one lane crosses (the candidates number at least `remaining`);
+    // the clamp keeps the lane index valid whatever the counts.
+    const int src =
+        max(0, __ffsll((long long)__ballot(excl < remaining && incl >= remaining)) - 1);
     unsigned digit = 0, rem = 0, cum = excl;
     bool found = false;
 #pragma unroll
