@@ -482,8 +482,11 @@ __device__ __forceinline__ int gemm_swz(int row) {
 // LDS of one tiled-projection workgroup.
 template <int BM, int NWN, int BK = 32>
 struct GemmLds {
-  static constexpr int TR = BM + 64 * NWN, PIECES = BK / 8;
-  u32x4 lds[2][TR * PIECES];
+  // staged rows, padded to a whole number of loads per thread (the padding
+  // rows receive clamped loads and are never read)
+  static constexpr int TR = BM + 64 * NWN, PIECES = BK / 8, NT = 128 * NWN;
+  static constexpr int TRP = (TR * PIECES + NT - 1) / NT * NT / PIECES;
+  u32x4 lds[2][TRP * PIECES];
   int s_blk[BM], s_off[BM], s_pos[BM];
 };
 
@@ -497,8 +500,8 @@ __device__ __forceinline__ void qkv_gemm_body(const FlashCacheArgs &a, int nrow_
   static_assert(BK == 32 || BK == 64, "K step");
   constexpr int MTW = BM / 64;                         // 32-row M tiles per wave
   constexpr int TR = BM + BN;                          // staged rows per step
-  constexpr int LD = TR * PIECES / NT;                 // 16-byte loads per thread per step
-  static_assert(TR * PIECES % NT == 0, "step must split evenly over the threads");
+  constexpr int LD = (TR * PIECES + NT - 1) / NT;      // 16-byte loads per thread per step
+  static_assert(NT % PIECES == 0, "whole rows per load round");
   auto &lds = L.lds;
   auto &s_blk = L.s_blk;
   auto &s_off = L.s_off;
@@ -780,29 +783,32 @@ hipError_t launch_flash_cache(const FlashCacheArgs &a, void *ws, size_t ws_bytes
     return hipGetLastError();
   }
   // More than 64 rows (or a hidden size the chunking does not divide): the
-  // tiled MFMA kernel, 128 rows x 128 rotary pairs per workgroup.  A grid
-  // that fits one workgroup per CU takes K in steps of 64 with one register
-  // stage (each workgroup owns its CU; half the barriers per MFMA); failing
-  // that, 256-row tiles in steps of 64 if their grid fits (one workgroup per
-  // CU again, twice the reuse of each weight tile); larger grids take 128-row
-  // tiles in steps of 32 with two stages, two workgroups per CU, whose loads
-  // in flight hide more of the weight stream's latency.  Measured on the
-  // bench: 85.6 against 94.5 us at 512 rows, 141.9 against 157.3 us at 1024,
-  // 241.3 against 254.3 us at 2048.  Every form accumulates in the same order,
-  // so the results are the same.
+  // tiled MFMA kernel.  When a grid of 128 rows x 96 rotary pairs (six waves)
+  // fits one workgroup per CU, that form runs with K in steps of 64 and one
+  // register stage (each workgroup owns its CU; half the barriers per MFMA);
+  // failing that, 256-row tiles of the same width if their grid fits (twice
+  // the reuse of each weight tile); larger grids take 128 rows x 128 pairs
+  // (eight waves) in steps of 32 with two register stages, two workgroups per
+  // CU, whose loads in flight hide more of the weight stream's latency.
+  // Measured on the bench: 76.9 against 94.5 us at 512 rows, 137.4 against
+  // 157.3 us at 1024, 237.5 against 254.3 us at 2048 (the other forms).  Every
+  // form accumulates in the same order, so the results are the same.
   const int total_pairs = 3 * a.c.H * (a.c.D / 2);
-  constexpr int BM = 128, NWN = 4, BP = 32 * NWN;
-  const int nrow = (a.rows + BM - 1) / BM, ncol = (total_pairs + BP - 1) / BP;
-  const int nrow2 = (a.rows + 2 * BM - 1) / (2 * BM);  // with 256-row tiles
-  if (nrow * ncol <= device_cus())
-    hipLaunchKernelGGL((qkv_gemm_kernel<BM, NWN, 1, 64>), dim3(nrow * ncol), dim3(128 * NWN), 0,
-                       s, a, nrow, ncol);
-  else if (nrow2 * ncol <= device_cus())
-    hipLaunchKernelGGL((qkv_gemm_kernel<2 * BM, NWN, 1, 64>), dim3(nrow2 * ncol), dim3(128 * NWN),
-                       0, s, a, nrow2, ncol);
-  else
-    hipLaunchKernelGGL((qkv_gemm_kernel<BM, NWN, 2, 32>), dim3(nrow * ncol), dim3(128 * NWN), 0,
-                       s, a, nrow, ncol);
+  constexpr int BM = 128;
+  const int cus = device_cus();
+  const int ncol6 = (total_pairs + 95) / 96;
+  const int nrow = (a.rows + BM - 1) / BM, nrow2 = (a.rows + 2 * BM - 1) / (2 * BM);
+  if (nrow * ncol6 <= cus) {
+    hipLaunchKernelGGL((qkv_gemm_kernel<BM, 3, 1, 64>), dim3(nrow * ncol6), dim3(128 * 3), 0, s,
+                       a, nrow, ncol6);
+  } else if (nrow2 * ncol6 <= cus) {
+    hipLaunchKernelGGL((qkv_gemm_kernel<2 * BM, 3, 1, 64>), dim3(nrow2 * ncol6), dim3(128 * 3), 0,
+                       s, a, nrow2, ncol6);
+  } else {
+    const int ncol8 = (total_pairs + 127) / 128;
+    hipLaunchKernelGGL((qkv_gemm_kernel<BM, 4, 2, 32>), dim3(nrow * ncol8), dim3(128 * 4), 0, s,
+                       a, nrow, ncol8);
+  }
   return hipGetLastError();
 }
 
