@@ -123,8 +123,7 @@ __device__ __forceinline__ u32x4 tile_softmax(const f32x4 s[2], const Vis &vis, 
   }
   float tmax = fmaxf(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])),
                      fmaxf(fmaxf(xs[4], xs[5]), fmaxf(xs[6], xs[7])));
-  tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+  tmax = rows4_max(tmax);
   const float mnew = fmaxf(m, tmax);
   const float msafe = mnew == kNegInf ? 0.f : mnew;  // a row that has seen nothing keeps zeros
   const float alpha = fast_exp2(m - msafe);
@@ -134,8 +133,7 @@ __device__ __forceinline__ u32x4 tile_softmax(const f32x4 s[2], const Vis &vis, 
     pv[e] = fast_exp2(xs[e] - msafe);
     rs += pv[e];
   }
-  rs += shfl_xor(rs, 16);
-  rs += shfl_xor(rs, 32);
+  rs = rows4_sum(rs);
   l = l * alpha + rs;
   m = mnew;
   if (__any(alpha != 1.f)) {
@@ -543,23 +541,23 @@ __global__ __launch_bounds__(256) void attn_mass_kernel(AttnArgs a, AttnPlan p) 
       for (int i = 0; i < 4; ++i) {
         const float give = b3 ? pv[i] : pv[i + 4];
         const float keep = b3 ? pv[i + 4] : pv[i];
-        q4[i] = keep + shfl_xor(give, 8);
+        q4[i] = keep + lane_xor8(give);
       }
       float q2[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const float give = b2 ? q4[i] : q4[i + 2];
         const float keep = b2 ? q4[i + 2] : q4[i];
-        q2[i] = keep + shfl_xor(give, 4);
+        q2[i] = keep + lane_xor4(give);
       }
       float q1;
       {
         const float give = b1 ? q2[0] : q2[1];
         const float keep = b1 ? q2[1] : q2[0];
-        q1 = keep + shfl_xor(give, 2);
+        q1 = keep + lane_xor2(give);
       }
       // Lanes l and l^1 now hold the same key; add them in a fixed order.
-      const float other = shfl_xor(q1, 1);
+      const float other = lane_xor1(q1);
       const float tot = (j & 1) ? other + q1 : q1 + other;
       if ((j & 1) == 0) wsum[wave][8 * g + 4 * b3 + 2 * b2 + b1] = tot;
       }
@@ -828,19 +826,19 @@ __device__ __forceinline__ void attn_rows_body(const AttnArgs &a, const AttnPlan
       for (int i = 0; i < 4; ++i) {
         const float give = b3 ? pv[i] : pv[i + 4];
         const float keep = b3 ? pv[i + 4] : pv[i];
-        q4[i] = keep + shfl_xor(give, 8);
+        q4[i] = keep + lane_xor8(give);
       }
       float q2[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const float give = b2 ? q4[i] : q4[i + 2];
         const float keep = b2 ? q4[i + 2] : q4[i];
-        q2[i] = keep + shfl_xor(give, 4);
+        q2[i] = keep + lane_xor4(give);
       }
       const float give = b1 ? q2[0] : q2[1];
       const float keep = b1 ? q2[1] : q2[0];
-      const float q1 = keep + shfl_xor(give, 2);
-      const float other = shfl_xor(q1, 1);
+      const float q1 = keep + lane_xor2(give);
+      const float other = lane_xor1(q1);
       const float tot = (j & 1) ? other + q1 : q1 + other;
       const int jj = (w + kRowWaves * kk) * KT + 8 * g + 4 * b3 + 2 * b2 + b1;
       if ((j & 1) == 0 && jj < si.L) mp[jj] = tot;

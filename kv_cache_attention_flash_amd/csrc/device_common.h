@@ -61,6 +61,37 @@ __device__ __forceinline__ T shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, kWave);
 }
 
+// Lane exchanges on the ALU instead of the LDS crossbar (`ds_bpermute`):
+// DPP moves for partners inside a row of 16 lanes and the gfx950 permlane
+// swaps across rows.  The whole wave must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// The value held by lane ^ 1, ^ 2, ^ 4, ^ 8.
+__device__ __forceinline__ float lane_xor1(float v) { return dpp_mov<0xB1>(v); }  // quad_perm 1032
+__device__ __forceinline__ float lane_xor2(float v) { return dpp_mov<0x4E>(v); }  // quad_perm 2301
+__device__ __forceinline__ float lane_xor8(float v) { return dpp_mov<0x128>(v); }  // row_ror:8
+__device__ __forceinline__ float lane_xor4(float v) {
+  const float down = dpp_mov<0x124>(v), up = dpp_mov<0x12C>(v);  // row_ror:4 (lane - 4), :12 (+ 4)
+  return (threadIdx.x & 4) ? down : up;
+}
+// Sum and maximum over lanes l, l ^ 16, l ^ 32, l ^ 48, the same in every one
+// of them.  The sum adds (row 0 + row 1) + (row 2 + row 3) for every lane, as
+// two xor-16 and xor-32 shuffle-and-add steps do (addition is commutative).
+__device__ __forceinline__ float rows4_sum(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float s = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+__device__ __forceinline__ float rows4_max(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float s = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS traffic,
 // not for its outstanding global loads (which stay in flight across it).
 __device__ __forceinline__ void lds_barrier() {
