@@ -41,6 +41,9 @@ constexpr int KT = 32;  // keys per tile
 #ifndef FDL_ATTN_MNPF
 #define FDL_ATTN_MNPF 2
 #endif
+#ifndef FDL_ATTN_ROWS_KLDS
+#define FDL_ATTN_ROWS_KLDS 1  // row-group path: K through a wave-private LDS tile
+#endif
 constexpr float kNegInf = -__builtin_huge_valf();
 
 struct SeqInfo {
@@ -618,19 +621,37 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnArgs a, AttnPlan p
 // the whole cached length.  The workgroup therefore ends with every row's
 // final log-sum-exp and needs no split merge; with the mass requested it also
 // needs no second pass over K.  8 waves = 8 key groups, wave w taking tiles
-// w, w + 8, ...  A wave's K operands load straight from HBM into MFMA
-// registers (lane j of M-tile mt reads 16 bytes of key 8(j/4) + 4mt + j%4, the
-// permutation that leaves lane group g holding keys 8g .. 8g+7 of S^T); its V
-// tile passes through a wave-private LDS buffer for the transposing read, so
-// the key loop has no workgroup barrier.  Two tiles per wave are in flight.
+// w, w + 8, ...  A wave loads its K and V tiles with coalesced 16-byte loads
+// and passes both through wave-private LDS tiles, so the key loop has no
+// workgroup barrier: K is read back in the MFMA operand layout (lane j of
+// M-tile mt takes key 8(j/4) + 4mt + j%4, the permutation that leaves lane
+// group g holding keys 8g .. 8g+7 of S^T), V transposed.  Two tiles per wave
+// are in flight.
 // With the mass requested each wave keeps its scaled scores (at most MAXT
 // tiles) in registers and, once the workgroup has combined the waves' maxima
 // and normalisers, sums exp2(s - LSE) over its 16 rows for each of its keys.
 constexpr int kRowWaves = 8;
 
+// Slot (in 16-byte chunks) of chunk ch of key row key in a wave's K tile.
+// One MFMA operand read gathers one chunk of the 16 keys 8a + b + 4m (a, b
+// < 4): the chunk index is XORed with the key bits that vary over that set,
+// so the 16 reads land in distinct banks.  D = 128: bits 0, 1, 3, 4 of the
+// key; D = 64 (two rows per 256-byte bank line, told apart by bit 0): bits 1,
+// 3, 4.  A row's chunks stay a permutation of its slots, so the coalesced
+// writes are conflict-free too.
+template <int D>
+__device__ __forceinline__ int kslot(int key, int ch) {
+  static_assert(D == 64 || D == 128, "head size");
+  if constexpr (D == 128) return key * 16 + (ch ^ ((key & 3) | ((key >> 1) & 12)));
+  else return key * 8 + (ch ^ (((key >> 1) & 1) | ((key >> 2) & 6)));
+}
+
 // LDS of one row-group workgroup.
 template <int D>
 struct RowsLds {
+#if FDL_ATTN_ROWS_KLDS
+  u32x4 kbuf[kRowWaves][KT * D / 8];
+#endif
   uint16_t vbuf[kRowWaves][KT][kVPad<D>];
   int s_page[kMaxPages];
   float s_ml[kRowWaves][16][2];
@@ -693,6 +714,13 @@ __device__ __forceinline__ void attn_rows_body(const AttnArgs &a, const AttnPlan
       const int page = s_page[key0 / a.c.bs];
       base = (((size_t)page * a.c.H + h) * a.c.bs + (key0 % a.c.bs)) * D;
     }
+#if FDL_ATTN_ROWS_KLDS
+    // A tile's keys are one contiguous run of its page: whole 128-byte lines
+    // per 8 lanes, the operand layout being formed in LDS.
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i)
+      st.k[i] = ld16(a.c.k + (real ? base + (size_t)(lane + 64 * i) * 8 : (size_t)0));
+#else
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int key = 8 * (j >> 2) + 4 * mt + (j & 3);
@@ -701,6 +729,7 @@ __device__ __forceinline__ void attn_rows_body(const AttnArgs &a, const AttnPlan
         st.k[mt * KS + ks] =
             ld16(a.c.k + (real ? base + (size_t)key * D + 32 * ks + 8 * g : (size_t)0));
     }
+#endif
 #pragma unroll
     for (int i = 0; i < VLD; ++i)
       st.v[i] = ld16(a.c.v + (real ? base + (size_t)(lane + 64 * i) * 8 : (size_t)0));
@@ -722,12 +751,26 @@ __device__ __forceinline__ void attn_rows_body(const AttnArgs &a, const AttnPlan
       for (int e = 0; e < 8; ++e) xs[e] = kNegInf;
       return;
     }
+#if FDL_ATTN_ROWS_KLDS
+    u32x4 *kb = L.kbuf[w];
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      const int c = lane + 64 * i;
+      kb[kslot<D>(c / CH, c % CH)] = st.k[i];
+    }
+#endif
     f32x4 s[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#if FDL_ATTN_ROWS_KLDS
+      const int key = 8 * (j >> 2) + 4 * mt + (j & 3);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma16(kb[kslot<D>(key, 4 * ks + g)], qf[ks], acc);
+#else
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) acc = mfma16(st.k[mt * KS + ks], qf[ks], acc);
+#endif
       s[mt] = acc;
     }
     const bool part = key0 + KT > si.L;
