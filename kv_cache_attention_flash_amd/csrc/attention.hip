@@ -44,6 +44,12 @@ constexpr int KT = 32;  // keys per tile
 #ifndef FDL_ATTN_ROWS_KLDS
 #define FDL_ATTN_ROWS_KLDS 1  // row-group path: K through a wave-private LDS tile
 #endif
+#ifndef FDL_ATTN_ROWS_BUF
+#define FDL_ATTN_ROWS_BUF 1  // row-group path: tiles read through range-checked buffer views
+#endif
+#if FDL_ATTN_ROWS_BUF && !FDL_ATTN_ROWS_KLDS
+#error "buffer-view tile loads use the coalesced K layout"
+#endif
 constexpr float kNegInf = -__builtin_huge_valf();
 
 struct SeqInfo {
@@ -685,7 +691,9 @@ __device__ __forceinline__ void attn_rows_body(const AttnArgs &a, const AttnPlan
   const int t0 = rg * 16;
   if (t0 >= si.nrows) return;
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // The wave index in a scalar register: the tile schedule and the tile
+  // descriptors derived from it are then wave-uniform to the compiler too.
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, j = lane & 15;
   const int t = t0 + j;  // local row of this lane
   const bool row_ok = t < si.nrows;
@@ -706,6 +714,28 @@ __device__ __forceinline__ void attn_rows_body(const AttnArgs &a, const AttnPlan
   // Loads of the wave's kk-th tile.  Past the wave's last tile the same number
   // of load instructions is issued at one fixed 16-byte address (every lane
   // alike), so the count of loads in flight never depends on the data.
+#if FDL_ATTN_ROWS_BUF
+  // Wave-uniform descriptors per tile: the tile's keys are one contiguous run
+  // of a page; keys at or past the cached length (and every key of a padding
+  // tile) lie outside the view and load as zeros, so V needs no masking and
+  // the per-lane addresses are the same for every tile.
+  const int bs_log2 = __builtin_ctz(a.c.bs);
+  auto issue = [&](Stage &st, int kk) {
+    const int key0 = (w + kRowWaves * kk) * KT;
+    size_t off = 0;
+    int bytes = 0;
+    if (kk < n_w) {
+      const int page = __builtin_amdgcn_readfirstlane(s_page[key0 >> bs_log2]);
+      off = (((size_t)page * a.c.H + h) * a.c.bs + (key0 & (a.c.bs - 1))) * D;
+      bytes = min(KT, si.L - key0) * D * 2;
+    }
+    const auto rk = buffer_view(a.c.k + off, bytes), rv = buffer_view(a.c.v + off, bytes);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) st.k[i] = buffer_ld16(rk, (lane + 64 * i) * 16);
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) st.v[i] = buffer_ld16(rv, (lane + 64 * i) * 16);
+  };
+#else
   auto issue = [&](Stage &st, int kk) {
     const bool real = kk < n_w;
     const int key0 = (w + kRowWaves * kk) * KT;
@@ -734,6 +764,7 @@ __device__ __forceinline__ void attn_rows_body(const AttnArgs &a, const AttnPlan
     for (int i = 0; i < VLD; ++i)
       st.v[i] = ld16(a.c.v + (real ? base + (size_t)(lane + 64 * i) * 8 : (size_t)0));
   };
+#endif
 
   f32x4 o[D / 16];
 #pragma unroll
@@ -773,13 +804,17 @@ __device__ __forceinline__ void attn_rows_body(const AttnArgs &a, const AttnPlan
 #endif
       s[mt] = acc;
     }
-    const bool part = key0 + KT > si.L;
 #pragma unroll
     for (int i = 0; i < VLD; ++i) {
       const int c = lane + 64 * i;
       const int key = c / CH;
+#if FDL_ATTN_ROWS_BUF
+      st16(&vb[key][(c % CH) * 8], st.v[i]);  // zeros past the length
+#else
+      const bool part = key0 + KT > si.L;
       st16(&vb[key][(c % CH) * 8],
            part && key0 + key >= si.L ? u32x4{0u, 0u, 0u, 0u} : st.v[i]);
+#endif
     }
     const u32x4 pb = tile_softmax<D / 16>(s, vis, tv, key0, g, a.scale_log2, m, l, o, xs);
 #pragma unroll

@@ -108,6 +108,18 @@ __device__ __forceinline__ u32x4 ld16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// Raw buffer view of [base, base + bytes) (base and bytes wave-uniform): a
+// 16-byte load at a byte offset at or past `bytes` returns zeros and touches
+// no memory (the buffer range check); bytes = 0 makes every load such a load.
+// Descriptor word 3 selects 32-bit raw elements (the gfx9-family layout).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_ld16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
 __device__ __forceinline__ void st16(void *p, const u32x4 &v) {
   *reinterpret_cast<u32x4 *>(p) = v;
 }
