@@ -44,6 +44,23 @@ def test_block_size_64_and_d128():
     full_check(wl)
 
 
+def test_block_size_256_both_attention_paths():
+    """The largest page size: tiles are runs of one page, a page holds eight
+    32-key tiles, lengths end inside a page.  Row-group path (head_dim 128,
+    short cache) and split path (head_dim 64, a cache past 1024 keys)."""
+    _banner("block size 256: row-group path")
+    g = np.random.default_rng(7)
+    specs = [SeqSpec(kv_len=600, window=(512, 32),
+                     tracked=tuple(sorted(int(x) for x in g.choice(512, 24, replace=False)))),
+             SeqSpec(kv_len=300, window=(200, 17)),
+             SeqSpec(kv_len=257, window=(256, 1), tracked=(0, 255))]
+    full_check(synth.build("bs256", 23, 256, 3, 128, 256, 5.0e5, specs, topb=16))
+    _banner("block size 256: split path")
+    specs = [SeqSpec(kv_len=1300, window=(1024, 32), tracked=(1, 500, 1000)),
+             SeqSpec(kv_len=520, window=(256, 32))]
+    full_check(synth.build("bs256_long", 24, 256, 2, 64, 256, 1.0e4, specs, topb=8))
+
+
 def test_empty_calls():
     fd = _fd()
     dev = "cuda:0"
