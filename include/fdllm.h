@@ -24,6 +24,15 @@
  *     Index contents of device arrays (positions, slots, block ids, lengths)
  *     are not read by the host: values out of range are undefined behaviour,
  *     as for any paged-attention kernel; the caller validates them.
+ *   - With FDL_DEBUG=1 in the environment (read at every call), the calls that
+ *     index the cache (flash_cache_step, flash_cache_step_unfused,
+ *     scheduled_attention, flash_cache_attention_step) first synchronise their
+ *     stream and check those arrays on the host: cu_rows starts at 0, never
+ *     decreases and ends at most at num_rows; active rows have positions >= 0
+ *     and logical slots inside their block-table row; every block id a row
+ *     writes or a visible slot reads lies in [0, num_blocks); lengths are
+ *     >= 0; no physical slot is written by two rows.  A violation returns
+ *     FDL_EINVAL with nothing launched (a failed copy, FDL_EHIP).
  *
  * Supported shapes: head_dim in {64, 128}; block_size in {32, 64, 128, 256};
  * hidden a multiple of 128 and at most 32768; num_heads * head_dim <= 16384;

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
+#include <vector>
 
 #include "../../include/fdllm.h"
 #include "internal.h"
@@ -46,6 +48,79 @@ fdl::CacheView view_of(const fdl_kv_cache *c) {
   v.v = static_cast<uint16_t *>(c->v_cache);
   v.block_table = c->block_table;
   return v;
+}
+
+// FDL_DEBUG=1 in the environment (read at every call): the calls that index
+// the cache synchronise their stream, copy the index arrays to the host and
+// refuse out-of-range or duplicate entries with FDL_EINVAL before launching.
+bool debug_mode() {
+  const char *e = std::getenv("FDL_DEBUG");
+  return e && e[0] == '1' && e[1] == '\0';
+}
+
+// n int32 values of device memory into h (the stream already synchronised).
+bool fetch_i32(std::vector<int32_t> &h, const int32_t *d, size_t n) {
+  h.assign(n, 0);
+  return n == 0 || hipMemcpy(h.data(), d, n * sizeof(int32_t), hipMemcpyDeviceToHost) == hipSuccess;
+}
+
+// Row offsets: cu[0] = 0, non-decreasing, cu[batch] <= num_rows.
+int debug_check_cu(const std::vector<int32_t> &cu, int batch, int num_rows) {
+  if (cu[0] != 0 || cu[batch] > num_rows) return FDL_EINVAL;
+  for (int b = 0; b < batch; ++b)
+    if (cu[b + 1] < cu[b]) return FDL_EINVAL;
+  return FDL_OK;
+}
+
+// flash_cache_step's index arrays: non-negative positions; logical slots within
+// the block table's row; block ids within the pool; no physical slot written
+// twice.
+int debug_check_rows(const fdl_kv_cache *c, int batch, int num_rows, const int32_t *cu_rows,
+                     const int32_t *positions, const int32_t *slots, hipStream_t s) {
+  if (hipStreamSynchronize(s) != hipSuccess) return FDL_EHIP;
+  std::vector<int32_t> cu, pos, sl, bt;
+  if (!fetch_i32(cu, cu_rows, (size_t)batch + 1)) return FDL_EHIP;
+  int st = debug_check_cu(cu, batch, num_rows);
+  if (st) return st;
+  const int act = cu[batch];
+  if (!fetch_i32(pos, positions, act) || !fetch_i32(sl, slots, act) ||
+      !fetch_i32(bt, c->block_table, (size_t)batch * c->max_blocks_per_seq))
+    return FDL_EHIP;
+  const long span = (long)c->max_blocks_per_seq * c->block_size;
+  std::vector<char> used((size_t)c->num_blocks * c->block_size, 0);
+  for (int b = 0; b < batch; ++b)
+    for (int r = cu[b]; r < cu[b + 1]; ++r) {
+      if (pos[r] < 0 || sl[r] < 0 || sl[r] >= span) return FDL_EINVAL;
+      const int blk = bt[(size_t)b * c->max_blocks_per_seq + sl[r] / c->block_size];
+      if (blk < 0 || blk >= c->num_blocks) return FDL_EINVAL;
+      char &u = used[(size_t)blk * c->block_size + sl[r] % c->block_size];
+      if (u) return FDL_EINVAL;
+      u = 1;
+    }
+  return FDL_OK;
+}
+
+// scheduled_attention's index arrays: row offsets, non-negative lengths, and
+// the block ids of every page a visible slot lies in.
+int debug_check_attention(const fdl_kv_cache *c, int batch, int num_rows,
+                          const int32_t *cu_rows, const int32_t *kv_len, int max_kv_len,
+                          hipStream_t s) {
+  if (hipStreamSynchronize(s) != hipSuccess) return FDL_EHIP;
+  std::vector<int32_t> cu, kl, bt;
+  if (!fetch_i32(cu, cu_rows, (size_t)batch + 1) || !fetch_i32(kl, kv_len, batch) ||
+      !fetch_i32(bt, c->block_table, (size_t)batch * c->max_blocks_per_seq))
+    return FDL_EHIP;
+  int st = debug_check_cu(cu, batch, num_rows);
+  if (st) return st;
+  for (int b = 0; b < batch; ++b) {
+    if (kl[b] < 0) return FDL_EINVAL;
+    const int L = kl[b] < max_kv_len ? kl[b] : max_kv_len;
+    for (int p = 0; p < (L + c->block_size - 1) / c->block_size; ++p) {
+      const int blk = bt[(size_t)b * c->max_blocks_per_seq + p];
+      if (blk < 0 || blk >= c->num_blocks) return FDL_EINVAL;
+    }
+  }
+  return FDL_OK;
 }
 
 }  // namespace
@@ -122,6 +197,9 @@ int flash_cache_common(bool unfused, const fdl_kv_cache *cache, const void *x, i
                                                  cache->head_dim);
   if (workspace_bytes < need || (need && !workspace)) return FDL_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_mode() &&
+      (st = debug_check_rows(cache, batch, num_rows, cu_rows, positions, slots, s)))
+    return st;
   return hip_status(unfused ? fdl::launch_flash_cache_unfused(a, workspace, workspace_bytes, s)
                             : fdl::launch_flash_cache(a, workspace, workspace_bytes, s));
 }
@@ -236,6 +314,9 @@ int scheduled_attention(const fdl_kv_cache *cache, const void *q, int32_t batch,
   if (st || empty == 1) return st;
   if (plan.bytes > workspace_bytes || (plan.bytes && !workspace)) return FDL_EWORKSPACE;
   if (empty) return FDL_OK;
+  if (debug_mode() && (st = debug_check_attention(cache, batch, num_rows, cu_rows, kv_len,
+                                                  max_kv_len, static_cast<hipStream_t>(stream))))
+    return st;
   a.ws = static_cast<char *>(workspace);
   return hip_status(fdl::launch_attention(a, plan, static_cast<hipStream_t>(stream)));
 }
@@ -273,6 +354,13 @@ int flash_cache_attention_step(const fdl_kv_cache *cache, const void *x, int32_t
   if (st || empty_at == 1) return st;
   if (!mass) return FDL_EINVAL;
   if (workspace_bytes < kFusedSyncBytes + plan.bytes || !workspace) return FDL_EWORKSPACE;
+  if (debug_mode()) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!empty_fc && (st = debug_check_rows(cache, batch, num_rows, cu_rows, positions, slots, s)))
+      return st;
+    if ((st = debug_check_attention(cache, batch, num_rows, cu_rows, kv_len, max_kv_len, s)))
+      return st;
+  }
   if (empty_fc) {
     // No rows to project: what remains is the attention call's (with the
     // mass asked for, it writes zeros).
