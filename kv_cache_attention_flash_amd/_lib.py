@@ -12,7 +12,10 @@ import os
 
 import torch  # noqa: F401  (loads the process's HIP runtime before the library)
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfdllm.so")
+# FDL_LIB names another build of the same library (the host-sanitised one,
+# for instance); by default the in-tree libfdllm.so.
+LIB_PATH = os.environ.get("FDL_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                     "libfdllm.so")
 
 FDL_OK, FDL_EINVAL, FDL_EUNSUPPORTED, FDL_EWORKSPACE, FDL_EHIP = 0, 1, 2, 3, 4
 

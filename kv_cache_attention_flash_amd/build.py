@@ -1,6 +1,7 @@
 """Build libfdllm.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc.
 
-Usage: python -m kv_cache_attention_flash_amd.build [--jobs N]
+Usage: python -m kv_cache_attention_flash_amd.build [--jobs N] [--asan]
+(--asan also builds libfdllm_asan.so, the host code under AddressSanitizer)
 """
 
 from __future__ import annotations
@@ -59,8 +60,47 @@ def build(jobs: int = 4, verbose: bool = True) -> str:
     return OUT
 
 
+ASAN_OUT = os.path.join(HERE, "libfdllm_asan.so")
+# Host code only: the device code is built as usual.
+ASAN_HOST_FLAGS = "-Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer".split()
+
+
+def asan_runtime() -> str | None:
+    """The compiler's shared AddressSanitizer runtime (to preload), if present."""
+    import glob
+    llvm = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(hipcc()))), "lib", "llvm")
+    hits = sorted(glob.glob(os.path.join(llvm, "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    return hits[-1] if hits else None
+
+
+def build_asan(verbose: bool = True) -> str:
+    """libfdllm_asan.so: the C ABI's host code (argument validation, planning,
+    dispatch) instrumented with AddressSanitizer, linked with the kernel
+    objects of the last build().  Load it with the runtime preloaded
+    (LD_PRELOAD=asan_runtime()) and FDL_LIB pointing at it."""
+    obj = os.path.join(OBJ_DIR, "abi_asan.cpp.o")
+    cmd = [hipcc(), *FLAGS, *ASAN_HOST_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, "abi.cpp"),
+           "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on abi.cpp (host ASan):\n{res.stdout}\n{res.stderr}")
+    objs = [os.path.join(OBJ_DIR, s + ".o") for s in SOURCES if s != "abi.cpp"] + [obj]
+    tmp = ASAN_OUT + ".tmp"
+    res = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, ASAN_OUT)
+    if verbose:
+        print(f"built {ASAN_OUT}")
+    return ASAN_OUT
+
+
 if __name__ == "__main__":
     j = 4
     if "--jobs" in sys.argv:
         j = int(sys.argv[sys.argv.index("--jobs") + 1])
     build(j)
+    if "--asan" in sys.argv:
+        build_asan()
