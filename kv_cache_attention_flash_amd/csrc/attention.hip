@@ -183,8 +183,22 @@ struct Tile {
   static constexpr int NCH = KT * CH / 256;         // chunks per thread
   u32x4 k[NCH], v[NCH];
 };
-template <int D> constexpr int kKPad = D + 8;   // K row stride (elements)
 template <int D> constexpr int kVPad = D + 16;  // V row stride: conflict-free transposed reads
+
+// Slot (in 16-byte chunks) of chunk ch of key row key in a K tile held in LDS.
+// One MFMA operand read gathers one chunk of the 16 keys 8a + b + 4m (a, b
+// < 4): the chunk index is XORed with the key bits that vary over that set,
+// so the 16 reads land in distinct banks.  D = 128: bits 0, 1, 3, 4 of the
+// key; D = 64 (two rows per 256-byte bank line, told apart by bit 0): bits 1,
+// 3, 4.  A row's chunks stay a permutation of its slots, so the coalesced
+// writes are conflict-free too.
+template <int D>
+__device__ __forceinline__ int kslot(int key, int ch) {
+  static_assert(D == 64 || D == 128, "head size");
+  if constexpr (D == 128) return key * 16 + (ch ^ ((key & 3) | ((key >> 1) & 12)));
+  else return key * 8 + (ch ^ (((key >> 1) & 1) | ((key >> 2) & 6)));
+}
+
 
 // Physical pages of the tiles a workgroup visits, staged once in LDS so that a
 // tile's address never waits on a block-table load.
@@ -215,7 +229,7 @@ __device__ __forceinline__ void load_tile(Tile<D> &t, const AttnArgs &a, const i
 // stored as zeros: those slots' contents are unspecified, and a zero weight
 // times a NaN would still poison the product.
 template <int D>
-__device__ __forceinline__ void store_tile(const Tile<D> &t, uint16_t (*klds)[kKPad<D>],
+__device__ __forceinline__ void store_tile(const Tile<D> &t, u32x4 *klds,
                                            uint16_t (*vlds)[kVPad<D>], bool want_v, int gtid,
                                            int vkeys = KT) {
   const bool part = vkeys < KT;
@@ -223,7 +237,7 @@ __device__ __forceinline__ void store_tile(const Tile<D> &t, uint16_t (*klds)[kK
   for (int i = 0; i < Tile<D>::NCH; ++i) {
     const int c = gtid + 256 * i;
     const int key = c / Tile<D>::CH, dc = c % Tile<D>::CH;
-    st16(&klds[key][dc * 8], t.k[i]);
+    klds[kslot<D>(key, dc)] = t.k[i];
     if (want_v)
       st16(&vlds[key][dc * 8], part && key >= vkeys ? u32x4{0u, 0u, 0u, 0u} : t.v[i]);
   }
@@ -250,7 +264,7 @@ __device__ __forceinline__ u32x4 vt_operand(uint16_t (*vlds)[kVPad<D>], int dm, 
 // S^T tile (32 keys x 16 rows) for one wave: s[mt][e] is key 8g + 4mt + e for
 // query row (lane & 15).
 template <int D>
-__device__ __forceinline__ void scores(const uint16_t (*klds)[kKPad<D>], const u32x4 *qf,
+__device__ __forceinline__ void scores(const u32x4 *klds, const u32x4 *qf,
                                        int lane, f32x4 s[2]) {
   const int g = lane >> 4, j = lane & 15;
 #pragma unroll
@@ -259,7 +273,7 @@ __device__ __forceinline__ void scores(const uint16_t (*klds)[kKPad<D>], const u
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
-      u32x4 kf = ld16(&klds[key][32 * ks + 8 * g]);
+      u32x4 kf = klds[kslot<D>(key, 4 * ks + g)];
       acc = mfma16(kf, qf[ks], acc);
     }
     s[mt] = acc;
@@ -282,7 +296,9 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, int r, int h, bool ok,
 template <int D>
 __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
   constexpr int NPF = FDL_ATTN_NPF;  // tiles in flight per key group
-  __shared__ uint16_t klds[2][2][KT][kKPad<D>];
+  // K tiles (swizzled chunks); 8 chunks more per tile make room for the
+  // merge scratch that reuses them.
+  __shared__ u32x4 klds[2][2][KT * D / 8 + 8];
   __shared__ uint16_t vlds[2][2][KT][kVPad<D>];
 
   int u = blockIdx.x;
@@ -358,7 +374,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
 
   // Combine the two key groups (group 1's state through LDS, reusing the tiles).
   lds_barrier();
-  float *mo = reinterpret_cast<float *>(&klds[0][0][0][0]);  // [4 row groups][16 rows][D]
+  float *mo = reinterpret_cast<float *>(&klds[0][0][0]);  // [4 row groups][16 rows][D]
   float *mml = mo + 64 * D;                                   // [64 rows][2]
   static_assert((64 * D + 128) * 4 <= (int)sizeof(klds), "merge scratch");
   const int rl = wr * 16 + j;
@@ -468,7 +484,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, AttnPlan p)
 template <int D>
 __global__ __launch_bounds__(256) void attn_mass_kernel(AttnArgs a, AttnPlan p) {
   constexpr int MAXK = 32 * KT;  // keys per chunk (bounded by the host plan)
-  __shared__ uint16_t klds[2][KT][kKPad<D>];
+  __shared__ u32x4 klds[2][KT * D / 8];
   __shared__ float wsum[4][KT];
   __shared__ float macc[MAXK];
 
@@ -637,20 +653,6 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnArgs a, AttnPlan p
 // tiles) in registers and, once the workgroup has combined the waves' maxima
 // and normalisers, sums exp2(s - LSE) over its 16 rows for each of its keys.
 constexpr int kRowWaves = 8;
-
-// Slot (in 16-byte chunks) of chunk ch of key row key in a wave's K tile.
-// One MFMA operand read gathers one chunk of the 16 keys 8a + b + 4m (a, b
-// < 4): the chunk index is XORed with the key bits that vary over that set,
-// so the 16 reads land in distinct banks.  D = 128: bits 0, 1, 3, 4 of the
-// key; D = 64 (two rows per 256-byte bank line, told apart by bit 0): bits 1,
-// 3, 4.  A row's chunks stay a permutation of its slots, so the coalesced
-// writes are conflict-free too.
-template <int D>
-__device__ __forceinline__ int kslot(int key, int ch) {
-  static_assert(D == 64 || D == 128, "head size");
-  if constexpr (D == 128) return key * 16 + (ch ^ ((key & 3) | ((key >> 1) & 12)));
-  else return key * 8 + (ch ^ (((key >> 1) & 1) | ((key >> 2) & 6)));
-}
 
 // LDS of one row-group workgroup.
 template <int D>
