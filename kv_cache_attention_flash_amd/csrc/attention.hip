@@ -962,10 +962,15 @@ __device__ __forceinline__ void attn_rows_mass_body(const AttnArgs &a, const Att
       const int hr = min(hr0 + 8 * i, n - 1);
       v[i] = mp[(size_t)hr * a.mass_stride];
     }
+    if (nrg == p.rgroups) {  // every row group of the sequence exists: no per-entry test
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int hr = hr0 + 8 * i;
-      sum += (hr < n && hr % p.rgroups < nrg && jj < L) ? v[i] : 0.f;
+      for (int i = 0; i < 16; ++i) sum += (hr0 + 8 * i < n && jj < L) ? v[i] : 0.f;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int hr = hr0 + 8 * i;
+        sum += (hr < n && hr % p.rgroups < nrg && jj < L) ? v[i] : 0.f;
+      }
     }
   }
   part[grp][k] = sum;
