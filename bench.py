@@ -4,23 +4,26 @@
 One step = flash_cache_step (QKV projection + rotary embedding + paged K/V write)
 -> scheduled_attention (with the attention mass when the tracking set is
 re-selected) -> track_topb (next tracking set) [-> verify_accept on the two-view
-workload].  Default workload: the LLaDA-8B-class single-layer decode step,
-hidden 4096, 32 heads x 128, batch 1, cache 768 (256 prompt + 512 generated),
-64 active rows (window of 32 + 32 tracked), rotary base 5e5, tracking budget 32.
-``--workload`` selects the other shapes of the same layer (batch 32 ragged,
-two-view batch 8, the 32-layer batch-16 stack at cache 4096).
+workload].  Default workload: the 32-layer stack of the LLaDA-8B-class layer
+(hidden 4096, 32 heads x 128, rotary base 5e5) at batch 16 with a 4096-slot
+cache per sequence, 64 active rows per sequence (window of 32 + 32 tracked),
+the tracking set re-selected in every layer: the largest workload, and the one
+that streams the whole ~34 GB cache plus 32 weights from HBM every step.
+``--workload`` selects the single-layer shapes (batch 1, batch 32 ragged,
+two-view batch 8); they are also parity cases of the tests.
 
 Inputs are resident in HBM before timing.  A single-layer step's working set
-(~116 MB at batch 1) would fit in the 256 MB last-level cache, so the benchmark
-rotates over independent copies of weights, hidden states and cache (a model's
-32 layers never share a weight either) until the rotation exceeds ~560 MB:
-every step streams its weight and cache from HBM.
+(~116 MB at batch 1) would fit in the 256 MB last-level cache, so those
+workloads rotate over independent copies of weights, hidden states and cache
+until the rotation exceeds ~560 MB: every step streams its weight and cache
+from HBM.  The stack needs no copies (38 GB per step).
 
 Prints ONE JSON line (N = 1): metric, value (active query tokens/s per layer),
-ms_per_step, the roofline of the call that takes longer (duration from HIP
-events recorded around each launch on its stream inside the timed loop) and of
-the other call, and the CPU oracle's throughput on a bounded sample of the same
-workload.
+ms_per_step (all layers of a step), the roofline of the call that takes longer
+(duration from HIP events recorded around each launch on its stream inside the
+timed loop) and of the other call, the whole step's HBM fraction against its
+algorithmic bytes, and the CPU oracle's throughput on a bounded sample of the
+same workload.
 """
 
 from __future__ import annotations
@@ -64,10 +67,10 @@ def log(msg):
 
 def flash_cache_bytes(wl) -> int:
     """Algorithmic HBM bytes of one flash_cache_step launch: the weight once,
-    the active rows' hidden states, their Q/K/V bf16 outputs, and the per-row
-    metadata (position, slot, slot mapping)."""
+    the active rows' hidden states and their written K and V (bf16).  Q's write
+    is half of the Q round trip, which is not algorithmic (q_round_trip_bytes)."""
     hd = wl.num_heads * wl.head_dim
-    return 2 * 3 * hd * wl.hid + wl.rows * (2 * wl.hid + 2 * 3 * hd + 4 + 4 + 8)
+    return 2 * 3 * hd * wl.hid + wl.rows * (2 * wl.hid + 4 * hd)
 
 
 def flash_cache_flops(wl) -> int:
@@ -76,11 +79,24 @@ def flash_cache_flops(wl) -> int:
 
 def attention_bytes(wl) -> int:
     """Algorithmic bytes of scheduled_attention: every cached K and V slot of a
-    sequence once per head, Q in (bf16), O out (fp32), the mass out (fp32)."""
+    sequence once per head, O out (fp32), the mass out (fp32) when asked.  Q's
+    read is the other half of the Q round trip (not algorithmic)."""
     hd = wl.num_heads * wl.head_dim
     kv = int(sum(int(v) for v in wl.kv_len)) * hd * 2 * 2
     mass = 4 * int(sum(int(v) for v in wl.kv_len)) if wl.topb else 0
-    return kv + wl.rows * hd * (2 + 4) + mass
+    return kv + wl.rows * hd * 4 + mass
+
+
+def q_round_trip_bytes(wl) -> int:
+    """Q written by flash_cache_step and read back by scheduled_attention (bf16):
+    moved because the two are separate calls, not part of the algorithmic bytes."""
+    return 4 * wl.rows * wl.num_heads * wl.head_dim
+
+
+def step_bytes(wl) -> int:
+    """Algorithmic bytes of one layer's step: W + R (2 hid + 4 HD + 4 HD) +
+    4 HD sum(L) + 4 sum(L) [mass] -- the projection's and the attention's."""
+    return flash_cache_bytes(wl) + attention_bytes(wl)
 
 
 def visible_pairs(wl) -> int:
@@ -537,7 +553,7 @@ def main():
                     help="timed steps (default 200; 5 for the 32-layer stack)")
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps (default 20; 1 for the 32-layer stack)")
-    ap.add_argument("--workload", default="llada8b_b1_l768", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="llada8b_stack32_b16_l4096", choices=sorted(WORKLOADS))
     ap.add_argument("--copies", type=int, default=0,
                     help="resident copies rotated per step (0: enough to exceed ~560 MB)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
@@ -691,7 +707,7 @@ def main():
     dominant, other = (rf_fc, rf_att) if fcs_ms >= att_ms else (rf_att, rf_fc)
     if args.fused:
         # one launch: its algorithmic bytes are both calls' (HBM-bound at this AI)
-        nb_f = flash_cache_bytes(wl) + attention_bytes(wl)
+        nb_f = step_bytes(wl)
         ach = nb_f / (fcs_ms / 1e3) / 1e9
         dominant = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
@@ -725,7 +741,14 @@ def main():
         log(f"cpu oracle {cpu['value']:.1f} tokens/s/layer on {cpu['cores']} threads; parity {parity}")
 
     hd = wl.num_heads * wl.head_dim
-    sb = flash_cache_bytes(wl) + attention_bytes(wl)
+    sb = step_bytes(wl)
+    layer_s = ms_per_step / layers_per_step / 1e3
+    step_ach = sb / layer_s / 1e9
+    step_roof = {"bound": "hbm", "achieved": round(step_ach, 1), "peak": HBM_PEAK_GBS,
+                 "unit": "GB/s", "frac": round(step_ach / HBM_PEAK_GBS, 4),
+                 "algorithmic_bytes": sb, "layer_us": round(layer_s * 1e6, 2),
+                 "what": "one layer's whole step (every call of it) against its algorithmic "
+                         "bytes: W + R(2 hid + 4 HD + 4 HD) + 4 HD sum(L) + 4 sum(L)"}
     tail = (" + scheduled_attention(+mass) + track_topb" if wl.topb else " + scheduled_attention")
     if args.unfused:
         tail += " [ablation: flash_cache_step_unfused, three launches with HBM intermediates]"
@@ -751,13 +774,18 @@ def main():
                               "layer_total": round(ms_per_step * 1e3 / layers_per_step, 2),
                               "layer_total_with_call_events": round(
                                   ms_per_step_instr * 1e3 / layers_per_step, 2)},
-        "step_hbm_fraction": round(sb / (ms_per_step / layers_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
-                                   4),
+        "step_roofline": step_roof,
+        "step_hbm_fraction": step_roof["frac"],
         "step_algorithmic_bytes": sb,
+        "non_algorithmic_bytes": {"q_round_trip": q_round_trip_bytes(wl)},
         "qkv_dims": [wl.rows, wl.hid, 3 * hd],
         "parity": parity,
     }
     print(json.dumps(line), flush=True)
+    # Release the resident tensors while the runtime is whole, in a fixed order.
+    torch.cuda.synchronize()
+    units = st = None
+    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

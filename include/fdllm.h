@@ -31,8 +31,10 @@
  *     decreases and ends at most at num_rows; active rows have positions >= 0
  *     and logical slots inside their block-table row; every block id a row
  *     writes or a visible slot reads lies in [0, num_blocks); lengths are
- *     >= 0; no physical slot is written by two rows.  A violation returns
- *     FDL_EINVAL with nothing launched (a failed copy, FDL_EHIP).
+ *     >= 0; no physical slot is written by two rows; no sequence has more
+ *     rows than max_rows_per_seq; two-view descriptors are non-negative and
+ *     meet their stated inequalities.  A violation returns FDL_EINVAL with
+ *     nothing launched (a failed copy, FDL_EHIP).
  *
  * Supported shapes: head_dim in {64, 128}; block_size in {32, 64, 128, 256};
  * hidden a multiple of 128 and at most 32768; num_heads * head_dim <= 16384;
@@ -215,16 +217,21 @@ int verify_accept(const int32_t *draft_tok, const int32_t *mask_tok,
  * the mass, as one persistent launch.  Arguments as for those two calls (the
  * attention reads the q_out this call writes); mass must not be NULL.
  * Results are bitwise those of the two separate calls: each phase runs the
- * same workgroup code.  The launch is cooperative (every workgroup resident):
- * the attention phase starts when every projection workgroup has finished,
- * the mass phase when every attention workgroup has; hand-offs between
- * workgroups use device-scope release/acquire on counters in the workspace.
+ * same workgroup code.  Workgroups take items from a ticket counter in phase
+ * order (projection, attention, mass); an attention item starts once every
+ * projection item has finished, a mass item once every attention item has.
+ * An item only waits for items with lower tickets, held by running
+ * workgroups, so the ordinary launch needs no co-residency guarantee.
+ * Hand-offs between workgroups use device-scope release/acquire on counters
+ * in the workspace.
  *   workspace  fdl_fused_step_workspace_bytes(...) bytes.  Its first 256
- *              bytes hold the counters and an error word: they must be zero
- *              before the first call (for example a zero-filled allocation);
- *              each call leaves the counters zero.  The error word (int32 at
- *              byte 12) becomes 1 if a phase wait ever timed out, which a
- *              cooperative launch rules out; results are then invalid.  Calls
+ *              bytes hold the counters, the ticket and an error word: they
+ *              must be zero before the first call (for example a zero-filled
+ *              allocation, made in stream order before the call); each call
+ *              leaves the counters zero.  The error word (int32 at byte 12)
+ *              becomes 1 if a phase wait ever timed out (it never should: every
+ *              wait is for a running workgroup); results are then invalid,
+ *              and the word stays set until the caller clears it.  Calls
  *              sharing a workspace must not run at the same time.
  * Supported: the shapes whose separate calls take a one-launch projection (no
  * split reduction) and the row-group attention path (few sequences x heads,

@@ -24,6 +24,8 @@ Memory-Efficient Diffusion LLMs" (ai4snews.wisdomeyes.cn summary), paras 1-3.
 
 from __future__ import annotations
 
+import atexit
+import contextlib
 import ctypes
 import dataclasses
 from typing import Optional
@@ -38,7 +40,7 @@ __all__ = ["PagedKVCache", "flash_cache_step", "flash_cache_step_unfused", "sche
            "flash_cache_workspace_bytes", "flash_cache_unfused_workspace_bytes", "DecodeStep",
            "decode_plan", "gather_hidden", "DecodeLoop", "lm_head_confidence",
            "lm_head_workspace_bytes", "flash_cache_attention_step", "fused_step_workspace_bytes",
-           "FdlError", "load"]
+           "fused_step_error", "FdlError", "load"]
 
 
 def load():
@@ -62,17 +64,46 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: Optional[int] = 
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
 
 
+def _on_stream(stream_handle: int, device):
+    """Context in which torch allocates (and fills) in the order of the launch
+    stream: memory handed to a call on that stream is then free with respect to
+    it, and a fill (zeros) is complete before the call's kernels start.  A
+    no-op when the launch stream is torch's current stream."""
+    if torch.cuda.current_stream(device).cuda_stream == stream_handle:
+        return contextlib.nullcontext()
+    return torch.cuda.stream(torch.cuda.ExternalStream(stream_handle, device=device))
+
+
 _FC_WS = {}
 
 
 def _flash_cache_workspace(device, stream_handle: int, nbytes: int):
-    """Split-reduction scratch, one per (device, stream)."""
+    """Split-reduction scratch, one per (device, stream), allocated in the
+    stream's order."""
     key = (device.index if device.index is not None else torch.cuda.current_device(), stream_handle)
     ws = _FC_WS.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=device)
+        with _on_stream(stream_handle, device):
+            ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=device)
         _FC_WS[key] = ws
     return ws
+
+
+def _release_cached_workspaces():
+    """At interpreter exit: wait for the device, then drop the cached
+    workspaces while the HIP runtime is still whole, so that their memory is
+    returned in a fixed order rather than during interpreter teardown."""
+    if not (_FC_WS or _FUSED_WS):
+        return
+    try:
+        torch.cuda.synchronize()
+    except Exception:  # pragma: no cover - nothing more to do at exit
+        pass
+    _FC_WS.clear()
+    _FUSED_WS.clear()
+
+
+atexit.register(_release_cached_workspaces)
 
 
 def flash_cache_workspace_bytes(num_rows, hidden, num_heads, head_dim) -> int:
@@ -136,14 +167,15 @@ def _flash_cache_call(unfused, cache, x, w_qkv, cu_rows, positions, slots, rope_
     if positions.numel() != r or slots.numel() != r:
         raise ValueError("positions/slots must have one entry per row")
     batch = cu_rows.numel() - 1
-    if q_out is None:
-        q_out = torch.empty((r, h, d), dtype=torch.bfloat16, device=x.device)
+    sh = _stream(stream, x.device)
+    with _on_stream(sh, x.device):
+        if q_out is None:
+            q_out = torch.empty((r, h, d), dtype=torch.bfloat16, device=x.device)
+        if slot_mapping_out is None:
+            slot_mapping_out = torch.empty((r,), dtype=torch.int64, device=x.device)
     _need(q_out, "q_out", torch.bfloat16, 3)
-    if slot_mapping_out is None:
-        slot_mapping_out = torch.empty((r,), dtype=torch.int64, device=x.device)
     _need(slot_mapping_out, "slot_mapping_out", torch.int64, 1)
     cs = cache.struct()
-    sh = _stream(stream, x.device)
     if unfused:
         need = flash_cache_unfused_workspace_bytes(r, hid, h, d)
         fn, name = lib.flash_cache_step_unfused, "flash_cache_step_unfused"
@@ -203,27 +235,31 @@ def scheduled_attention(cache: PagedKVCache, q, cu_rows, kv_len, max_kv_len, max
         if tuple(views.shape) != (batch, 3):
             raise ValueError("views must be int32 [batch, 3]")
     r = q.shape[0]
-    if out is None:
-        out = torch.empty((r, cache.num_heads, cache.head_dim), dtype=torch.float32,
-                          device=q.device)
-    _need(out, "out", torch.float32, 3)
-    if want_mass or mass is not None:
-        if mass_stride is None:
-            mass_stride = mass.shape[1] if mass is not None else int(max_kv_len)
-        if mass is None:
+    sh = _stream(stream, q.device)
+    with _on_stream(sh, q.device):
+        if out is None:
+            out = torch.empty((r, cache.num_heads, cache.head_dim), dtype=torch.float32,
+                              device=q.device)
+        if (want_mass or mass is not None) and mass is None:
+            if mass_stride is None:
+                mass_stride = int(max_kv_len)
             mass = torch.empty((batch, mass_stride), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, 3)
+    if mass is not None:
+        if mass_stride is None:
+            mass_stride = mass.shape[1]
         _need(mass, "mass", torch.float32, 2)
     ms = int(mass_stride) if mass is not None else 0
     need = attention_workspace_bytes(batch, r, cache.num_heads, cache.head_dim, int(max_kv_len),
                                      int(max_rows_per_seq), ms)
     if workspace is None or workspace.numel() < need:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+        with _on_stream(sh, q.device):
+            workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
     cs = cache.struct()
     st = lib.scheduled_attention(ctypes.byref(cs), q.data_ptr(), batch, r, cu_rows.data_ptr(),
                                  kv_len.data_ptr(), int(max_kv_len), int(max_rows_per_seq),
                                  _ptr(views), float(softmax_scale), out.data_ptr(),
-                                 _ptr(mass), ms, workspace.data_ptr(), workspace.numel(),
-                                 _stream(stream, q.device))
+                                 _ptr(mass), ms, workspace.data_ptr(), workspace.numel(), sh)
     _lib.check("scheduled_attention", st)
     return out, mass
 
@@ -236,11 +272,13 @@ def track_topb(mass, kv_len, topb, out=None, stream=None):
     batch = mass.shape[0]
     if kv_len.numel() != batch:
         raise ValueError("kv_len must have one entry per sequence")
+    sh = _stream(stream, mass.device)
     if out is None:
-        out = torch.empty((batch, int(topb)), dtype=torch.int32, device=mass.device)
+        with _on_stream(sh, mass.device):
+            out = torch.empty((batch, int(topb)), dtype=torch.int32, device=mass.device)
     _need(out, "out", torch.int32, 2)
     st = lib.track_topb(mass.data_ptr(), mass.shape[1], kv_len.data_ptr(), batch, int(topb),
-                        out.data_ptr(), _stream(stream, mass.device))
+                        out.data_ptr(), sh)
     _lib.check("track_topb", st)
     return out
 
@@ -254,12 +292,13 @@ def verify_accept(draft_tok, mask_tok, conf, threshold, out=None, stream=None):
     if draft_tok.shape != mask_tok.shape or draft_tok.shape != conf.shape:
         raise ValueError("draft_tok, mask_tok and conf must have the same shape")
     batch, window = draft_tok.shape
+    sh = _stream(stream, draft_tok.device)
     if out is None:
-        out = torch.empty((batch,), dtype=torch.int32, device=draft_tok.device)
+        with _on_stream(sh, draft_tok.device):
+            out = torch.empty((batch,), dtype=torch.int32, device=draft_tok.device)
     _need(out, "out", torch.int32, 1)
     st = lib.verify_accept(draft_tok.data_ptr(), mask_tok.data_ptr(), conf.data_ptr(), batch,
-                           window, ctypes.c_float(float(threshold)), out.data_ptr(),
-                           _stream(stream, draft_tok.device))
+                           window, ctypes.c_float(float(threshold)), out.data_ptr(), sh)
     _lib.check("verify_accept", st)
     return out
 
@@ -271,7 +310,9 @@ class DecodeStep:
 
     The ctypes argument lists are built once, so ``run()`` only issues the three
     asynchronous library calls on the given stream (suitable for timing loops
-    and HIP-graph capture)."""
+    and HIP-graph capture).  The buffers are allocated on torch's current
+    stream at construction; a caller that runs the step on another stream
+    keeps the object alive until that stream is done with it."""
 
     def __init__(self, cache: PagedKVCache, x, w_qkv, cu_rows, positions, slots, kv_len,
                  rope_base, max_kv_len, max_rows_per_seq, views=None, topb=0,
@@ -324,6 +365,8 @@ class DecodeStep:
                                                   int(max_rows_per_seq), self.mass_stride)
             self.fused_workspace = torch.zeros((max(fus_need, 256),), dtype=torch.uint8,
                                                device=dev)
+            # run() may use another stream: the fill must be complete first
+            torch.cuda.current_stream(dev).synchronize()
             self._fus = (ctypes.byref(self.cs), x.data_ptr(), x.shape[1], w_qkv.data_ptr(),
                          self.batch, r, cu_rows.data_ptr(), positions.data_ptr(),
                          slots.data_ptr(), float(rope_base), self.q.data_ptr(),
@@ -349,6 +392,13 @@ class DecodeStep:
     def run_fused(self, stream: int):
         _lib.check("flash_cache_attention_step",
                    self.lib.flash_cache_attention_step(*self._fus, stream))
+
+    def fused_error(self) -> int:
+        """The single-launch step's error word after the runs so far (waits
+        for the device); 0 when every wait completed."""
+        torch.cuda.synchronize(self.x.device)
+        return int(self.fused_workspace[FUSED_ERROR_OFFSET:FUSED_ERROR_OFFSET + 4]
+                   .view(torch.int32).item())
 
     def run_attention(self, stream: int):
         _lib.check("scheduled_attention", self.lib.scheduled_attention(*self._att, stream))
@@ -397,14 +447,16 @@ def decode_plan(kv_len, frontier, tracked, accept_len, step, window_len, block_s
             raise ValueError("accept_len must have one entry per sequence")
     dev = kv_len.device
     cap = batch * (int(window_len) + topb)
-    if cu_rows_out is None:
-        cu_rows_out = torch.empty((batch + 1,), dtype=torch.int32, device=dev)
-    if positions_out is None:
-        positions_out = torch.empty((max(cap, 1),), dtype=torch.int32, device=dev)
-    if slots_out is None:
-        slots_out = torch.empty((max(cap, 1),), dtype=torch.int32, device=dev)
-    if stage_out is None:
-        stage_out = torch.empty((max(batch, 1),), dtype=torch.int32, device=dev)
+    sh = _stream(stream, dev)
+    with _on_stream(sh, dev):
+        if cu_rows_out is None:
+            cu_rows_out = torch.empty((batch + 1,), dtype=torch.int32, device=dev)
+        if positions_out is None:
+            positions_out = torch.empty((max(cap, 1),), dtype=torch.int32, device=dev)
+        if slots_out is None:
+            slots_out = torch.empty((max(cap, 1),), dtype=torch.int32, device=dev)
+        if stage_out is None:
+            stage_out = torch.empty((max(batch, 1),), dtype=torch.int32, device=dev)
     for t, n in ((cu_rows_out, "cu_rows_out"), (positions_out, "positions_out"),
                  (slots_out, "slots_out"), (stage_out, "stage_out")):
         _need(t, n, torch.int32, 1)
@@ -413,8 +465,7 @@ def decode_plan(kv_len, frontier, tracked, accept_len, step, window_len, block_s
     st = lib.decode_plan(batch, kv_len.data_ptr(), int(window_len), int(block_size),
                          int(refresh_period), int(step), _ptr(tracked), topb, _ptr(accept_len),
                          frontier.data_ptr(), cu_rows_out.data_ptr(), positions_out.data_ptr(),
-                         slots_out.data_ptr(), stage_out.data_ptr(), positions_out.numel(),
-                         _stream(stream, dev))
+                         slots_out.data_ptr(), stage_out.data_ptr(), positions_out.numel(), sh)
     _lib.check("decode_plan", st)
     return cu_rows_out, positions_out, slots_out, stage_out
 
@@ -436,15 +487,16 @@ def gather_hidden(cu_rows, positions, frontier, hidden_committed, hidden_masked,
     if cu_rows.numel() != batch + 1 or frontier.numel() != batch:
         raise ValueError("cu_rows/frontier do not match the tables' batch")
     cap = positions.numel()
+    sh = _stream(stream, positions.device)
     if x_out is None:
-        x_out = torch.empty((cap, hid), dtype=torch.bfloat16, device=positions.device)
+        with _on_stream(sh, positions.device):
+            x_out = torch.empty((cap, hid), dtype=torch.bfloat16, device=positions.device)
     _need(x_out, "x_out", torch.bfloat16, 2)
     if x_out.shape[1] != hid or x_out.shape[0] < cap:
         raise ValueError(f"x_out must be [>= {cap}, {hid}]")
     st = lib.gather_hidden(batch, cap, cu_rows.data_ptr(), positions.data_ptr(),
                            frontier.data_ptr(), hidden_committed.data_ptr(),
-                           hidden_masked.data_ptr(), max_len, hid, x_out.data_ptr(),
-                           _stream(stream, positions.device))
+                           hidden_masked.data_ptr(), max_len, hid, x_out.data_ptr(), sh)
     _lib.check("gather_hidden", st)
     return x_out
 
@@ -582,20 +634,23 @@ def lm_head_confidence(hidden_states, w_lm, token_out=None, conf_out=None, works
     if w_lm.shape[1] != hid:
         raise ValueError(f"w_lm must be [vocab, {hid}], got {tuple(w_lm.shape)}")
     dev = hidden_states.device
-    if token_out is None:
-        token_out = torch.empty((rows,), dtype=torch.int32, device=dev)
-    if conf_out is None:
-        conf_out = torch.empty((rows,), dtype=torch.float32, device=dev)
+    sh = _stream(stream, dev)
+    with _on_stream(sh, dev):
+        if token_out is None:
+            token_out = torch.empty((rows,), dtype=torch.int32, device=dev)
+        if conf_out is None:
+            conf_out = torch.empty((rows,), dtype=torch.float32, device=dev)
     _need(token_out, "token_out", torch.int32, 1)
     _need(conf_out, "conf_out", torch.float32, 1)
     if token_out.numel() < rows or conf_out.numel() < rows:
         raise ValueError("token_out/conf_out need one entry per row")
     need = lm_head_workspace_bytes(rows, vocab)
     if workspace is None or workspace.numel() < need:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+        with _on_stream(sh, dev):
+            workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     st = lib.lm_head_confidence(hidden_states.data_ptr(), w_lm.data_ptr(), rows, vocab, hid,
                                 token_out.data_ptr(), conf_out.data_ptr(),
-                                workspace.data_ptr(), workspace.numel(), _stream(stream, dev))
+                                workspace.data_ptr(), workspace.numel(), sh)
     _lib.check("lm_head_confidence", st)
     return token_out, conf_out
 
@@ -611,24 +666,41 @@ _FUSED_WS = {}
 
 
 def _fused_workspace(device, stream_handle: int, nbytes: int):
-    """Zero-filled workspace per (device, stream): its first 256 bytes are the
-    single-launch step's counters, which every call leaves at zero."""
+    """Zero-filled workspace per (device, stream), allocated and filled in the
+    stream's order (so the fill is done before the call's kernel starts): its
+    first 256 bytes are the single-launch step's counters, which every call
+    leaves at zero."""
     key = (device.index if device.index is not None else torch.cuda.current_device(), stream_handle)
     ws = _FUSED_WS.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros((max(nbytes, 256),), dtype=torch.uint8, device=device)
+        with _on_stream(stream_handle, device):
+            ws = torch.zeros((max(nbytes, 256),), dtype=torch.uint8, device=device)
         _FUSED_WS[key] = ws
     return ws
+
+
+FUSED_ERROR_OFFSET = 12  # byte offset of the single-launch step's error word
+
+
+def fused_step_error(workspace: torch.Tensor, stream=None) -> int:
+    """The single-launch step's error word (1 if a phase wait timed out; the
+    results of that call are then invalid).  Synchronises the stream."""
+    sh = _stream(stream, workspace.device)
+    with _on_stream(sh, workspace.device):
+        word = workspace[FUSED_ERROR_OFFSET:FUSED_ERROR_OFFSET + 4].view(torch.int32).item()
+    return int(word)
 
 
 def flash_cache_attention_step(cache: PagedKVCache, x, w_qkv, cu_rows, positions, slots,
                                rope_base, kv_len, max_kv_len, max_rows_per_seq, views=None,
                                softmax_scale=0.0, mass_stride=None, q_out=None,
                                slot_mapping_out=None, out=None, mass=None, workspace=None,
-                               stream=None):
+                               stream=None, check=True):
     """flash_cache_step then scheduled_attention with the mass, as one launch
     (bitwise the same results).  ``workspace``, if given, must be zero-filled
-    before its first use.  Returns (q_out, slot_mapping, out, mass)."""
+    before its first use, in the launch stream's order.  With ``check`` the
+    call waits for its stream and raises if the kernel reported a timed-out
+    wait.  Returns (q_out, slot_mapping, out, mass)."""
     lib = _lib.load()
     _need(x, "x", torch.bfloat16, 2)
     _need(w_qkv, "w_qkv", torch.bfloat16, 2)
@@ -647,21 +719,22 @@ def flash_cache_attention_step(cache: PagedKVCache, x, w_qkv, cu_rows, positions
     if views is not None:
         _need(views, "views", torch.int32, 2)
     dev = x.device
-    if q_out is None:
-        q_out = torch.empty((r, h, d), dtype=torch.bfloat16, device=dev)
-    if slot_mapping_out is None:
-        slot_mapping_out = torch.empty((r,), dtype=torch.int64, device=dev)
-    if out is None:
-        out = torch.empty((r, h, d), dtype=torch.float32, device=dev)
+    sh = _stream(stream, dev)
     if mass_stride is None:
         mass_stride = mass.shape[1] if mass is not None else int(max_kv_len)
-    if mass is None:
-        mass = torch.empty((batch, int(mass_stride)), dtype=torch.float32, device=dev)
+    with _on_stream(sh, dev):
+        if q_out is None:
+            q_out = torch.empty((r, h, d), dtype=torch.bfloat16, device=dev)
+        if slot_mapping_out is None:
+            slot_mapping_out = torch.empty((r,), dtype=torch.int64, device=dev)
+        if out is None:
+            out = torch.empty((r, h, d), dtype=torch.float32, device=dev)
+        if mass is None:
+            mass = torch.empty((batch, int(mass_stride)), dtype=torch.float32, device=dev)
     _need(q_out, "q_out", torch.bfloat16, 3)
     _need(slot_mapping_out, "slot_mapping_out", torch.int64, 1)
     _need(out, "out", torch.float32, 3)
     _need(mass, "mass", torch.float32, 2)
-    sh = _stream(stream, dev)
     need = fused_step_workspace_bytes(batch, r, h, d, int(max_kv_len), int(max_rows_per_seq),
                                       int(mass_stride))
     if workspace is None:
@@ -674,4 +747,6 @@ def flash_cache_attention_step(cache: PagedKVCache, x, w_qkv, cu_rows, positions
         _ptr(views), float(softmax_scale), out.data_ptr(), mass.data_ptr(), int(mass_stride),
         workspace.data_ptr(), workspace.numel(), sh)
     _lib.check("flash_cache_attention_step", st)
+    if check and fused_step_error(workspace, sh):
+        raise RuntimeError("flash_cache_attention_step: a phase wait timed out (results invalid)")
     return q_out, slot_mapping_out, out, mass

@@ -100,20 +100,31 @@ int debug_check_rows(const fdl_kv_cache *c, int batch, int num_rows, const int32
   return FDL_OK;
 }
 
-// scheduled_attention's index arrays: row offsets, non-negative lengths, and
-// the block ids of every page a visible slot lies in.
+// scheduled_attention's index arrays: row offsets, each sequence's row count
+// within max_rows_per_seq, non-negative lengths, the block ids of every page a
+// visible slot lies in, and the two-view descriptors' stated inequalities
+// (window_start + window_len <= draft_slot_start, draft_slot_start +
+// window_len <= kv_len, all non-negative).
 int debug_check_attention(const fdl_kv_cache *c, int batch, int num_rows,
                           const int32_t *cu_rows, const int32_t *kv_len, int max_kv_len,
-                          hipStream_t s) {
+                          int max_rows_per_seq, const fdl_two_view *views, hipStream_t s) {
   if (hipStreamSynchronize(s) != hipSuccess) return FDL_EHIP;
-  std::vector<int32_t> cu, kl, bt;
+  std::vector<int32_t> cu, kl, bt, vw;
   if (!fetch_i32(cu, cu_rows, (size_t)batch + 1) || !fetch_i32(kl, kv_len, batch) ||
       !fetch_i32(bt, c->block_table, (size_t)batch * c->max_blocks_per_seq))
+    return FDL_EHIP;
+  if (views && !fetch_i32(vw, reinterpret_cast<const int32_t *>(views), (size_t)batch * 3))
     return FDL_EHIP;
   int st = debug_check_cu(cu, batch, num_rows);
   if (st) return st;
   for (int b = 0; b < batch; ++b) {
+    if (cu[b + 1] - cu[b] > max_rows_per_seq) return FDL_EINVAL;
     if (kl[b] < 0) return FDL_EINVAL;
+    if (views) {
+      const int w0 = vw[3 * b], wl = vw[3 * b + 1], d0 = vw[3 * b + 2];
+      if (w0 < 0 || wl < 0 || d0 < 0) return FDL_EINVAL;
+      if (wl > 0 && ((long)w0 + wl > d0 || (long)d0 + wl > kl[b])) return FDL_EINVAL;
+    }
     const int L = kl[b] < max_kv_len ? kl[b] : max_kv_len;
     for (int p = 0; p < (L + c->block_size - 1) / c->block_size; ++p) {
       const int blk = bt[(size_t)b * c->max_blocks_per_seq + p];
@@ -251,7 +262,7 @@ int attn_args(const fdl_kv_cache *cache, const void *q, int32_t batch, int32_t n
   return FDL_OK;
 }
 
-constexpr size_t kFusedSyncBytes = 256;  // 4 counters / flags, padded
+constexpr size_t kFusedSyncBytes = 256;  // counters, ticket and error word, padded
 
 }  // namespace
 
@@ -314,8 +325,9 @@ int scheduled_attention(const fdl_kv_cache *cache, const void *q, int32_t batch,
   if (st || empty == 1) return st;
   if (plan.bytes > workspace_bytes || (plan.bytes && !workspace)) return FDL_EWORKSPACE;
   if (empty) return FDL_OK;
-  if (debug_mode() && (st = debug_check_attention(cache, batch, num_rows, cu_rows, kv_len,
-                                                  max_kv_len, static_cast<hipStream_t>(stream))))
+  if (debug_mode() &&
+      (st = debug_check_attention(cache, batch, num_rows, cu_rows, kv_len, max_kv_len,
+                                  max_rows_per_seq, views, static_cast<hipStream_t>(stream))))
     return st;
   a.ws = static_cast<char *>(workspace);
   return hip_status(fdl::launch_attention(a, plan, static_cast<hipStream_t>(stream)));
@@ -358,7 +370,8 @@ int flash_cache_attention_step(const fdl_kv_cache *cache, const void *x, int32_t
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (!empty_fc && (st = debug_check_rows(cache, batch, num_rows, cu_rows, positions, slots, s)))
       return st;
-    if ((st = debug_check_attention(cache, batch, num_rows, cu_rows, kv_len, max_kv_len, s)))
+    if ((st = debug_check_attention(cache, batch, num_rows, cu_rows, kv_len, max_kv_len,
+                                    max_rows_per_seq, views, s)))
       return st;
   }
   if (empty_fc) {

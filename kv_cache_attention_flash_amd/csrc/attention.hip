@@ -34,22 +34,9 @@ namespace fdl {
 
 namespace {
 
-constexpr int KT = 32;  // keys per tile
-#ifndef FDL_ATTN_NPF
-#define FDL_ATTN_NPF 2
-#endif
-#ifndef FDL_ATTN_MNPF
-#define FDL_ATTN_MNPF 2
-#endif
-#ifndef FDL_ATTN_ROWS_KLDS
-#define FDL_ATTN_ROWS_KLDS 1  // row-group path: K through a wave-private LDS tile
-#endif
-#ifndef FDL_ATTN_ROWS_BUF
-#define FDL_ATTN_ROWS_BUF 1  // row-group path: tiles read through range-checked buffer views
-#endif
-#if FDL_ATTN_ROWS_BUF && !FDL_ATTN_ROWS_KLDS
-#error "buffer-view tile loads use the coalesced K layout"
-#endif
+constexpr int KT = 32;   // keys per tile
+constexpr int kNpf = 2;  // split path: tiles in flight per key group (pass 1)
+constexpr int kMnpf = 2; // split path: K tiles in flight (mass pass)
 constexpr float kNegInf = -__builtin_huge_valf();
 
 struct SeqInfo {
@@ -295,7 +282,7 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, int r, int h, bool ok,
 // first), so two waves per SIMD hide each other's latency.
 template <int D>
 __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
-  constexpr int NPF = FDL_ATTN_NPF;  // tiles in flight per key group
+  constexpr int NPF = kNpf;  // tiles in flight per key group
   // K tiles (swizzled chunks); 8 chunks more per tile make room for the
   // merge scratch that reuses them.
   __shared__ u32x4 klds[2][2][KT * D / 8 + 8];
@@ -518,7 +505,7 @@ __global__ __launch_bounds__(256) void attn_mass_kernel(AttnArgs a, AttnPlan p) 
     const int r = si.r0 + (row_ok ? t : 0);
     const size_t rh = (size_t)r * a.c.H + h;
     const Vis vis = row_vis(si, t, row_ok);
-    constexpr int MNPF = FDL_ATTN_MNPF;  // K tiles in flight
+    constexpr int MNPF = kMnpf;  // K tiles in flight
     Tile<D> pf[MNPF];
 #pragma unroll
     for (int i = 0; i < MNPF; ++i)
@@ -657,9 +644,7 @@ constexpr int kRowWaves = 8;
 // LDS of one row-group workgroup.
 template <int D>
 struct RowsLds {
-#if FDL_ATTN_ROWS_KLDS
   u32x4 kbuf[kRowWaves][KT * D / 8];
-#endif
   uint16_t vbuf[kRowWaves][KT][kVPad<D>];
   int s_page[kMaxPages];
   float s_ml[kRowWaves][16][2];
@@ -716,7 +701,6 @@ __device__ __forceinline__ void attn_rows_body(const AttnArgs &a, const AttnPlan
   // Loads of the wave's kk-th tile.  Past the wave's last tile the same number
   // of load instructions is issued at one fixed 16-byte address (every lane
   // alike), so the count of loads in flight never depends on the data.
-#if FDL_ATTN_ROWS_BUF
   // Wave-uniform descriptors per tile: the tile's keys are one contiguous run
   // of a page; keys at or past the cached length (and every key of a padding
   // tile) lie outside the view and load as zeros, so V needs no masking and
@@ -737,36 +721,6 @@ __device__ __forceinline__ void attn_rows_body(const AttnArgs &a, const AttnPlan
 #pragma unroll
     for (int i = 0; i < VLD; ++i) st.v[i] = buffer_ld16(rv, (lane + 64 * i) * 16);
   };
-#else
-  auto issue = [&](Stage &st, int kk) {
-    const bool real = kk < n_w;
-    const int key0 = (w + kRowWaves * kk) * KT;
-    size_t base = 0;
-    if (real) {
-      const int page = s_page[key0 / a.c.bs];
-      base = (((size_t)page * a.c.H + h) * a.c.bs + (key0 % a.c.bs)) * D;
-    }
-#if FDL_ATTN_ROWS_KLDS
-    // A tile's keys are one contiguous run of its page: whole 128-byte lines
-    // per 8 lanes, the operand layout being formed in LDS.
-#pragma unroll
-    for (int i = 0; i < 2 * KS; ++i)
-      st.k[i] = ld16(a.c.k + (real ? base + (size_t)(lane + 64 * i) * 8 : (size_t)0));
-#else
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int key = 8 * (j >> 2) + 4 * mt + (j & 3);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        st.k[mt * KS + ks] =
-            ld16(a.c.k + (real ? base + (size_t)key * D + 32 * ks + 8 * g : (size_t)0));
-    }
-#endif
-#pragma unroll
-    for (int i = 0; i < VLD; ++i)
-      st.v[i] = ld16(a.c.v + (real ? base + (size_t)(lane + 64 * i) * 8 : (size_t)0));
-  };
-#endif
 
   f32x4 o[D / 16];
 #pragma unroll
@@ -784,39 +738,26 @@ __device__ __forceinline__ void attn_rows_body(const AttnArgs &a, const AttnPlan
       for (int e = 0; e < 8; ++e) xs[e] = kNegInf;
       return;
     }
-#if FDL_ATTN_ROWS_KLDS
     u32x4 *kb = L.kbuf[w];
 #pragma unroll
     for (int i = 0; i < 2 * KS; ++i) {
       const int c = lane + 64 * i;
       kb[kslot<D>(c / CH, c % CH)] = st.k[i];
     }
-#endif
     f32x4 s[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#if FDL_ATTN_ROWS_KLDS
       const int key = 8 * (j >> 2) + 4 * mt + (j & 3);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) acc = mfma16(kb[kslot<D>(key, 4 * ks + g)], qf[ks], acc);
-#else
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma16(st.k[mt * KS + ks], qf[ks], acc);
-#endif
       s[mt] = acc;
     }
 #pragma unroll
     for (int i = 0; i < VLD; ++i) {
       const int c = lane + 64 * i;
       const int key = c / CH;
-#if FDL_ATTN_ROWS_BUF
       st16(&vb[key][(c % CH) * 8], st.v[i]);  // zeros past the length
-#else
-      const bool part = key0 + KT > si.L;
-      st16(&vb[key][(c % CH) * 8],
-           part && key0 + key >= si.L ? u32x4{0u, 0u, 0u, 0u} : st.v[i]);
-#endif
     }
     const u32x4 pb = tile_softmax<D / 16>(s, vis, tv, key0, g, a.scale_log2, m, l, o, xs);
 #pragma unroll
@@ -999,9 +940,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // sequences x heads) and the mass is asked for: there it saves the split
 // merge and the second pass over K, which at that size cost more than the
 // row groups' repeated reads of the head's keys (served from L2).
-#ifndef FDL_ATTN_ROWS_MAX_GRID
-#define FDL_ATTN_ROWS_MAX_GRID 256
-#endif
+constexpr long kRowsMaxGrid = 256;
 
 AttnPlan plan_attention(int batch, int rows, int H, int D, int max_kv_len,
                         int max_rows_per_seq, int mass_stride) {
@@ -1011,7 +950,7 @@ AttnPlan plan_attention(int batch, int rows, int H, int D, int max_kv_len,
   // (at most 4 tiles per wave, 1024 keys) and the grid is small.
   const bool mass = mass_stride > 0;
   const int rgroups = max(1, (max_rows_per_seq + 15) / 16);
-  if (mass && max_tiles <= kRowWaves * 4 && (long)batch * H * rgroups <= FDL_ATTN_ROWS_MAX_GRID) {
+  if (mass && max_tiles <= kRowWaves * 4 && (long)batch * H * rgroups <= kRowsMaxGrid) {
     p.rows_path = 1;
     p.rgroups = rgroups;
     p.maxt = max_tiles <= kRowWaves ? 1 : max_tiles <= 2 * kRowWaves ? 2 : 4;
@@ -1023,10 +962,8 @@ AttnPlan plan_attention(int batch, int rows, int H, int D, int max_kv_len,
   }
   p.row_tiles = max(1, (max_rows_per_seq + 63) / 64);
   const long base = (long)batch * p.row_tiles * H;
-#ifndef FDL_ATTN_UNITS
-#define FDL_ATTN_UNITS 128
-#endif
-  int splits = (int)((FDL_ATTN_UNITS + base - 1) / max(base, 1L));
+  constexpr long kUnits = 128;  // target (sequence, row tile, head, split) units
+  int splits = (int)((kUnits + base - 1) / max(base, 1L));
   splits = max(1, min(splits, (max_tiles + 1) / 2));
   p.splits = splits;
   if (mass_stride > 0) {

@@ -286,11 +286,8 @@ __device__ __forceinline__ void qkv_splitk_body(const FlashCacheArgs &a, const S
   // Column groups visit their chunks in rotated order: at any moment the
   // groups read different 256-byte offsets of their weight rows (rows are a
   // power-of-two stride apart), spreading requests over the HBM channels.
-#ifndef FDL_FC_ROT
-#define FDL_FC_ROT 1
-#endif
   const int nch_rt = NCH > 0 ? NCH : sp.ks / KC;
-  const int rot = FDL_FC_ROT ? grp % nch_rt : 0;
+  const int rot = grp % nch_rt;
   auto load = [&](u32x4 *reg, int c) {
     int cc = c + rot;
     cc = cc >= nch_rt ? cc - nch_rt : cc;
@@ -675,30 +672,13 @@ __global__ __launch_bounds__(256) void scatter_kv_kernel(FlashCacheArgs a, const
 
 }  // namespace
 
-// Tile shape of the split-K projection: NTW 16-feature tiles per wave, NGW
-// wave groups across features, NST register stages, SNW waves, KC reduction
-// elements per staged chunk; at most SPLIT_CAP workgroups before splitting.
-
-#ifndef FDL_FC_NTW
-#define FDL_FC_NTW 3
-#endif
-#ifndef FDL_FC_NGW
-#define FDL_FC_NGW 1
-#endif
-#ifndef FDL_FC_NST
-#define FDL_FC_NST 2
-#endif
-#ifndef FDL_FC_SNW
-#define FDL_FC_SNW 8
-#endif
-#ifndef FDL_FC_KC
-#define FDL_FC_KC 256
-#endif
-#ifndef FDL_FC_SPLIT_CAP
-#define FDL_FC_SPLIT_CAP 320
-#endif
+// Tile shape of the split-K projection: kSplitNTW 16-feature tiles per wave,
+// kSplitNGW wave groups across features, kSplitNST register stages,
+// kSplitWaves waves, kSplitKC reduction elements per staged chunk; at most
+// kSplitCap workgroups before the reduction is split.
 namespace {
-constexpr int kSplitNTW = FDL_FC_NTW, kSplitNGW = FDL_FC_NGW;
+constexpr int kSplitNTW = 3, kSplitNGW = 1, kSplitNST = 2, kSplitWaves = 8, kSplitKC = 256;
+constexpr int kSplitCap = 320;
 
 // Compute units of the current device (cached per device; 256 if the query
 // fails, the part's count).
@@ -726,11 +706,11 @@ struct FcPlan {
 FcPlan plan_fc(int rows, int hidden, int H, int D) {
   FcPlan p{};
   const int total_pairs = 3 * H * (D / 2);
-  if (rows > 64 || hidden % FDL_FC_KC != 0) return p;  // tiled kernel, no workspace
+  if (rows > 64 || hidden % kSplitKC != 0) return p;  // tiled kernel, no workspace
   p.splitk = true;
   p.G = (total_pairs + kSplitCW / 2 - 1) / (kSplitCW / 2);
   p.S = 1;
-  while (p.S < 8 && p.G * 2 * p.S <= FDL_FC_SPLIT_CAP && hidden % (FDL_FC_KC * 2 * p.S) == 0) p.S *= 2;
+  while (p.S < 8 && p.G * 2 * p.S <= kSplitCap && hidden % (kSplitKC * 2 * p.S) == 0) p.S *= 2;
   if (p.S > 1) p.bytes = (size_t)p.G * p.S * 64 * kSplitCW * sizeof(float);
   return p;
 }
@@ -752,27 +732,27 @@ hipError_t launch_flash_cache(const FlashCacheArgs &a, void *ws, size_t ws_bytes
     sp.S = fp.S;
     sp.ks = a.hidden / fp.S;
     sp.partials = fp.bytes ? static_cast<float *>(ws) : nullptr;
-    const int nch = sp.ks / FDL_FC_KC;
-    const dim3 grid(fp.G * fp.S), block(FDL_FC_SNW * 64);
+    const int nch = sp.ks / kSplitKC;
+    const dim3 grid(fp.G * fp.S), block(kSplitWaves * 64);
     switch (nch) {
       case 4:
-        hipLaunchKernelGGL((qkv_splitk_kernel<kSplitNTW, kSplitNGW, FDL_FC_NST, 4, FDL_FC_SNW, FDL_FC_KC>), grid, block, 0,
+        hipLaunchKernelGGL((qkv_splitk_kernel<kSplitNTW, kSplitNGW, kSplitNST, 4, kSplitWaves, kSplitKC>), grid, block, 0,
                            s, a, sp);
         break;
       case 8:
-        hipLaunchKernelGGL((qkv_splitk_kernel<kSplitNTW, kSplitNGW, FDL_FC_NST, 8, FDL_FC_SNW, FDL_FC_KC>), grid, block, 0,
+        hipLaunchKernelGGL((qkv_splitk_kernel<kSplitNTW, kSplitNGW, kSplitNST, 8, kSplitWaves, kSplitKC>), grid, block, 0,
                            s, a, sp);
         break;
       case 16:
-        hipLaunchKernelGGL((qkv_splitk_kernel<kSplitNTW, kSplitNGW, FDL_FC_NST, 16, FDL_FC_SNW, FDL_FC_KC>), grid, block,
+        hipLaunchKernelGGL((qkv_splitk_kernel<kSplitNTW, kSplitNGW, kSplitNST, 16, kSplitWaves, kSplitKC>), grid, block,
                            0, s, a, sp);
         break;
       case 32:
-        hipLaunchKernelGGL((qkv_splitk_kernel<kSplitNTW, kSplitNGW, FDL_FC_NST, 32, FDL_FC_SNW, FDL_FC_KC>), grid, block,
+        hipLaunchKernelGGL((qkv_splitk_kernel<kSplitNTW, kSplitNGW, kSplitNST, 32, kSplitWaves, kSplitKC>), grid, block,
                            0, s, a, sp);
         break;
       default:
-        hipLaunchKernelGGL((qkv_splitk_kernel<kSplitNTW, kSplitNGW, FDL_FC_NST, 0, FDL_FC_SNW, FDL_FC_KC>), grid, block, 0,
+        hipLaunchKernelGGL((qkv_splitk_kernel<kSplitNTW, kSplitNGW, kSplitNST, 0, kSplitWaves, kSplitKC>), grid, block, 0,
                            s, a, sp);
     }
     hipError_t e = hipGetLastError();

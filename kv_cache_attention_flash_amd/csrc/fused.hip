@@ -10,15 +10,18 @@
 // The unit compiles the projection and attention files for their workgroup
 // bodies (FDL_DEVICE_ONLY leaves their own launchers out), so each phase runs
 // exactly the code of the separate calls: the results are bitwise theirs.
-// Phases: every projection item, then (once all are done) the row-group
-// attention items, then (once those are done) the mass items.  A cooperative
-// launch makes every workgroup resident, so a workgroup that finished its
-// items can wait for the others.  Hand-offs cross XCDs (each has its own L2):
-// a workgroup's items end with a device-scope release (the writes leave its
-// L2) and a count; a waiting workgroup polls the count, then acquires at
-// device scope (its caches are invalidated before it reads).  Every wait is
-// bounded: past the bound it sets the error word and goes on.  The last
-// workgroup to finish resets the counts for the next call.
+// Items: every projection item, then the row-group attention items (each
+// waits until all projection items are done), then the mass items (each waits
+// until all attention items are done).  A workgroup takes its next item from
+// a ticket counter, so the items are claimed in that order: an item only ever
+// waits for items with lower tickets, which are held by running workgroups
+// that do not wait for it, and the launch needs no co-residency guarantee
+// (an ordinary launch, not a cooperative one).  Hand-offs cross XCDs (each
+// has its own L2): a workgroup's items end with a device-scope release (the
+// writes leave its L2) and a count; a waiting workgroup polls the count, then
+// acquires at device scope (its caches are invalidated before it reads).
+// Every wait is bounded: past the bound it sets the error word and goes on.
+// The last workgroup to leave resets the counters for the next call.
 #include <algorithm>
 
 #define FDL_DEVICE_ONLY 1
@@ -65,61 +68,70 @@ __global__ __launch_bounds__(kFusedThreads) void fused_step_kernel(FlashCacheArg
                                                                    int nrow_tiles, int ncol_tiles,
                                                                    AttnArgs aa, AttnPlan ap,
                                                                    int *sync) {
-  static_assert(FDL_FC_SNW * 64 == kFusedThreads, "split-K workgroup size");
+  static_assert(kSplitWaves * 64 == kFusedThreads, "split-K workgroup size");
   union Lds {
-    SplitLds<kSplitNTW, kSplitNGW, FDL_FC_KC> split;
+    SplitLds<kSplitNTW, kSplitNGW, kSplitKC> split;
     GemmLds<128, 4> gemm;
     RowsLds<D> rows;
     float mass[2][8][32];
   };
   __shared__ Lds lds;
+  __shared__ int s_ticket;
   int *proj_done = sync, *attn_done = sync + 1, *exit_count = sync + 2, *error = sync + 3;
+  int *ticket = sync + 4;
 
   const int nproj = KIND == 2 ? nrow_tiles * ncol_tiles : sp.G * sp.S;
-  for (int it = blockIdx.x; it < nproj; it += gridDim.x) {
-    if constexpr (KIND == 0)
-      qkv_splitk_body<kSplitNTW, kSplitNGW, FDL_FC_NST, 16, FDL_FC_SNW, FDL_FC_KC>(fa, sp, it,
-                                                                                   lds.split);
-    else if constexpr (KIND == 1)
-      qkv_splitk_body<kSplitNTW, kSplitNGW, FDL_FC_NST, 0, FDL_FC_SNW, FDL_FC_KC>(fa, sp, it,
-                                                                                  lds.split);
-    else
-      qkv_gemm_body<128, 4, 2>(fa, nrow_tiles, ncol_tiles, it, lds.gemm);
-    phase_signal(proj_done);
-  }
-
   const int natt = aa.batch * aa.c.H * ap.rgroups;
-  if ((int)blockIdx.x < natt) phase_wait(proj_done, nproj, error);
-  for (int it = blockIdx.x; it < natt; it += gridDim.x) {
-    attn_rows_body<D, MAXT, true>(aa, ap, it, natt, lds.rows);
-    phase_signal(attn_done);
-  }
-
-  // Mass items two at a time, one per 256-thread half.
   const int nmass = aa.batch * ((aa.mass_stride + 31) / 32);
-  const int npair = (nmass + 1) / 2;
-  if ((int)blockIdx.x < npair) phase_wait(attn_done, natt, error);
-  const int half = threadIdx.x >> 8;
-  for (int it = blockIdx.x; it < npair; it += gridDim.x) {
-    const int item = 2 * it + half;
-    attn_rows_mass_body(aa, ap, item, threadIdx.x & 255, item < nmass, lds.mass[half]);
+  const int npair = (nmass + 1) / 2;  // mass items two at a time, one per 256-thread half
+  const int total = nproj + natt + npair;
+  bool waited_proj = false, waited_attn = false;
+  for (;;) {
+    __syncthreads();  // the previous item is done with s_ticket and the LDS
+    if (threadIdx.x == 0)
+      s_ticket = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
+    const int it = s_ticket;
+    if (it >= total) break;
+    if (it < nproj) {
+      if constexpr (KIND == 0)
+        qkv_splitk_body<kSplitNTW, kSplitNGW, kSplitNST, 16, kSplitWaves, kSplitKC>(fa, sp, it,
+                                                                                   lds.split);
+      else if constexpr (KIND == 1)
+        qkv_splitk_body<kSplitNTW, kSplitNGW, kSplitNST, 0, kSplitWaves, kSplitKC>(fa, sp, it,
+                                                                                  lds.split);
+      else
+        qkv_gemm_body<128, 4, 2>(fa, nrow_tiles, ncol_tiles, it, lds.gemm);
+      phase_signal(proj_done);
+    } else if (it < nproj + natt) {
+      if (!waited_proj) phase_wait(proj_done, nproj, error);
+      waited_proj = true;
+      attn_rows_body<D, MAXT, true>(aa, ap, it - nproj, natt, lds.rows);
+      phase_signal(attn_done);
+    } else {
+      if (!waited_attn) phase_wait(attn_done, natt, error);
+      waited_attn = true;
+      const int half = threadIdx.x >> 8;
+      const int item = 2 * (it - nproj - natt) + half;
+      attn_rows_mass_body(aa, ap, item, threadIdx.x & 255, item < nmass, lds.mass[half]);
+    }
   }
 
-  // The last workgroup out (every other one is past all of its waits)
-  // resets the counts for the next call.
-  __syncthreads();
+  // The last workgroup out (every other one has claimed its final ticket and
+  // is past all of its waits) resets the counters for the next call.
   if (threadIdx.x == 0) {
     const int n = __hip_atomic_fetch_add(exit_count, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     if (n == (int)gridDim.x - 1) {
       __hip_atomic_store(proj_done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(attn_done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(exit_count, 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
-// Resident workgroups of one instantiation on the current device (cached).
+// Resident workgroups of one instantiation on the current device (cached):
+// more would only claim the final ticket and leave.
 template <int D, int MAXT, int KIND>
 int fused_capacity() {
   static int cap[64] = {0};
@@ -146,11 +158,10 @@ hipError_t launch_fused_inst(FlashCacheArgs fa, SplitPlan sp, int nrow, int ncol
   const int npair = (aa.batch * ((aa.mass_stride + 31) / 32) + 1) / 2;
   const int cap = fused_capacity<D, MAXT, KIND>();
   if (cap <= 0) return hipErrorInvalidConfiguration;
-  const int grid = std::min(std::max(nproj, std::max(natt, npair)), cap);
-  void *args[] = {&fa, &sp, &nrow, &ncol, &aa, &ap, &sync};
-  return hipLaunchCooperativeKernel(
-      reinterpret_cast<const void *>(&fused_step_kernel<D, MAXT, KIND>), dim3(grid),
-      dim3(kFusedThreads), args, 0, s);
+  const int grid = std::max(1, std::min(std::max(nproj, std::max(natt, npair)), cap));
+  hipLaunchKernelGGL((fused_step_kernel<D, MAXT, KIND>), dim3(grid), dim3(kFusedThreads), 0, s,
+                     fa, sp, nrow, ncol, aa, ap, sync);
+  return hipGetLastError();
 }
 
 template <int D, int KIND>
@@ -168,7 +179,7 @@ bool fused_step_supported(const FlashCacheArgs &fa, const AttnPlan &ap, bool mas
   const FcPlan fp = plan_fc(fa.rows, fa.hidden, fa.c.H, fa.c.D);
   if (!fp.splitk) return true;
   if (fp.S != 1) return false;
-  const int nch = fa.hidden / FDL_FC_KC;
+  const int nch = fa.hidden / kSplitKC;
   return nch == 16 || (nch != 4 && nch != 8 && nch != 32);
 }
 
@@ -182,7 +193,7 @@ hipError_t launch_fused_step(const FlashCacheArgs &fa, const AttnArgs &aa, const
     sp.S = 1;
     sp.ks = fa.hidden;
     sp.partials = nullptr;
-    kind = fa.hidden / FDL_FC_KC == 16 ? 0 : 1;
+    kind = fa.hidden / kSplitKC == 16 ? 0 : 1;
   } else {
     const int total_pairs = 3 * fa.c.H * (fa.c.D / 2);
     nrow = (fa.rows + 127) / 128;

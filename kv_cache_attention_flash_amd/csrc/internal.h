@@ -60,7 +60,7 @@ hipError_t launch_attention(const AttnArgs &a, const AttnPlan &p, hipStream_t s)
 
 // Single-launch step (fused.hip): the projection then row-group attention with
 // the mass, for shapes whose separate calls take a one-launch projection (no
-// split reduction) and the row-group attention path.  sync: 4 ints of device
+// split reduction) and the row-group attention path.  sync: 5 ints of device
 // memory, zero before the first call (each call leaves them zero).
 bool fused_step_supported(const FlashCacheArgs &fa, const AttnPlan &ap, bool mass);
 hipError_t launch_fused_step(const FlashCacheArgs &fa, const AttnArgs &aa, const AttnPlan &ap,

@@ -1,10 +1,13 @@
 """Summaries of rocprofv3 output for the library's kernels.
 
     python -m kv_cache_attention_flash_amd.profiling stats  <kernel_stats.csv> <out.md> <command...>
+    python -m kv_cache_attention_flash_amd.profiling stats-db <results.db> <out.md> <command...>
     python -m kv_cache_attention_flash_amd.profiling traffic <fetch_counter.csv> <write_counter.csv> \
         <out.json> <kernel-substrings> <calibration-bytes> <source-file> <command...>
 
-``stats`` writes a Markdown table of per-kernel call counts and durations.
+``stats`` writes a Markdown table of per-kernel call counts and durations
+(from the ``--output-format csv`` statistics file); ``stats-db`` makes the same
+table from the SQLite database rocprofv3 writes by default.
 ``traffic`` turns two counter runs (FETCH_SIZE, then WRITE_SIZE, KiB per
 dispatch) into HBM bytes per call of one library entry point: the sum over
 its kernels (comma-separated name substrings) of each kernel's median.  Each counter is scaled by
@@ -41,6 +44,21 @@ def kernel_stats_markdown(stats_csv: str, command: str) -> str:
         out.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                    f"{float(r['Percentage']):.1f}% |")
+    return f"Command: `{command}`\n\n" + "\n".join(out) + "\n"
+
+
+def kernel_stats_markdown_db(db_path: str, command: str) -> str:
+    import sqlite3
+    con = sqlite3.connect(db_path)
+    rows = list(con.execute("select name, count(*), avg(end - start), min(end - start), "
+                            "max(end - start), sum(end - start) from kernels group by name "
+                            "order by sum(end - start) desc"))
+    total = sum(r[5] for r in rows) or 1
+    out = ["| kernel | calls | average (us) | min (us) | max (us) | share |",
+           "|---|---|---|---|---|---|"]
+    for name, n, avg, mn, mx, tot in rows:
+        out.append(f"| `{short_name(name)}` | {n} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | "
+                   f"{mx / 1e3:.2f} | {100.0 * tot / total:.1f}% |")
     return f"Command: `{command}`\n\n" + "\n".join(out) + "\n"
 
 
@@ -97,8 +115,9 @@ def traffic(fetch_csv, write_csv, kernel_substrs, calib_bytes, source_file):
 
 
 def main(argv):
-    if argv[0] == "stats":
-        md = kernel_stats_markdown(argv[1], " ".join(argv[3:]))
+    if argv[0] in ("stats", "stats-db"):
+        fn = kernel_stats_markdown if argv[0] == "stats" else kernel_stats_markdown_db
+        md = fn(argv[1], " ".join(argv[3:]))
         with open(argv[2], "w") as f:
             f.write(md)
         print(md)

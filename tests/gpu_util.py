@@ -64,11 +64,14 @@ class GpuRun:
         rows_per_seq = np.diff(wl.cu_rows)
         self.max_rows = int(rows_per_seq.max()) if len(rows_per_seq) else 0
 
-    def step(self, topb=None, stream=None):
+    def step(self, topb=None, stream=None, unfused=False):
+        """flash_cache_step (or, with ``unfused``, its three-launch ablation
+        flash_cache_step_unfused) -> scheduled_attention (+ mass) -> track_topb."""
         wl = self.wl
         topb = wl.topb if topb is None else topb
-        q, sm = fd.flash_cache_step(self.cache, self.x, self.w, self.cu, self.pos, self.slots,
-                                    wl.rope_base, stream=stream)
+        fc = fd.flash_cache_step_unfused if unfused else fd.flash_cache_step
+        q, sm = fc(self.cache, self.x, self.w, self.cu, self.pos, self.slots, wl.rope_base,
+                   stream=stream)
         out, mass = fd.scheduled_attention(self.cache, q, self.cu, self.kv_len, wl.max_kv_len,
                                            self.max_rows, views=self.views,
                                            want_mass=bool(topb), stream=stream)

@@ -84,6 +84,38 @@ def test_debug_checks_refuse_bad_indices(monkeypatch):
     kv_bad[0] = -5
     _refused(fd, lambda: fd.scheduled_attention(run.cache, q1, run.cu, kv_bad, wl.max_kv_len,
                                                 run.max_rows))
+    # a sequence with more rows than max_rows_per_seq (its extra rows would
+    # otherwise be left unwritten)
+    _refused(fd, lambda: fd.scheduled_attention(run.cache, q1, run.cu, run.kv_len,
+                                                wl.max_kv_len, run.max_rows - 1, want_mass=True))
     torch.cuda.synchronize()
     # nothing was written by the refused calls
     assert torch.equal(run.cache.k_cache, k_ref) and torch.equal(run.cache.v_cache, v_ref)
+
+
+def test_debug_checks_refuse_bad_two_view_descriptors(monkeypatch):
+    """Two-view descriptors that break window_start + window_len <=
+    draft_slot_start or draft_slot_start + window_len <= kv_len, or hold a
+    negative entry, are refused on the host; valid ones pass."""
+    fd = _fd()
+    wl = synth.WORKLOADS["small_verify_b3"]()
+    print(f"[debug] {wl.name}: two-view descriptors", flush=True)
+    run = G.GpuRun(wl, DEV)
+    q, _ = fd.flash_cache_step(run.cache, run.x, run.w, run.cu, run.pos, run.slots, wl.rope_base)
+    o0, _ = fd.scheduled_attention(run.cache, q, run.cu, run.kv_len, wl.max_kv_len, run.max_rows,
+                                   views=run.views)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("FDL_DEBUG", "1")
+    o1, _ = fd.scheduled_attention(run.cache, q, run.cu, run.kv_len, wl.max_kv_len, run.max_rows,
+                                   views=run.views)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o0)
+    w0, wlen, d0 = (int(v) for v in wl.views[0])
+    for bad_row in ([d0 - wlen + 1, wlen, d0],            # window runs into the draft slots
+                    [w0, wlen, int(wl.kv_len[0]) - wlen + 1],  # draft slots past kv_len
+                    [-1, wlen, d0]):                      # negative entry
+        v = wl.views.copy()
+        v[0] = bad_row
+        vt = G.i32(v, DEV)
+        _refused(fd, lambda: fd.scheduled_attention(run.cache, q, run.cu, run.kv_len,
+                                                    wl.max_kv_len, run.max_rows, views=vt))

@@ -3,7 +3,8 @@ results of flash_cache_step followed by scheduled_attention with the mass (the
 phases run the same workgroup code), over both projection kinds (split-K at
 <= 64 rows, tiled above), both head sizes, ragged sequences and the two-view
 mask; repeated calls leave the workspace counters at zero with no timed-out
-wait; shapes outside its scope are refused before anything is launched.
+wait; the call on a side stream; shapes outside its scope are refused before
+anything is launched.
 Parity with the CPU oracle follows from the separate calls' parity tests and
 is also checked directly on the batch-1 layer.
 """
@@ -68,8 +69,28 @@ def test_bitwise_equal_to_the_two_calls(name):
         assert torch.equal(r2.cache.v_cache, r1.cache.v_cache), (name, rep, "V cache")
         assert torch.equal(o2, o1), (name, rep, "attention output")
         assert torch.equal(m2, m1), (name, rep, "mass")
-    counters = ws[:16].view(torch.int32).cpu().tolist()
-    assert counters == [0, 0, 0, 0], counters  # counts reset, error word clear
+    counters = ws[:20].view(torch.int32).cpu().tolist()
+    assert counters == [0, 0, 0, 0, 0], counters  # counts and ticket reset, error word clear
+
+
+def test_on_a_side_stream():
+    """The call on a stream other than torch's current one (its outputs and
+    zero-filled workspace allocated in that stream's order): bitwise the two
+    calls' results, no timed-out wait."""
+    fd = _fd()
+    wl = synth.llada8b_b1()
+    _banner("side stream")
+    r1, q1, sm1, o1, m1 = _two_calls(fd, wl)
+    run = G.GpuRun(wl, DEV)
+    torch.cuda.synchronize()  # inputs uploaded before the side stream reads them
+    side = torch.cuda.Stream()
+    q2, sm2, o2, m2 = fd.flash_cache_attention_step(
+        run.cache, run.x, run.w, run.cu, run.pos, run.slots, wl.rope_base, run.kv_len,
+        wl.max_kv_len, run.max_rows, views=run.views, stream=side)
+    side.synchronize()
+    assert torch.equal(q2, q1) and torch.equal(sm2, sm1)
+    assert torch.equal(run.cache.k_cache, r1.cache.k_cache)
+    assert torch.equal(o2, o1) and torch.equal(m2, m1)
 
 
 def test_batch1_layer_against_the_oracle():
