@@ -176,7 +176,15 @@ size_t fdl_flash_cache_workspace_bytes(int32_t num_rows, int32_t hidden,
  *              in a fixed order: results are bitwise reproducible.
  *   mass_stride >= max_kv_len when mass is given.
  *   workspace  device scratch of at least fdl_attention_workspace_bytes(...)
- *              bytes (same arguments); contents need no initialisation. */
+ *              bytes (same arguments); contents need no initialisation.  On
+ *              FDL_PATH_SPLIT_MASS_EXCHANGE (fdl_attention_path) with a cache
+ *              past 1024 keys, the splits of a sequence wait for each other's
+ *              row statistics through counters the call clears itself at its
+ *              start; the int32 at byte 4 is then an error word that becomes
+ *              1 if such a wait ever timed out (it never should: every wait is
+ *              for a running workgroup) and stays 1 until the caller clears
+ *              it; the results of such a call are invalid.  Calls that share a
+ *              workspace must not run at the same time. */
 int scheduled_attention(const fdl_kv_cache *cache, const void *q, int32_t batch,
                         int32_t num_rows, const int32_t *cu_rows,
                         const int32_t *kv_len, int32_t max_kv_len,
@@ -184,6 +192,28 @@ int scheduled_attention(const fdl_kv_cache *cache, const void *q, int32_t batch,
                         float softmax_scale, float *out, float *mass,
                         int32_t mass_stride, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/* The kernels scheduled_attention uses for these sizes (mass_stride 0 = no
+ * mass); the results agree on every path within float rounding:
+ *   FDL_PATH_ROW_GROUPS  one workgroup per (sequence, head, 16 rows) over the
+ *       whole cache (small grids, caches up to 1024 keys, mass asked for);
+ *   FDL_PATH_SPLIT  (sequence, 64 rows, head, KV split) workgroups with a
+ *       fixed-order merge of the splits (no mass);
+ *   FDL_PATH_SPLIT_MASS_EXCHANGE  (sequence, 64 rows, head, 1024-key split)
+ *       workgroups keeping their scores on chip; the splits of a longer cache
+ *       exchange row statistics, so keys are read once;
+ *   FDL_PATH_SPLIT_MASS_REREAD  one workgroup per (sequence, 64 rows, head)
+ *       whose mass is a second, last-first pass over K right after the first
+ *       (caches past 1024 keys with enough sequences x heads to fill the GPU).
+ * Returns 0 for invalid sizes. */
+enum {
+  FDL_PATH_ROW_GROUPS = 1,
+  FDL_PATH_SPLIT = 2,
+  FDL_PATH_SPLIT_MASS_EXCHANGE = 3,
+  FDL_PATH_SPLIT_MASS_REREAD = 4
+};
+int fdl_attention_path(int32_t batch, int32_t num_rows, int32_t num_heads, int32_t head_dim,
+                       int32_t max_kv_len, int32_t max_rows_per_seq, int32_t mass_stride);
 
 /* Workspace bytes scheduled_attention needs for these sizes (mass_stride 0 =
  * no mass).  Returns 0 for invalid sizes. */

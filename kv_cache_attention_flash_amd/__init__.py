@@ -40,7 +40,7 @@ __all__ = ["PagedKVCache", "flash_cache_step", "flash_cache_step_unfused", "sche
            "flash_cache_workspace_bytes", "flash_cache_unfused_workspace_bytes", "DecodeStep",
            "decode_plan", "gather_hidden", "DecodeLoop", "lm_head_confidence",
            "lm_head_workspace_bytes", "flash_cache_attention_step", "fused_step_workspace_bytes",
-           "fused_step_error", "FdlError", "load"]
+           "fused_step_error", "attention_error", "attention_path", "FdlError", "load"]
 
 
 def load():
@@ -217,6 +217,19 @@ def attention_workspace_bytes(batch, num_rows, num_heads, head_dim, max_kv_len,
                                                          mass_stride))
 
 
+ATTENTION_PATHS = {1: "row_groups", 2: "split", 3: "split_mass_exchange", 4: "split_mass_reread"}
+
+
+def attention_path(batch, num_rows, num_heads, head_dim, max_kv_len, max_rows_per_seq,
+                   mass_stride=0) -> str:
+    """Which kernels scheduled_attention runs for these sizes (see include/fdllm.h)."""
+    k = int(_lib.load().fdl_attention_path(batch, num_rows, num_heads, head_dim, max_kv_len,
+                                           max_rows_per_seq, mass_stride))
+    if k not in ATTENTION_PATHS:
+        raise ValueError("invalid sizes")
+    return ATTENTION_PATHS[k]
+
+
 def scheduled_attention(cache: PagedKVCache, q, cu_rows, kv_len, max_kv_len, max_rows_per_seq,
                         views=None, softmax_scale=0.0, out=None, want_mass=False, mass=None,
                         mass_stride=None, workspace=None, stream=None):
@@ -262,6 +275,21 @@ def scheduled_attention(cache: PagedKVCache, q, cu_rows, kv_len, max_kv_len, max
                                  _ptr(mass), ms, workspace.data_ptr(), workspace.numel(), sh)
     _lib.check("scheduled_attention", st)
     return out, mass
+
+
+ATTENTION_ERROR_OFFSET = 4  # byte offset of scheduled_attention's error word in its workspace
+
+
+def attention_error(workspace: torch.Tensor, stream=None) -> int:
+    """scheduled_attention's error word, for calls whose cache needs more than
+    one 1024-key split with the mass asked for (the splits wait for each
+    other): 1 if such a wait ever timed out on this workspace (those results
+    are invalid; the word stays set until cleared), else 0.  Synchronises the
+    stream."""
+    sh = _stream(stream, workspace.device)
+    with _on_stream(sh, workspace.device):
+        word = workspace[ATTENTION_ERROR_OFFSET:ATTENTION_ERROR_OFFSET + 4].view(torch.int32).item()
+    return int(word)
 
 
 def track_topb(mass, kv_len, topb, out=None, stream=None):

@@ -42,6 +42,7 @@ EXPORTS = {
                                            c_vp, c_i32, c_i32, c_vp, c_f32, c_vp, c_vp, c_i32,
                                            c_vp, c_size, c_vp]),
     "fdl_attention_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "fdl_attention_path": (ctypes.c_int, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "track_topb": (ctypes.c_int, [c_vp, c_i32, c_vp, c_i32, c_i32, c_vp, c_vp]),
     "verify_accept": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i32, c_i32, c_f32, c_vp, c_vp]),
     "decode_plan": (ctypes.c_int, [c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp,

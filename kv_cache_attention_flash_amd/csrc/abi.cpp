@@ -312,6 +312,19 @@ size_t fdl_attention_workspace_bytes(int32_t batch, int32_t num_rows, int32_t nu
       .bytes;
 }
 
+int fdl_attention_path(int32_t batch, int32_t num_rows, int32_t num_heads, int32_t head_dim,
+                       int32_t max_kv_len, int32_t max_rows_per_seq, int32_t mass_stride) {
+  if (batch < 0 || num_rows < 0 || num_heads <= 0 || head_dim <= 0 || max_kv_len < 0 ||
+      max_rows_per_seq < 0 || mass_stride < 0)
+    return 0;
+  const fdl::AttnPlan p = fdl::plan_attention(batch, num_rows, num_heads, head_dim, max_kv_len,
+                                              max_rows_per_seq, mass_stride);
+  if (p.rows_path) return FDL_PATH_ROW_GROUPS;
+  if (p.fwd_mass) return FDL_PATH_SPLIT_MASS_REREAD;
+  if (p.xmass) return FDL_PATH_SPLIT_MASS_EXCHANGE;
+  return FDL_PATH_SPLIT;
+}
+
 int scheduled_attention(const fdl_kv_cache *cache, const void *q, int32_t batch,
                         int32_t num_rows, const int32_t *cu_rows, const int32_t *kv_len,
                         int32_t max_kv_len, int32_t max_rows_per_seq, const fdl_two_view *views,

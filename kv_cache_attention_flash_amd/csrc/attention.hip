@@ -36,7 +36,6 @@ namespace {
 
 constexpr int KT = 32;   // keys per tile
 constexpr int kNpf = 2;  // split path: tiles in flight per key group (pass 1)
-constexpr int kMnpf = 2; // split path: K tiles in flight (mass pass)
 constexpr float kNegInf = -__builtin_huge_valf();
 
 struct SeqInfo {
@@ -132,6 +131,56 @@ __device__ __forceinline__ u32x4 tile_softmax(const f32x4 s[2], const Vis &vis, 
   rs = rows4_sum(rs);
   l = l * alpha + rs;
   m = mnew;
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int dm = 0; dm < NO; ++dm) o[dm] *= alpha;
+  }
+  u32x4 pb;
+  pb[0] = cvt_pk_bf16(pv[0], pv[1]);
+  pb[1] = cvt_pk_bf16(pv[2], pv[3]);
+  pb[2] = cvt_pk_bf16(pv[4], pv[5]);
+  pb[3] = cvt_pk_bf16(pv[6], pv[7]);
+  return pb;
+}
+
+// The same step handing back, instead of the scaled scores, the fp32
+// probabilities pv[e] = exp2(x - mt) of the tile's keys and the maximum mt they
+// are taken against (the row's running maximum after this tile; 0 while the
+// row has seen nothing, when every pv is 0).  exp2(x - LSE) = pv * exp2(mt -
+// LSE): one exponential per row and tile forms the mass once the LSE is known.
+template <int NO>
+__device__ __forceinline__ u32x4 tile_softmax_pv(const f32x4 s[2], const Vis &vis, int tv,
+                                                 int key0, int g, float scale, float &m, float &l,
+                                                 f32x4 *o, float *pv, float &mt) {
+  float xs[8];
+  if (tv == 2) {
+#pragma unroll
+    for (int mt_ = 0; mt_ < 2; ++mt_)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xs[mt_ * 4 + e] = s[mt_][e] * scale;
+  } else {
+#pragma unroll
+    for (int mt_ = 0; mt_ < 2; ++mt_)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        xs[mt_ * 4 + e] = vis(key0 + 8 * g + 4 * mt_ + e) ? s[mt_][e] * scale : kNegInf;
+  }
+  float tmax = fmaxf(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])),
+                     fmaxf(fmaxf(xs[4], xs[5]), fmaxf(xs[6], xs[7])));
+  tmax = rows4_max(tmax);
+  const float mnew = fmaxf(m, tmax);
+  const float msafe = mnew == kNegInf ? 0.f : mnew;
+  const float alpha = fast_exp2(m - msafe);
+  float rs = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    pv[e] = fast_exp2(xs[e] - msafe);
+    rs += pv[e];
+  }
+  rs = rows4_sum(rs);
+  l = l * alpha + rs;
+  m = mnew;
+  mt = msafe;
   if (__any(alpha != 1.f)) {
 #pragma unroll
     for (int dm = 0; dm < NO; ++dm) o[dm] *= alpha;
@@ -280,7 +329,15 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, int r, int h, bool ok,
 // tiles, row group wave % 4 owns 16 query rows; the two key groups keep their
 // own online-softmax state and are combined through LDS at the end (group 0
 // first), so two waves per SIMD hide each other's latency.
-template <int D>
+//
+// MASS (one unit per (sequence, row tile, head): no KV split): the same
+// workgroup then forms the attention mass of its keys, m_h[j] = sum over its
+// rows of exp2(x_rj - LSE_r), in a second pass over K that starts right after
+// the first and visits the tiles last-first: the keys read last are the ones
+// still in the last-level cache, so the second read mostly avoids HBM.  The
+// per-(sequence, head, row tile) sums go to the workspace; attn_xfinish adds
+// them over heads and row tiles.
+template <int D, bool MASS>
 __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
   constexpr int NPF = kNpf;  // tiles in flight per key group
   // K tiles (swizzled chunks); 8 chunks more per tile make room for the
@@ -375,6 +432,114 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
     }
   }
   lds_barrier();
+  if constexpr (MASS) {
+    __shared__ float s_lse[64];
+    __shared__ float wsum[2][2][4][KT];  // [buffer][key group][row group][key]
+    if (kg == 0) {
+      const float m1 = mml[2 * rl], l1 = mml[2 * rl + 1];
+      const float mx = fmaxf(m, m1);
+      const float f0 = m == kNegInf ? 0.f : exp2f(m - mx);
+      const float f1 = m1 == kNegInf ? 0.f : exp2f(m1 - mx);
+      l = l * f0 + l1 * f1;
+      m = mx;
+      if (row_ok) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        float *dst = a.out + ((size_t)r * a.c.H + h) * D + 4 * g;
+#pragma unroll
+        for (int dm = 0; dm < D / 16; ++dm)
+          *reinterpret_cast<f32x4 *>(dst + 16 * dm) =
+              (o[dm] * f0 + *reinterpret_cast<const f32x4 *>(&mo[rl * D + 16 * dm + 4 * g]) * f1) *
+              inv;
+      }
+      if (g == 0) s_lse[rl] = row_ok && l > 0.f ? m + log2f(l) : kNegInf;
+    }
+    lds_barrier();
+    // A row that sees no key has LSE -inf; subtracting +inf instead sends
+    // every exp2 to 0.
+    const float lr = s_lse[rl];
+    const float lsafe = lr == kNegInf ? __builtin_huge_valf() : lr;
+    float *mp = reinterpret_cast<float *>(a.ws + p.off_mass_part) +
+                (((size_t)b * a.c.H + h) * p.row_tiles + rt) * a.mass_stride;
+    // Pass 2: key group kg takes tiles te-1-kg, te-3-kg, ... (last first), K
+    // only, the same uniform ring of loads as pass 1.
+    const int n2 = (te - tb + 1) / 2;
+    const int n2r = (n2 + NPF - 1) / NPF * NPF;
+    Tile<D> kf[NPF];
+    if (te > tb) {
+#pragma unroll
+      for (int i = 0; i < NPF; ++i)
+        load_tile<D>(kf[i], a, s_page, tb, h, max(te - 1 - kg - 2 * i, tb) * KT, false, gtid);
+    }
+    const int b3 = (j >> 3) & 1, b2 = (j >> 2) & 1, b1 = (j >> 1) & 1;
+    // The sums of the previous iteration's tile (buffer pb_) are added over
+    // the row groups after the next barrier, by 64 threads (key group
+    // threadIdx.x / 32, key threadIdx.x % 32).
+    auto flush = [&](int it_prev) {
+      if (threadIdx.x < 2 * KT) {
+        const int fk = threadIdx.x / KT, key = threadIdx.x % KT, pb_ = it_prev & 1;
+        const int tile = te - 1 - fk - 2 * it_prev;
+        if (it_prev < n2 && tile >= tb) {
+          const float v = ((wsum[pb_][fk][0][key] + wsum[pb_][fk][1][key]) + wsum[pb_][fk][2][key]) +
+                          wsum[pb_][fk][3][key];
+          const int jj = tile * KT + key;
+          if (jj < si.L) mp[jj] = v;
+        }
+      }
+    };
+    for (int it0 = 0; it0 < n2r; it0 += NPF) {
+#pragma unroll
+      for (int ii = 0; ii < NPF; ++ii) {
+        const int it = it0 + ii;
+        const int tile = te - 1 - kg - 2 * it;
+        const bool have = it < n2 && tile >= tb;
+        const int buf = it & 1;
+        store_tile<D>(kf[ii], klds[kg][buf], nullptr, false, gtid);
+        load_tile<D>(kf[ii], a, s_page, tb, h, max(tile - 2 * NPF, tb) * KT, false, gtid);
+        lds_barrier();
+        if (it > 0) flush(it - 1);
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = 0.f;
+        const int key0 = tile * KT;
+        const int tv = have ? tile_vis(vis, key0) : 0;
+        if (tv != 0) {
+          f32x4 sv[2];
+          scores<D>(klds[kg][buf], qf, lane, sv);
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x = fast_exp2(sv[mt][e] * a.scale_log2 - lsafe);
+              pv[mt * 4 + e] = (tv == 2 || vis(key0 + 8 * g + 4 * mt + e)) ? x : 0.f;
+            }
+        }
+        // Reduce over the wave's 16 rows (lanes sharing g): reduce-scatter.
+        float q4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float give = b3 ? pv[i] : pv[i + 4];
+          const float keep = b3 ? pv[i + 4] : pv[i];
+          q4[i] = keep + lane_xor8(give);
+        }
+        float q2[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const float give = b2 ? q4[i] : q4[i + 2];
+          const float keep = b2 ? q4[i + 2] : q4[i];
+          q2[i] = keep + lane_xor4(give);
+        }
+        const float give = b1 ? q2[0] : q2[1];
+        const float keep = b1 ? q2[1] : q2[0];
+        const float q1 = keep + lane_xor2(give);
+        const float other = lane_xor1(q1);
+        const float tot = (j & 1) ? other + q1 : q1 + other;
+        if ((j & 1) == 0) wsum[buf][kg][wr][8 * g + 4 * b3 + 2 * b2 + b1] = tot;
+      }
+    }
+    lds_barrier();
+    if (n2r > 0) flush(n2r - 1);
+    return;
+  }
   if (kg == 1 || !row_ok) return;
   {
     const float m1 = mml[2 * rl], l1 = mml[2 * rl + 1];
@@ -395,10 +560,6 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
     for (int dm = 0; dm < D / 16; ++dm) {
       f32x4 val = o[dm] * inv;
       *reinterpret_cast<f32x4 *>(dst + 16 * dm) = val;
-    }
-    if (p.mass_splits && g == 0) {
-      float *lse = reinterpret_cast<float *>(a.ws + p.off_lse);
-      lse[(size_t)r * a.c.H + h] = l > 0.f ? m + log2f(l) : kNegInf;
     }
   } else {
     float *po = reinterpret_cast<float *>(a.ws + p.off_part_o);
@@ -462,92 +623,283 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, AttnPlan p)
   merge_row<4>(a, p, rh, D, d4, a.out);
 }
 
-// Attention mass pass: one workgroup per (sequence, head, key chunk).  Each
-// lane first forms its row's LSE (from pass 1 directly, or by combining the
-// KV-split maxima and normalisers, loaded with the first K tile), then K
-// tiles stream through double-buffered LDS and P = exp2(s - LSE) is summed over
-// the rows: in-wave by a reduce-scatter over the 16 row lanes, across the
-// 4 waves in wave order.
-template <int D>
-__global__ __launch_bounds__(256) void attn_mass_kernel(AttnArgs a, AttnPlan p) {
-  constexpr int MAXK = 32 * KT;  // keys per chunk (bounded by the host plan)
-  __shared__ u32x4 klds[2][KT * D / 8];
-  __shared__ float wsum[4][KT];
-  __shared__ float macc[MAXK];
+// Split path with the mass: pass 1 and the mass in one launch, the scores
+// kept on chip.  m[b][j] = sum_h sum_r exp2(x_rj - LSE_r) needs each row's
+// final log-sum-exp, which exists only once every key has been seen.  A
+// workgroup covers one KV split of kXSplitTiles tiles (1024 keys) of one
+// (sequence, 64-row tile, head) group, as attn_fwd does, and keeps its scaled
+// scores: kXRegTiles of a wave's tiles in registers, the rest in LDS.  When a
+// sequence's cache fits one split the workgroup has the LSE at the end of its
+// pass.  Otherwise the splits of the group exchange their row maxima and
+// normalisers: each publishes its (m, l) with device-coherent stores, waits
+// for its own stores to complete, counts itself in, and waits until all S_b
+// splits are in; each then forms the same LSE from the S_b pairs in split
+// order.  The keys are read once.  The unnormalised split outputs go to the
+// workspace and attn_xfinish merges them in split order.
+// Workgroups take their units from a ticket counter (cleared by
+// attn_xclear_kernel before the launch), so every unit with a lower ticket is
+// held by a running workgroup: a wait is only ever for a workgroup that is
+// running and does not wait for it.  Every wait is bounded; past the bound
+// the error word is set and the results of the call are invalid.
+constexpr int kXSplitTiles = 32;  // tiles (of KT keys) per split: 1024 keys
+constexpr int kXWaveTiles = kXSplitTiles / 2;
+constexpr int kXRegTiles = 11;    // of a wave's tiles, the scores held in registers
+constexpr int kXLdsTiles = kXWaveTiles - kXRegTiles;
+constexpr int kXSpinLimit = 1 << 16;  // polls: ~0.1 s, far beyond any pass
+constexpr int kXSyncHead = 4;     // ticket, error word, 2 spare; then one count per group
 
-  // Reverse order, blocks and tiles alike: pass 1 read the last units' last
-  // tiles most recently, so they are the likeliest still to sit in the
-  // last-level cache.  Per-key sums do not depend on this order.
-  int u = gridDim.x - 1 - blockIdx.x;
-  const int chunk = u % p.mass_splits; u /= p.mass_splits;
+// Completes this thread's outstanding memory operations (stores included:
+// on this architecture the vector memory counter covers both), with no
+// compiler motion of memory accesses across it.
+__device__ __forceinline__ void wait_mem() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); lgkmcnt, expcnt untouched
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ void store_agent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(256) void attn_xclear_kernel(int *sync, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    if (i != 1) sync[i] = 0;  // the error word stays as it is
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void attn_xmass_kernel(AttnArgs a, AttnPlan p) {
+  constexpr int NPF = kNpf;
+  __shared__ u32x4 klds[2][2][KT * D / 8 + 8];
+  __shared__ uint16_t vlds[2][2][KT][kVPad<D>];
+  __shared__ float sc_lds[8][kXLdsTiles][8][64];  // [wave][tile][element][lane]
+  __shared__ float s_tmax[2][kXWaveTiles][64];     // [key group][tile][row]
+  __shared__ int s_page[kXSplitTiles * KT / 32];   // block size >= 32
+  __shared__ float s_lse[64];
+  __shared__ int s_unit;
+
+  int *sync = reinterpret_cast<int *>(a.ws + p.off_sync);
+  if (p.splits > 1) {
+    if (threadIdx.x == 0)
+      s_unit = __hip_atomic_fetch_add(sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+  } else if (threadIdx.x == 0) {
+    s_unit = blockIdx.x;  // no waits: the launch order is enough
+  }
+  __syncthreads();
+  int u = s_unit;
+  const int S = p.splits;
+  const int split = u % S;
+  const int grp = u / S;  // (sequence, row tile, head)
+  u = grp;
   const int h = u % a.c.H;
-  const int b = u / a.c.H;
+  u /= a.c.H;
+  const int rt = u % p.row_tiles;
+  const int b = u / p.row_tiles;
   const SeqInfo si = seq_info(a, b);
+  const int t0 = rt * 64;
   const int tiles = (si.L + KT - 1) / KT;
-  const int tpc = (tiles + p.mass_splits - 1) / p.mass_splits;
-  const int tb = chunk * tpc, te = min(tiles, tb + tpc);
-  const int nrt = (si.nrows + 63) / 64;
-  if (tb >= te) return;
-  const int nkeys = max(0, te - tb) * KT;
+  const int Sb = max(1, (tiles + kXSplitTiles - 1) / kXSplitTiles);
+  if (t0 >= si.nrows || split >= Sb) return;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kg = wave >> 2, wr = wave & 3, gtid = threadIdx.x & 255;
   const int g = lane >> 4, j = lane & 15;
-  const float *lse_ws = reinterpret_cast<const float *>(a.ws + p.off_lse);
+  const int t = t0 + wr * 16 + j;  // local row of this lane
+  const bool row_ok = t < si.nrows;
+  const int r = si.r0 + (row_ok ? t : 0);
+  const int rl = wr * 16 + j;      // row of the lane inside the tile
+  const Vis vis = row_vis(si, t, row_ok);
 
-  __shared__ int s_page[kMaxPages];
+  const int tb = split * kXSplitTiles, te = min(tiles, tb + kXSplitTiles);
+  const int niter = (te - tb + 1) / 2;  // iterations per key group
+
   stage_pages(a, b, tb, te, s_page);
-  for (int k = threadIdx.x; k < nkeys; k += blockDim.x) macc[k] = 0.f;
   lds_barrier();
+  const int tlast = max(te - 1, tb);
+  u32x4 qf[D / 32];
+  load_q<D>(a, r, h, row_ok, g, qf);
 
-  for (int rt = 0; rt < nrt; ++rt) {
-    const int t = rt * 64 + wave * 16 + j;
-    const bool row_ok = t < si.nrows;
-    const int r = si.r0 + (row_ok ? t : 0);
-    const size_t rh = (size_t)r * a.c.H + h;
-    const Vis vis = row_vis(si, t, row_ok);
-    constexpr int MNPF = kMnpf;  // K tiles in flight
-    Tile<D> pf[MNPF];
+  f32x4 o[D / 16];
 #pragma unroll
-    for (int i = 0; i < MNPF; ++i)
-      load_tile<D>(pf[i], a, s_page, tb, h, max(te - 1 - i, tb) * KT, false, threadIdx.x);
-    u32x4 qf[D / 32];
-    load_q<D>(a, r, h, row_ok, g, qf);
-    float lr = kNegInf;
-    if (row_ok) lr = p.splits == 1 ? lse_ws[rh] : merge_row<4>(a, p, rh, D, 0, nullptr);
-    // A row that sees no key has LSE -inf; subtracting +inf instead sends
-    // every exp2 to 0.
-    const float lsafe = lr == kNegInf ? __builtin_huge_valf() : lr;
+  for (int dm = 0; dm < D / 16; ++dm) o[dm] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf, l = 0.f;
+  // fp32 probabilities of the wave's tiles, each against its tile's running
+  // maximum (kept in s_tmax)
+  float sc[kXRegTiles][8];
 
-    // Same uniform ring as pass 1: no branch around a load.
-    const int nt_r = (te - tb + MNPF - 1) / MNPF * MNPF;
-    for (int it0 = 0; it0 < nt_r; it0 += MNPF) {
+  // The same uniform ring as attn_fwd, unrolled over the wave's tiles so that
+  // every probability lands in a fixed register (or LDS slot).  An empty
+  // cache (no tile, no staged page) issues no load at all.
+  if (te > tb) {
+  Tile<D> pf[NPF];
 #pragma unroll
-    for (int ii = 0; ii < MNPF; ++ii) {
-      const int tile = te - 1 - (it0 + ii);  // descending
-      const bool have = tile >= tb;
-      const int buf = ii & 1;
-      store_tile<D>(pf[ii], klds[buf], nullptr, false, threadIdx.x);
-      load_tile<D>(pf[ii], a, s_page, tb, h, max(tile - MNPF, tb) * KT, false, threadIdx.x);
-      lds_barrier();
-      if (have) {
-      const int key0 = tile * KT;
-      const int tv = tile_vis(vis, key0);
-      float pv[8];
+  for (int i = 0; i < NPF; ++i)
+    load_tile<D>(pf[i], a, s_page, tb, h, min(tb + kg + 2 * i, tlast) * KT, true, gtid);
+#pragma unroll
+  for (int it = 0; it < kXWaveTiles; ++it) {
+    const int ii = it % NPF;
+    const int tile = tb + kg + 2 * it;
+    const bool have = it < niter && tile < te;
+    const int buf = it & 1;
+    store_tile<D>(pf[ii], klds[kg][buf], vlds[kg][buf], true, gtid, si.L - tile * KT);
+    load_tile<D>(pf[ii], a, s_page, tb, h, min(tile + 2 * NPF, tlast) * KT, true, gtid);
+    lds_barrier();
+    const int key0 = tile * KT;
+    const int tv = have ? tile_vis(vis, key0) : 0;
+    float pv[8], mt = 0.f;
+    if (tv != 0) {
+      f32x4 sv[2];
+      scores<D>(klds[kg][buf], qf, lane, sv);
+      const u32x4 pb = tile_softmax_pv<D / 16>(sv, vis, tv, key0, g, a.scale_log2, m, l, o, pv, mt);
+#pragma unroll
+      for (int dm = 0; dm < D / 16; ++dm)
+        o[dm] = mfma16(vt_operand<D>(vlds[kg][buf], dm, lane), pb, o[dm]);
+    } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) pv[e] = 0.f;
-      if (tv != 0) {
-        f32x4 s[2];
-        scores<D>(klds[buf], qf, lane, s);
+    }
+    if (g == 0) s_tmax[kg][it][rl] = mt;
+    if (it < kXRegTiles) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+      for (int e = 0; e < 8; ++e) sc[it < kXRegTiles ? it : 0][e] = pv[e];
+    } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = fast_exp2(s[mt][e] * a.scale_log2 - lsafe);
-            pv[mt * 4 + e] = (tv == 2 || vis(key0 + 8 * g + 4 * mt + e)) ? x : 0.f;
-          }
+      for (int e = 0; e < 8; ++e) sc_lds[wave][it - kXRegTiles][e][lane] = pv[e];
+    }
+  }
+  }
+
+  // Combine the two key groups: group 1's state through LDS (reusing the
+  // tiles), the maxima and normalisers first so that they can be published
+  // before the outputs are merged.
+  lds_barrier();
+  float *mo = reinterpret_cast<float *>(&klds[0][0][0]);  // [64 rows][D]
+  float *mml = mo + 64 * D;                                   // [64 rows][2]
+  static_assert((64 * D + 128) * 4 <= (int)sizeof(klds), "merge scratch");
+  if (kg == 1) {
+#pragma unroll
+    for (int dm = 0; dm < D / 16; ++dm)
+      *reinterpret_cast<f32x4 *>(&mo[rl * D + 16 * dm + 4 * g]) = o[dm];
+    if (g == 0) {
+      mml[2 * rl] = m;
+      mml[2 * rl + 1] = l;
+    }
+  }
+  lds_barrier();
+  float f0 = 0.f, f1 = 0.f;
+  if (kg == 0) {
+    const float m1 = mml[2 * rl], l1 = mml[2 * rl + 1];
+    const float mx = fmaxf(m, m1);
+    f0 = m == kNegInf ? 0.f : exp2f(m - mx);
+    f1 = m1 == kNegInf ? 0.f : exp2f(m1 - mx);
+    l = l * f0 + l1 * f1;
+    m = mx;
+  }
+  float *po = reinterpret_cast<float *>(a.ws + p.off_part_o);
+  float *pml = reinterpret_cast<float *>(a.ws + p.off_part_ml);
+  const size_t stride = (size_t)a.rows * a.c.H;
+  const size_t rh0 = (size_t)r * a.c.H + h;
+  int *count = sync + kXSyncHead + grp;
+  if (Sb > 1) {
+    // Publish this split's (m, l) with device-coherent stores, complete them,
+    // then count the split in.
+    if (kg == 0 && row_ok && g == 0) {
+      store_agent(&pml[2 * (split * stride + rh0)], m);
+      store_agent(&pml[2 * (split * stride + rh0) + 1], l);
+    }
+    wait_mem();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(count, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // The outputs, while the other splits arrive: the final (normalised) rows
+  // when the cache fits one split, else this split's unnormalised partial.
+  if (kg == 0 && row_ok) {
+#pragma unroll
+    for (int dm = 0; dm < D / 16; ++dm)
+      o[dm] = o[dm] * f0 + *reinterpret_cast<const f32x4 *>(&mo[rl * D + 16 * dm + 4 * g]) * f1;
+    if (Sb == 1) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      float *dst = a.out + rh0 * D + 4 * g;
+#pragma unroll
+      for (int dm = 0; dm < D / 16; ++dm) *reinterpret_cast<f32x4 *>(dst + 16 * dm) = o[dm] * inv;
+    } else {
+      float *dst = po + (split * stride + rh0) * D + 4 * g;
+#pragma unroll
+      for (int dm = 0; dm < D / 16; ++dm) *reinterpret_cast<f32x4 *>(dst + 16 * dm) = o[dm];
+    }
+  }
+
+  // The row's log-sum-exp over the whole cache.
+  float lse = kNegInf;
+  if (Sb == 1) {
+    if (kg == 0 && row_ok) lse = l > 0.f ? m + log2f(l) : kNegInf;
+  } else {
+    if (threadIdx.x == 0) {
+      int spins = 0;
+      while (__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < Sb) {
+        if (++spins > kXSpinLimit) {
+          __hip_atomic_store(sync + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
       }
-      // Reduce over the 16 rows of the wave (lanes sharing g): reduce-scatter.
-      const int b3 = (j >> 3) & 1, b2 = (j >> 2) & 1, b1 = (j >> 1) & 1;
+    }
+    __syncthreads();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (kg == 0 && row_ok) {
+      // Eight splits' pairs at a time, all loads in flight together; the
+      // chunks are combined in split order.
+      float mx = kNegInf, lsum = 0.f;
+      for (int s0 = 0; s0 < Sb; s0 += 8) {
+        float mv[8], lv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const size_t k = (size_t)min(s0 + i, Sb - 1) * stride + rh0;
+          mv[i] = load_agent(&pml[2 * k]);
+          lv[i] = load_agent(&pml[2 * k + 1]);
+        }
+        float cm = kNegInf;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cm = s0 + i < Sb ? fmaxf(cm, mv[i]) : cm;
+        const float nm = fmaxf(mx, cm);
+        if (nm != kNegInf) {
+          float cs = mx == kNegInf ? 0.f : lsum * exp2f(mx - nm);
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            cs += (s0 + i < Sb && mv[i] != kNegInf) ? lv[i] * exp2f(mv[i] - nm) : 0.f;
+          lsum = cs;
+        }
+        mx = nm;
+      }
+      lse = lsum > 0.f ? mx + log2f(lsum) : kNegInf;
+    }
+  }
+  if (kg == 0 && g == 0) s_lse[rl] = lse;
+  lds_barrier();
+  const float lr = s_lse[rl];
+
+  // Mass of the wave's keys over its 16 rows: each probability rescaled by
+  // its tile's factor exp2(mt - LSE), a reduce-scatter over the row lanes,
+  // then the 4 row groups added in order through LDS.
+  float *wsum = reinterpret_cast<float *>(&klds[0][0][0]);  // [4 row groups][kXSplitTiles * KT]
+  static_assert(4 * kXSplitTiles * KT * 4 <= (int)sizeof(klds), "mass scratch");
+  const int b3 = (j >> 3) & 1, b2 = (j >> 2) & 1, b1 = (j >> 1) & 1;
+#pragma unroll
+  for (int it = 0; it < kXWaveTiles; ++it) {
+    const int tile = tb + kg + 2 * it;
+    if (it < niter && tile < te) {
+      const float f = lr == kNegInf ? 0.f : fast_exp2(s_tmax[kg][it][rl] - lr);
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = it < kXRegTiles ? sc[it < kXRegTiles ? it : 0][e]
+                                        : sc_lds[wave][it < kXRegTiles ? 0 : it - kXRegTiles][e][lane];
+        pv[e] = x * f;
+      }
       float q4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -562,46 +914,72 @@ __global__ __launch_bounds__(256) void attn_mass_kernel(AttnArgs a, AttnPlan p) 
         const float keep = b2 ? q4[i + 2] : q4[i];
         q2[i] = keep + lane_xor4(give);
       }
-      float q1;
-      {
-        const float give = b1 ? q2[0] : q2[1];
-        const float keep = b1 ? q2[1] : q2[0];
-        q1 = keep + lane_xor2(give);
-      }
-      // Lanes l and l^1 now hold the same key; add them in a fixed order.
+      const float give = b1 ? q2[0] : q2[1];
+      const float keep = b1 ? q2[1] : q2[0];
+      const float q1 = keep + lane_xor2(give);
       const float other = lane_xor1(q1);
       const float tot = (j & 1) ? other + q1 : q1 + other;
-      if ((j & 1) == 0) wsum[wave][8 * g + 4 * b3 + 2 * b2 + b1] = tot;
-      }
-      lds_barrier();
-      if (have && threadIdx.x < KT) {
-        const int k = threadIdx.x;
-        const float sum = ((wsum[0][k] + wsum[1][k]) + wsum[2][k]) + wsum[3][k];
-        macc[(tile - tb) * KT + k] += sum;
-      }
+      if ((j & 1) == 0)
+        wsum[wr * (kXSplitTiles * KT) + (tile - tb) * KT + 8 * g + 4 * b3 + 2 * b2 + b1] = tot;
     }
-    }
-    lds_barrier();
   }
+  lds_barrier();
   float *mp = reinterpret_cast<float *>(a.ws + p.off_mass_part) +
-              ((size_t)b * a.c.H + h) * a.mass_stride;
-  for (int k = threadIdx.x; k < nkeys; k += blockDim.x) {
+              (((size_t)b * a.c.H + h) * p.row_tiles + rt) * a.mass_stride;
+  const int nk = (te - tb) * KT;
+  for (int k = threadIdx.x; k < nk; k += blockDim.x) {
     const int jj = tb * KT + k;
-    if (jj < si.L) mp[jj] = macc[k];
+    constexpr int W = kXSplitTiles * KT;
+    const float v = ((wsum[k] + wsum[W + k]) + wsum[2 * W + k]) + wsum[3 * W + k];
+    if (jj < si.L) mp[jj] = v;
   }
 }
 
-// Last launch of a mass-requesting call: blocks [0, nb_mass) add the per-head
-// partial masses in head order (mass[b][j]; the loads of 32 heads are issued
-// before their sum), blocks after that merge the KV-split partial outputs
-// (one thread per row, head and 4 features), when there are splits.
+// Sequence of row r: the largest b with cu_rows[b] <= r.
+__device__ __forceinline__ int attn_row_seq(const int32_t *cu_rows, int batch, int r) {
+  int lo = 0, hi = batch;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu_rows[mid] <= r) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Last launch of the split path with the mass: blocks [0, nb_mass) form
+// mass[b][j], the per-(head, row tile) partials added in head, then row-tile
+// order (zero from kv_len to the stride); the blocks after that merge the
+// split outputs of rows whose sequence took more than one split, in split
+// order (one thread per row, head and 4 features).
 template <int D>
-__global__ __launch_bounds__(256) void attn_finish_kernel(AttnArgs a, AttnPlan p, int nb_mass) {
+__global__ __launch_bounds__(256) void attn_xfinish_kernel(AttnArgs a, AttnPlan p, int nb_mass) {
   if ((int)blockIdx.x >= nb_mass) {
     const size_t idx = (size_t)(blockIdx.x - nb_mass) * blockDim.x + threadIdx.x;
     const size_t rh = idx / (D / 4);
     const int d4 = (int)(idx % (D / 4)) * 4;
-    if (rh < (size_t)active_rows(a) * a.c.H) merge_row<4>(a, p, rh, D, d4, a.out);
+    if (rh >= (size_t)active_rows(a) * a.c.H) return;
+    const int r = (int)(rh / a.c.H);
+    const int b = attn_row_seq(a.cu_rows, a.batch, r);
+    const int L = min(a.kv_len[b], a.max_kv_len);
+    const int Sb = max(1, ((L + KT - 1) / KT + kXSplitTiles - 1) / kXSplitTiles);
+    if (Sb == 1) return;  // written by the pass itself
+    const float *po = reinterpret_cast<const float *>(a.ws + p.off_part_o);
+    const float *pml = reinterpret_cast<const float *>(a.ws + p.off_part_ml);
+    const size_t stride = (size_t)a.rows * a.c.H;
+    float mx = kNegInf;
+    for (int s = 0; s < Sb; ++s) mx = fmaxf(mx, pml[2 * (s * stride + rh)]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f;
+    if (mx != kNegInf) {
+      for (int s = 0; s < Sb; ++s) {
+        const size_t k = s * stride + rh;
+        const float ms = pml[2 * k];
+        const float f = ms == kNegInf ? 0.f : exp2f(ms - mx);
+        lsum += pml[2 * k + 1] * f;
+        acc += *reinterpret_cast<const f32x4 *>(po + k * D + d4) * f;
+      }
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    *reinterpret_cast<f32x4 *>(a.out + rh * D + d4) = acc * inv;
     return;
   }
   const int per_b = (a.mass_stride + 255) / 256;
@@ -609,17 +987,24 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnArgs a, AttnPlan p
   const int jj = (blockIdx.x % per_b) * blockDim.x + threadIdx.x;
   if (jj >= a.mass_stride) return;
   const int L = min(a.kv_len[b], a.max_kv_len);
+  const int nrt = min(p.row_tiles, (a.cu_rows[b + 1] - a.cu_rows[b] + 63) / 64);
   float sum = 0.f;
   if (jj < L) {
     const float *mp = reinterpret_cast<const float *>(a.ws + p.off_mass_part) +
-                      (size_t)b * a.c.H * a.mass_stride + jj;
+                      (size_t)b * a.c.H * p.row_tiles * a.mass_stride + jj;
     for (int h0 = 0; h0 < a.c.H; h0 += 32) {
       float v[32];
+      if (nrt == 1) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = h0 + i < a.c.H ? mp[(size_t)(h0 + i) * a.mass_stride] : 0.f;
+        for (int i = 0; i < 32; ++i)
+          v[i] = h0 + i < a.c.H ? mp[(size_t)(h0 + i) * p.row_tiles * a.mass_stride] : 0.f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i)
-        if (h0 + i < a.c.H) sum += v[i];
+        for (int i = 0; i < 32; ++i) sum += v[i];
+      } else {
+        for (int i = 0; i < 32 && h0 + i < a.c.H; ++i)
+          for (int q = 0; q < nrt; ++q)
+            sum += mp[((size_t)(h0 + i) * p.row_tiles + q) * a.mass_stride];
+      }
     }
   }
   a.mass[(size_t)b * a.mass_stride + jj] = sum;
@@ -941,6 +1326,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // merge and the second pass over K, which at that size cost more than the
 // row groups' repeated reads of the head's keys (served from L2).
 constexpr long kRowsMaxGrid = 256;
+// Split path with the mass: (sequence, row tile, head) units from which one
+// workgroup per unit (attn_fwd_kernel<D, true>) fills the GPU.
+constexpr long kFwdMassMinUnits = 256;
 
 AttnPlan plan_attention(int batch, int rows, int H, int D, int max_kv_len,
                         int max_rows_per_seq, int mass_stride) {
@@ -961,29 +1349,48 @@ AttnPlan plan_attention(int batch, int rows, int H, int D, int max_kv_len,
     return p;
   }
   p.row_tiles = max(1, (max_rows_per_seq + 63) / 64);
+  size_t off = 0;
+  if (mass) {
+    p.xmass = 1;
+    const long units = (long)batch * p.row_tiles * H;
+    if (max_tiles > kXSplitTiles && units >= kFwdMassMinUnits) {
+      // Long caches and enough units to fill the GPU: one workgroup per
+      // unit, the mass as a second pass over K right after the first
+      // (attn_fwd_kernel<D, true>).
+      p.fwd_mass = 1;
+      p.splits = 1;
+      p.off_mass_part = 0;
+      p.bytes = align256((size_t)batch * H * p.row_tiles * mass_stride * sizeof(float));
+      return p;
+    }
+    // Otherwise pass 1 and the mass in one launch with the scores on chip
+    // (attn_xmass): one split per 1024 keys, the splits of a long cache
+    // exchanging their row statistics.
+    p.splits = (max_tiles + kXSplitTiles - 1) / kXSplitTiles;
+    if (p.splits > 1) {
+      p.off_sync = 0;  // first, so the error word sits at byte 4 of the workspace
+      p.sync_ints = kXSyncHead + batch * p.row_tiles * H;
+      off = align256((size_t)p.sync_ints * sizeof(int));
+      p.off_part_o = off;
+      off = align256(off + (size_t)p.splits * rows * H * D * sizeof(float));
+      p.off_part_ml = off;
+      off = align256(off + (size_t)p.splits * rows * H * 2 * sizeof(float));
+    }
+    p.off_mass_part = off;
+    off = align256(off + (size_t)batch * H * p.row_tiles * mass_stride * sizeof(float));
+    p.bytes = off;
+    return p;
+  }
   const long base = (long)batch * p.row_tiles * H;
   constexpr long kUnits = 128;  // target (sequence, row tile, head, split) units
   int splits = (int)((kUnits + base - 1) / max(base, 1L));
   splits = max(1, min(splits, (max_tiles + 1) / 2));
   p.splits = splits;
-  if (mass_stride > 0) {
-    const long mb = (long)batch * H;
-    int ms = (int)((1024 + mb - 1) / max(mb, 1L));
-    ms = max(ms, (max_tiles + 31) / 32);  // at most 32 tiles per chunk (LDS accumulator)
-    p.mass_splits = max(1, min(ms, max_tiles));
-  }
-  size_t off = 0;
   if (p.splits > 1) {
     p.off_part_o = off;
     off = align256(off + (size_t)p.splits * rows * H * D * sizeof(float));
     p.off_part_ml = off;
     off = align256(off + (size_t)p.splits * rows * H * 2 * sizeof(float));
-  }
-  if (p.mass_splits) {
-    p.off_lse = off;
-    off = align256(off + (size_t)rows * H * sizeof(float));
-    p.off_mass_part = off;
-    off = align256(off + (size_t)batch * H * mass_stride * sizeof(float));
   }
   p.bytes = off;
   return p;
@@ -1009,17 +1416,47 @@ hipError_t launch_rows(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_xmass(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
+  if (p.fwd_mass) {
+    const int units = a.batch * p.row_tiles * a.c.H;
+    hipLaunchKernelGGL((attn_fwd_kernel<D, true>), dim3(units), dim3(512), 0, s, a, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nb_mass = a.batch * ((a.mass_stride + 255) / 256);
+    hipLaunchKernelGGL(attn_xfinish_kernel<D>, dim3(nb_mass), dim3(256), 0, s, a, p, nb_mass);
+    return hipGetLastError();
+  }
+  if (p.splits > 1) {
+    int *sync = reinterpret_cast<int *>(a.ws + p.off_sync);
+    hipLaunchKernelGGL(attn_xclear_kernel, dim3((p.sync_ints + 255) / 256), dim3(256), 0, s, sync,
+                       p.sync_ints);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int units = a.batch * p.row_tiles * a.c.H * p.splits;
+  hipLaunchKernelGGL(attn_xmass_kernel<D>, dim3(units), dim3(512), 0, s, a, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nb_mass = a.batch * ((a.mass_stride + 255) / 256);
+  const size_t mthreads = p.splits > 1 ? (size_t)a.rows * a.c.H * (D / 4) : 0;
+  const int nb = nb_mass + (int)((mthreads + 255) / 256);
+  hipLaunchKernelGGL(attn_xfinish_kernel<D>, dim3(nb), dim3(256), 0, s, a, p, nb_mass);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
   if (p.rows_path) return a.c.D == 128 ? launch_rows<128>(a, p, s) : launch_rows<64>(a, p, s);
+  if (p.xmass) return a.c.D == 128 ? launch_xmass<128>(a, p, s) : launch_xmass<64>(a, p, s);
   const int units = a.batch * p.row_tiles * a.c.H * p.splits;
   if (a.c.D == 128) {
-    hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(units), dim3(512), 0, s, a, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<128, false>), dim3(units), dim3(512), 0, s, a, p);
   } else {
-    hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(units), dim3(512), 0, s, a, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<64, false>), dim3(units), dim3(512), 0, s, a, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.splits > 1 && !p.mass_splits) {
+  if (p.splits > 1) {
     const size_t threads = (size_t)a.rows * a.c.H * (a.c.D / 4);
     const unsigned blocks = (unsigned)((threads + 255) / 256);
     if (blocks) {
@@ -1029,22 +1466,6 @@ hipError_t launch_attention(const AttnArgs &a, const AttnPlan &p, hipStream_t s)
         hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(blocks), dim3(256), 0, s, a, p);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-  }
-  if (p.mass_splits) {
-    const int mu = a.batch * a.c.H * p.mass_splits;
-    if (a.c.D == 128)
-      hipLaunchKernelGGL(attn_mass_kernel<128>, dim3(mu), dim3(256), 0, s, a, p);
-    else
-      hipLaunchKernelGGL(attn_mass_kernel<64>, dim3(mu), dim3(256), 0, s, a, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int nb_mass = a.batch * ((a.mass_stride + 255) / 256);
-    const size_t mthreads = p.splits > 1 ? (size_t)a.rows * a.c.H * (a.c.D / 4) : 0;
-    const int nb = nb_mass + (int)((mthreads + 255) / 256);
-    if (a.c.D == 128)
-      hipLaunchKernelGGL(attn_finish_kernel<128>, dim3(nb), dim3(256), 0, s, a, p, nb_mass);
-    else
-      hipLaunchKernelGGL(attn_finish_kernel<64>, dim3(nb), dim3(256), 0, s, a, p, nb_mass);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
 }

@@ -36,9 +36,11 @@ struct AttnPlan {
   int rgroups;        // ceil(max_rows_per_seq / 16), row-group path
   int maxt;           // tiles per wave kept for the mass, row-group path
   int row_tiles;      // ceil(max_rows_per_seq / 64), split path
-  int splits;         // KV splits of the first pass, split path
-  int mass_splits;    // KV chunks of the mass pass (0: no mass), split path
-  size_t off_part_o, off_part_ml, off_lse, off_mass_part, bytes;
+  int splits;         // KV splits per (sequence, row tile, head), split path
+  int xmass;          // 1: split path with the mass
+  int fwd_mass;       // xmass by one workgroup per unit with a second pass over K (long caches)
+  int sync_ints;      // xmass with splits > 1: ticket, error word, one count per group
+  size_t off_part_o, off_part_ml, off_mass_part, off_sync, bytes;
 };
 
 AttnPlan plan_attention(int batch, int rows, int H, int D, int max_kv_len,

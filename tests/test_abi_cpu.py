@@ -212,3 +212,19 @@ def test_fused_step_validation(lib):
     # a narrow layer at 40 rows splits its projection's reduction: not one launch
     assert call() == _lib.FDL_EUNSUPPORTED
     assert call(hid=200) == _lib.FDL_EUNSUPPORTED        # as flash_cache_step
+
+
+def test_attention_path_selection(lib):
+    """The planner's choice for the workload shapes (host only)."""
+    import kv_cache_attention_flash_amd as fd
+    # batch-1 layer, cache 768, mass: row groups
+    assert fd.attention_path(1, 64, 32, 128, 768, 64, 768) == "row_groups"
+    # batch 32 ragged up to 1024 keys, mass: scores on chip, one split per sequence
+    assert fd.attention_path(32, 2048, 32, 128, 1024, 64, 1024) == "split_mass_exchange"
+    # two-view batch 8, no mass: split path with merges
+    assert fd.attention_path(8, 512, 32, 128, 1056, 64, 0) == "split"
+    # 32-layer stack's layer: batch 16, cache 4096, 512 units: second pass over K
+    assert fd.attention_path(16, 1024, 32, 128, 4096, 64, 4096) == "split_mass_reread"
+    # long caches with few units: splits exchanging row statistics
+    assert fd.attention_path(2, 48, 2, 64, 1500, 24, 1500) == "split_mass_exchange"
+    assert lib.fdl_attention_path(-1, 0, 1, 64, 0, 0, 0) == 0

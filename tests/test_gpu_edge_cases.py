@@ -87,6 +87,50 @@ def test_deterministic_reruns():
     assert torch.equal(a.cache.k_cache, b.cache.k_cache)
 
 
+@pytest.mark.parametrize("name", ["small_long_l1500", "long_b4_l4096"])
+def test_exchange_path_reruns_and_workspace(name):
+    """The split path whose splits exchange row statistics (caches past 1024
+    keys, mass asked for): bitwise the same results on three calls in a row
+    through one workspace that starts filled with garbage (the call clears its
+    own counters), and on a fresh workspace; the error word stays 0; the
+    output and mass agree with the oracle."""
+    import kv_cache_attention_flash_amd as fd
+    fd.load()
+    dev = "cuda:0"
+    if name == "long_b4_l4096":
+        g = np.random.default_rng(7)
+        specs = [SeqSpec(kv_len=4096 - 37 * b, window=(int(g.integers(32, 3000)), 32),
+                         tracked=tuple(sorted(int(p) for p in g.choice(32, 32, replace=False))))
+                 for b in range(4)]
+        wl = synth.build(name, 25, 512, 8, 128, 32, 5.0e5, specs, topb=32)
+    else:
+        wl = synth.WORKLOADS[name]()
+    _banner(f"exchange path {name}: lengths {wl.kv_len.tolist()}")
+    run = G.GpuRun(wl, dev)
+    q, sm = fd.flash_cache_step(run.cache, run.x, run.w, run.cu, run.pos, run.slots, wl.rope_base)
+    need = fd.attention_workspace_bytes(wl.batch, wl.rows, wl.num_heads, wl.head_dim,
+                                        wl.max_kv_len, run.max_rows, wl.max_kv_len)
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device=dev)
+    ws[fd.ATTENTION_ERROR_OFFSET:fd.ATTENTION_ERROR_OFFSET + 4] = 0
+    outs = []
+    for _ in range(3):
+        o, m = fd.scheduled_attention(run.cache, q, run.cu, run.kv_len, wl.max_kv_len,
+                                      run.max_rows, views=run.views, want_mass=True,
+                                      workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((o.clone(), m.clone()))
+    assert fd.attention_error(ws) == 0
+    o4, m4 = fd.scheduled_attention(run.cache, q, run.cu, run.kv_len, wl.max_kv_len,
+                                    run.max_rows, views=run.views, want_mass=True)
+    torch.cuda.synchronize()
+    for o, m in outs[1:] + [(o4, m4)]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(m, outs[0][1])
+    idx = fd.track_topb(m4, run.kv_len, wl.topb)
+    torch.cuda.synchronize()
+    run.q, run.out, run.mass, run.idx, run.slot_mapping = q, o4, m4, idx, sm
+    full_check(wl, run=run)
+
+
 def test_block_permutation_invariance():
     _banner("block-table permutation invariance")
     wl = synth.small_ragged()
@@ -274,3 +318,50 @@ def test_unfused_ablation_is_bitwise_equal(name):
                      G.bits_of(run.cache.v_cache)))
     for what, a_, b_ in zip(("q", "slot mapping", "K cache", "V cache"), outs[0], outs[1]):
         assert np.array_equal(a_, b_), what
+
+
+@pytest.mark.parametrize("case", ["d64_b16_h16", "d128_b8_h32_views"])
+def test_second_pass_mass_path(case):
+    """Caches past 1024 keys with enough sequences x heads for one workgroup
+    per unit: the mass comes from a second, last-first pass over K in the same
+    workgroup.  Ragged lengths (not multiples of the block size), two row tiles
+    in some sequences, two-view sequences; element-wise against the oracle,
+    and bitwise equal on a rerun."""
+    import kv_cache_attention_flash_amd as fd
+    fd.load()
+    g = np.random.default_rng(31 if case.startswith("d64") else 32)
+    specs = []
+    if case == "d64_b16_h16":
+        for b in range(16):
+            L = int(g.integers(1030, 2200))
+            w = int(g.integers(8, 49))
+            w0 = int(g.integers(0, L - w))
+            pool = [p for p in range(L) if not (w0 <= p < w0 + w)]
+            nt = int(g.integers(0, 41))
+            tr = tuple(sorted(int(p) for p in g.choice(pool, size=nt, replace=False)))
+            specs.append(SeqSpec(kv_len=L, window=(w0, w), tracked=tr))
+        wl = synth.build("reread_d64", 26, 256, 16, 64, 64, 1.0e4, specs, topb=16)
+    else:
+        for b in range(8):
+            L = int(g.integers(1100, 1800))
+            if b % 3 == 0:
+                ctx = L - 16
+                w0 = int(g.integers(0, ctx - 16))
+                specs.append(SeqSpec(kv_len=L, window=(w0, 16), tracked=(), draft_start=ctx))
+            else:
+                w0 = int(g.integers(32, L - 32))
+                tr = tuple(sorted(int(p) for p in g.choice(w0, 32, replace=False)))
+                specs.append(SeqSpec(kv_len=L, window=(w0, 32), tracked=tr))
+        wl = synth.build("reread_d128", 27, 512, 32, 128, 32, 5.0e5, specs, topb=32)
+    run = G.GpuRun(wl, "cuda:0")
+    path = fd.attention_path(wl.batch, wl.rows, wl.num_heads, wl.head_dim, wl.max_kv_len,
+                             run.max_rows, wl.max_kv_len)
+    _banner(f"second-pass mass {case}: lengths {wl.kv_len.tolist()}, path {path}")
+    assert path == "split_mass_reread"
+    run.step()
+    a_out, a_mass = run.out.clone(), run.mass.clone()
+    full_check(wl, run=run)
+    o2, m2 = fd.scheduled_attention(run.cache, run.q, run.cu, run.kv_len, wl.max_kv_len,
+                                    run.max_rows, views=run.views, want_mass=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, a_out) and torch.equal(m2, a_mass)

@@ -8,6 +8,12 @@ lengths, windows and tracked rows (some sequences two-view), and a top-B
 budget (zero leaves out the mass, which moves attention to the split path).
 The rows total crosses 64 in some cases, so both projection kernels and both
 attention paths occur.
+
+A second family draws long caches (up to 3500 slots, lengths on and next to
+the 1024-key split boundaries) with the mass always asked for: attention then
+takes the split path whose splits exchange their row statistics (more than
+one split per sequence), with up to 88 rows per sequence (two row tiles),
+both head sizes, block sizes up to 256 and two-view sequences.
 """
 
 import numpy as np
@@ -67,4 +73,54 @@ def test_random_shape(seed):
     print(f"[random] seed {seed}: rows {wl.rows}, batch {wl.batch}, {wl.num_heads}x{wl.head_dim}, "
           f"hidden {wl.hid}, block {wl.block_size}, topb {wl.topb}, "
           f"views {wl.views is not None}", flush=True)
+    full_check(wl)
+
+
+LONG_CASES = 24
+
+
+def random_long_workload(seed):
+    g = np.random.default_rng(5000 + seed)
+    heads = int(g.choice([1, 2, 3, 4]))
+    dim = int(g.choice([64, 128]))
+    hid = int(g.choice([256, 384, 512]))
+    bs = int(g.choice([32, 64, 128, 256]))
+    batch = int(g.integers(1, 5))
+    two_view = g.random() < 0.3
+    specs = []
+    for _ in range(batch):
+        if g.random() < 0.3:
+            length = int(g.choice([1024, 1025, 2047, 2048, 2049, 3072]))
+        else:
+            length = int(g.integers(700, 3501))
+        if two_view and g.random() < 0.6:
+            w = int(g.integers(1, 33))
+            ctx = length - w
+            w0 = int(g.integers(0, ctx - w + 1))
+            pool = [p for p in range(ctx) if not (w0 <= p < w0 + w)]
+            nt = int(g.integers(0, 17))
+            tr = tuple(sorted(int(p) for p in g.choice(pool, size=nt, replace=False))) if nt else ()
+            specs.append(synth.SeqSpec(kv_len=length, window=(w0, w), tracked=tr,
+                                       draft_start=ctx))
+        else:
+            w = int(g.integers(0, 49))
+            w0 = int(g.integers(0, length - w + 1))
+            pool = [p for p in range(length) if not (w0 <= p < w0 + w)]
+            nt = int(g.integers(0, 41))
+            tr = tuple(sorted(int(p) for p in g.choice(pool, size=nt, replace=False))) if nt else ()
+            specs.append(synth.SeqSpec(kv_len=length, window=(w0, w), tracked=tr))
+    topb = int(g.choice([4, 8, 16, 32]))
+    return synth.build(f"random_long_{seed}", 200 + seed, hid, heads, dim, bs, 1.0e4, specs,
+                       topb=topb)
+
+
+@pytest.mark.parametrize("seed", range(LONG_CASES))
+def test_random_long_cache(seed):
+    wl = random_long_workload(seed)
+    if wl.rows == 0:
+        pytest.skip("no active rows drawn")
+    print(f"[random-long] seed {seed}: rows {wl.rows}, batch {wl.batch}, "
+          f"{wl.num_heads}x{wl.head_dim}, hidden {wl.hid}, block {wl.block_size}, "
+          f"lengths {wl.kv_len.tolist()}, topb {wl.topb}, views {wl.views is not None}",
+          flush=True)
     full_check(wl)
