@@ -55,7 +55,8 @@ enum {
   FDL_EINVAL = 1,       /* null pointer, negative or inconsistent size */
   FDL_EUNSUPPORTED = 2, /* shape outside the supported set above */
   FDL_EWORKSPACE = 3,   /* workspace smaller than fdl_attention_workspace_bytes() */
-  FDL_EHIP = 4          /* a HIP launch failed; see fdl_last_hip_error() */
+  FDL_EHIP = 4,         /* a HIP launch failed; see fdl_last_hip_error() */
+  FDL_ESCRATCH = 5      /* the sizes need more scratch than the static buffer holds */
 };
 
 /* Paged KV cache of one layer [P4 para 1: keys and values written directly into
@@ -192,6 +193,31 @@ int scheduled_attention(const fdl_kv_cache *cache, const void *q, int32_t batch,
                         float softmax_scale, float *out, float *mass,
                         int32_t mass_stride, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/* scheduled_attention for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, semantics and results (the same kernels) as
+ * scheduled_attention, without the workspace: its scratch is one static
+ * device buffer of fdl_static_scratch_bytes() bytes (16 MiB) per GPU, held by
+ * the library until the process ends; its address is looked up once per
+ * device (the first call on it) and no call allocates or frees memory.
+ *   Sizes whose fdl_attention_workspace_bytes(...) exceeds that buffer are
+ *   refused with FDL_ESCRATCH before anything is launched.
+ *   The buffer belongs to the current device; `stream` must be a stream of
+ *   that device.  Every call on a GPU uses the same buffer, which keeps the
+ *   previous call's contents (the call clears what must start at zero):
+ *   calls that overlap on one GPU (other streams, other host threads) race
+ *   and must not be issued.  The error word of the exchange path (see
+ *   scheduled_attention) is byte 4 of the buffer. */
+int scheduled_attention_static(const fdl_kv_cache *cache, const void *q, int32_t batch,
+                               int32_t num_rows, const int32_t *cu_rows,
+                               const int32_t *kv_len, int32_t max_kv_len,
+                               int32_t max_rows_per_seq, const fdl_two_view *views,
+                               float softmax_scale, float *out, float *mass,
+                               int32_t mass_stride, void *stream);
+
+/* Size in bytes of scheduled_attention_static's static scratch buffer. */
+size_t fdl_static_scratch_bytes(void);
 
 /* The kernels scheduled_attention uses for these sizes (mass_stride 0 = no
  * mass); the results agree on every path within float rounding:

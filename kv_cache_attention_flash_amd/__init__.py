@@ -40,7 +40,8 @@ __all__ = ["PagedKVCache", "flash_cache_step", "flash_cache_step_unfused", "sche
            "flash_cache_workspace_bytes", "flash_cache_unfused_workspace_bytes", "DecodeStep",
            "decode_plan", "gather_hidden", "DecodeLoop", "lm_head_confidence",
            "lm_head_workspace_bytes", "flash_cache_attention_step", "fused_step_workspace_bytes",
-           "fused_step_error", "attention_error", "attention_path", "FdlError", "load"]
+           "fused_step_error", "attention_error", "attention_path", "scheduled_attention_static",
+           "static_scratch_bytes", "FdlError", "load"]
 
 
 def load():
@@ -290,6 +291,40 @@ def attention_error(workspace: torch.Tensor, stream=None) -> int:
     with _on_stream(sh, workspace.device):
         word = workspace[ATTENTION_ERROR_OFFSET:ATTENTION_ERROR_OFFSET + 4].view(torch.int32).item()
     return int(word)
+
+
+def static_scratch_bytes() -> int:
+    return int(_lib.load().fdl_static_scratch_bytes())
+
+
+def scheduled_attention_static(cache: PagedKVCache, q, cu_rows, kv_len, max_kv_len,
+                               max_rows_per_seq, out, mass=None, views=None, softmax_scale=0.0,
+                               stream=None):
+    """scheduled_attention without a workspace, for callers that cannot
+    allocate: the library's static per-GPU scratch buffer stands in for it
+    (include/fdllm.h).  Nothing is allocated here either: ``out`` (and
+    ``mass`` when the mass is wanted) must be given.  Returns (out, mass)."""
+    lib = _lib.load()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(cu_rows, "cu_rows", torch.int32, 1)
+    _need(kv_len, "kv_len", torch.int32, 1)
+    _need(out, "out", torch.float32, 3)
+    batch = kv_len.numel()
+    if cu_rows.numel() != batch + 1:
+        raise ValueError("cu_rows must have batch + 1 entries")
+    if views is not None:
+        _need(views, "views", torch.int32, 2)
+    ms = 0
+    if mass is not None:
+        _need(mass, "mass", torch.float32, 2)
+        ms = mass.shape[1]
+    cs = cache.struct()
+    st = lib.scheduled_attention_static(ctypes.byref(cs), q.data_ptr(), batch, q.shape[0],
+                                        cu_rows.data_ptr(), kv_len.data_ptr(), int(max_kv_len),
+                                        int(max_rows_per_seq), _ptr(views), float(softmax_scale),
+                                        out.data_ptr(), _ptr(mass), ms, _stream(stream, q.device))
+    _lib.check("scheduled_attention_static", st)
+    return out, mass
 
 
 def track_topb(mass, kv_len, topb, out=None, stream=None):

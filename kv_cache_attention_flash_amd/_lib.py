@@ -17,7 +17,7 @@ import torch  # noqa: F401  (loads the process's HIP runtime before the library)
 LIB_PATH = os.environ.get("FDL_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                      "libfdllm.so")
 
-FDL_OK, FDL_EINVAL, FDL_EUNSUPPORTED, FDL_EWORKSPACE, FDL_EHIP = 0, 1, 2, 3, 4
+FDL_OK, FDL_EINVAL, FDL_EUNSUPPORTED, FDL_EWORKSPACE, FDL_EHIP, FDL_ESCRATCH = 0, 1, 2, 3, 4, 5
 
 c_i32, c_i64, c_f32, c_size, c_vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                                      ctypes.c_size_t, ctypes.c_void_p)
@@ -43,6 +43,10 @@ EXPORTS = {
                                            c_vp, c_size, c_vp]),
     "fdl_attention_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "fdl_attention_path": (ctypes.c_int, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "scheduled_attention_static": (ctypes.c_int, [ctypes.POINTER(KVCacheStruct), c_vp, c_i32, c_i32,
+                                                  c_vp, c_vp, c_i32, c_i32, c_vp, c_f32, c_vp, c_vp,
+                                                  c_i32, c_vp]),
+    "fdl_static_scratch_bytes": (c_size, []),
     "track_topb": (ctypes.c_int, [c_vp, c_i32, c_vp, c_i32, c_i32, c_vp, c_vp]),
     "verify_accept": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i32, c_i32, c_f32, c_vp, c_vp]),
     "decode_plan": (ctypes.c_int, [c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp,

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdlib>
+#include <mutex>
 #include <vector>
 
 #include "../../include/fdllm.h"
@@ -145,6 +146,8 @@ const char *fdl_status_string(int status) {
     case FDL_EUNSUPPORTED: return "unsupported shape (head_dim, block_size or hidden)";
     case FDL_EWORKSPACE: return "workspace too small";
     case FDL_EHIP: return "HIP launch failed";
+    case FDL_ESCRATCH:
+      return "sizes need more scratch than the static buffer holds (fdl_static_scratch_bytes)";
     default: return "unknown status";
   }
 }
@@ -310,6 +313,74 @@ size_t fdl_attention_workspace_bytes(int32_t batch, int32_t num_rows, int32_t nu
   return fdl::plan_attention(batch, num_rows, num_heads, head_dim, max_kv_len, max_rows_per_seq,
                              mass_stride)
       .bytes;
+}
+
+}  // extern "C"
+
+namespace {
+
+// scheduled_attention_static's scratch: one static device buffer per GPU
+// (each device holds its own copy of the array, at its own address).  In host
+// code `scratch` names a host-side stand-in, never device memory: kernels and
+// copies get the per-device address from hipGetSymbolAddress.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on the device's first
+// call, with the device current); nullptr and a HIP status on failure.
+void *device_scratch(hipError_t &err) {
+  int dev = 0;
+  err = hipGetDevice(&dev);
+  if (err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !p) {
+      if (err == hipSuccess) err = hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fdl_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+int scheduled_attention_static(const fdl_kv_cache *cache, const void *q, int32_t batch,
+                               int32_t num_rows, const int32_t *cu_rows, const int32_t *kv_len,
+                               int32_t max_kv_len, int32_t max_rows_per_seq,
+                               const fdl_two_view *views, float softmax_scale, float *out,
+                               float *mass, int32_t mass_stride, void *stream) {
+  fdl::AttnArgs a;
+  fdl::AttnPlan plan;
+  int empty;
+  int st = attn_args(cache, q, batch, num_rows, cu_rows, kv_len, max_kv_len, max_rows_per_seq,
+                     views, softmax_scale, out, mass, mass_stride, a, plan, empty);
+  if (st || empty == 1) return st;
+  if (plan.bytes > kStaticScratchBytes) return FDL_ESCRATCH;
+  if (empty) return FDL_OK;
+  if (debug_mode() &&
+      (st = debug_check_attention(cache, batch, num_rows, cu_rows, kv_len, max_kv_len,
+                                  max_rows_per_seq, views, static_cast<hipStream_t>(stream))))
+    return st;
+  hipError_t err;
+  void *ws = device_scratch(err);
+  if (!ws) return hip_status(err);
+  a.ws = static_cast<char *>(ws);
+  return hip_status(fdl::launch_attention(a, plan, static_cast<hipStream_t>(stream)));
 }
 
 int fdl_attention_path(int32_t batch, int32_t num_rows, int32_t num_heads, int32_t head_dim,

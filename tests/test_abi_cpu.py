@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         s = lib.fdl_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.fdl_status_string(99).decode() == "unknown status"
