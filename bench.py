@@ -566,7 +566,10 @@ def main():
                          "known size that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--fused", action="store_true",
                     help="time flash_cache_attention_step (projection, attention and mass in one "
-                         "launch) in place of the two calls")
+                         "call) in place of the two calls")
+    ap.add_argument("--single-launch", action="store_true",
+                    help="time flash_cache_attention_step_single_launch (projection, attention "
+                         "and mass in one persistent launch) in place of the two calls")
     ap.add_argument("--loop", action="store_true",
                     help="time the multi-step decode loop (batch 32, planned on the device) and "
                          "report steps/s instead of the single-step metric")
@@ -626,7 +629,8 @@ def main():
     def make_step(cache, x, w):
         return fd.DecodeStep(cache, x, w, cu, pos, slots, kv, wl.rope_base, wl.max_kv_len,
                              max_rows, views=views, topb=wl.topb, verify=verify,
-                             unfused=args.unfused, fused=args.fused)
+                             unfused=args.unfused, fused=args.fused,
+                             single_launch=args.single_launch)
 
     # units[i % len(units)] = the per-layer steps that make up logical step i
     units = []
@@ -684,12 +688,12 @@ def main():
     for i in range(K):
         for st, e in zip(units[i % len(units)], ev[i]):
             ht.record(e[0], sh)
-            if args.fused:
-                st.run_fused(sh)  # one launch: its time is booked to the first bracket
+            if args.fused or args.single_launch:
+                st.run_fused(sh)  # one call: its time is booked to the first bracket
             else:
                 st.run_flash_cache(sh)
             ht.record(e[1], sh)
-            if not args.fused:
+            if not (args.fused or args.single_launch):
                 st.run_attention(sh)
             ht.record(e[2], sh)
             st.run_topb(sh)
@@ -705,13 +709,14 @@ def main():
     rf_fc = roofline_entry(fc_call, wl, fcs_ms, args.workload)
     rf_att = roofline_entry("scheduled_attention", wl, att_ms, args.workload)
     dominant, other = (rf_fc, rf_att) if fcs_ms >= att_ms else (rf_att, rf_fc)
-    if args.fused:
-        # one launch: its algorithmic bytes are both calls' (HBM-bound at this AI)
+    if args.fused or args.single_launch:
+        # one call: its algorithmic bytes are both calls' (HBM-bound at this AI)
         nb_f = step_bytes(wl)
         ach = nb_f / (fcs_ms / 1e3) / 1e9
         dominant = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernel": "flash_cache_attention_step", "algorithmic_bytes": nb_f,
+                    "kernel": ("flash_cache_attention_step_single_launch" if args.single_launch
+                               else "flash_cache_attention_step"), "algorithmic_bytes": nb_f,
                     "algorithmic_flops": flash_cache_flops(wl) + attention_flops(wl),
                     "avg_launch_us": round(fcs_ms * 1e3, 2)}
         other = None
@@ -752,8 +757,11 @@ def main():
     tail = (" + scheduled_attention(+mass) + track_topb" if wl.topb else " + scheduled_attention")
     if args.unfused:
         tail += " [ablation: flash_cache_step_unfused, three launches with HBM intermediates]"
-    if args.fused:
-        tail += (" [flash_cache_attention_step: projection, attention and mass in one launch; "
+    if args.single_launch:
+        tail += (" [flash_cache_attention_step_single_launch: projection, attention and mass in "
+                 "one persistent launch; its whole time is in the flash_cache_step bracket]")
+    elif args.fused:
+        tail += (" [flash_cache_attention_step: projection, attention and mass in one call; "
                  "its whole time is in the flash_cache_step bracket]")
     tail += " + verify_accept" if verify is not None else ""
     line = {

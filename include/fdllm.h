@@ -268,18 +268,43 @@ int verify_accept(const int32_t *draft_tok, const int32_t *mask_tok,
                   const float *conf, int32_t batch, int32_t window,
                   float threshold, int32_t *accept_len_out, void *stream);
 
-/* Single-launch step [P4 para 1: the fused cache kernel combined with
+/* One call for the step [P4 para 1: the fused cache kernel combined with
  * scheduled attention]: flash_cache_step followed by scheduled_attention with
- * the mass, as one persistent launch.  Arguments as for those two calls (the
- * attention reads the q_out this call writes); mass must not be NULL.
- * Results are bitwise those of the two separate calls: each phase runs the
- * same workgroup code.  Workgroups take items from a ticket counter in phase
- * order (projection, attention, mass); an attention item starts once every
- * projection item has finished, a mass item once every attention item has.
- * An item only waits for items with lower tickets, held by running
- * workgroups, so the ordinary launch needs no co-residency guarantee.
- * Hand-offs between workgroups use device-scope release/acquire on counters
- * in the workspace.
+ * the mass, the two calls' kernels launched back to back on `stream` (on this
+ * part a kernel boundary is the cheapest hand-off of Q and the written K/V
+ * between XCDs: a single persistent launch, and a projection overlapped with
+ * the cached keys' attention on a second stream, were both measured slower).
+ * Arguments as for those two calls (the attention reads the q_out this call
+ * writes); mass must not be NULL.  Results are bitwise those of the two
+ * separate calls.  Every shape the two calls take is supported.
+ *   workspace  fdl_fused_step_workspace_bytes(...) bytes (the same workspace
+ *              also serves flash_cache_attention_step_single_launch); contents
+ *              need no initialisation.  The attention's workspace starts at
+ *              byte 256, so its error word (see scheduled_attention) is the
+ *              int32 at byte 260. */
+int flash_cache_attention_step(const fdl_kv_cache *cache, const void *x, int32_t hidden,
+                               const void *w_qkv, int32_t batch, int32_t num_rows,
+                               const int32_t *cu_rows, const int32_t *positions,
+                               const int32_t *slots, float rope_base, void *q_out,
+                               int64_t *slot_mapping_out, const int32_t *kv_len,
+                               int32_t max_kv_len, int32_t max_rows_per_seq,
+                               const fdl_two_view *views, float softmax_scale, float *out,
+                               float *mass, int32_t mass_stride, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* Single-launch step [P4 para 1: the fused cache kernel combined with
+ * scheduled attention; P4 para 3: the verify mask inside the fused kernel]:
+ * flash_cache_step followed by scheduled_attention with the mass, as one
+ * persistent launch (an alternative form of flash_cache_attention_step, kept
+ * for comparison: on this part it is slower than the back-to-back kernels).
+ * Arguments as for flash_cache_attention_step.  Results are bitwise those of
+ * the two separate calls: each phase runs the same workgroup code.
+ * Workgroups take items from a ticket counter in phase order (projection,
+ * attention, mass); an attention item starts once every projection item has
+ * finished, a mass item once every attention item has.  An item only waits
+ * for items with lower tickets, held by running workgroups, so the ordinary
+ * launch needs no co-residency guarantee.  Hand-offs between workgroups use
+ * device-scope release/acquire on counters in the workspace.
  *   workspace  fdl_fused_step_workspace_bytes(...) bytes.  Its first 256
  *              bytes hold the counters, the ticket and an error word: they
  *              must be zero before the first call (for example a zero-filled
@@ -292,18 +317,17 @@ int verify_accept(const int32_t *draft_tok, const int32_t *mask_tok,
  * Supported: the shapes whose separate calls take a one-launch projection (no
  * split reduction) and the row-group attention path (few sequences x heads,
  * caches up to 1024 keys); otherwise FDL_EUNSUPPORTED and nothing launched. */
-int flash_cache_attention_step(const fdl_kv_cache *cache, const void *x, int32_t hidden,
-                               const void *w_qkv, int32_t batch, int32_t num_rows,
-                               const int32_t *cu_rows, const int32_t *positions,
-                               const int32_t *slots, float rope_base, void *q_out,
-                               int64_t *slot_mapping_out, const int32_t *kv_len,
-                               int32_t max_kv_len, int32_t max_rows_per_seq,
-                               const fdl_two_view *views, float softmax_scale, float *out,
-                               float *mass, int32_t mass_stride, void *workspace,
-                               size_t workspace_bytes, void *stream);
+int flash_cache_attention_step_single_launch(
+    const fdl_kv_cache *cache, const void *x, int32_t hidden, const void *w_qkv, int32_t batch,
+    int32_t num_rows, const int32_t *cu_rows, const int32_t *positions, const int32_t *slots,
+    float rope_base, void *q_out, int64_t *slot_mapping_out, const int32_t *kv_len,
+    int32_t max_kv_len, int32_t max_rows_per_seq, const fdl_two_view *views, float softmax_scale,
+    float *out, float *mass, int32_t mass_stride, void *workspace, size_t workspace_bytes,
+    void *stream);
 
-/* Workspace bytes flash_cache_attention_step needs (0 for invalid sizes;
- * mass_stride > 0). */
+/* Workspace bytes flash_cache_attention_step and
+ * flash_cache_attention_step_single_launch need, for any hidden size (0 for
+ * invalid sizes; mass_stride > 0). */
 size_t fdl_fused_step_workspace_bytes(int32_t batch, int32_t num_rows, int32_t num_heads,
                                       int32_t head_dim, int32_t max_kv_len,
                                       int32_t max_rows_per_seq, int32_t mass_stride);

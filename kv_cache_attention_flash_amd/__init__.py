@@ -13,7 +13,8 @@ Calls (same names as the C ABI):
   decode_plan          next loop step's rows, planned on the device
   gather_hidden        hidden-state rows of the planned rows
   lm_head_confidence   argmax token and softmax confidence of each row (LM head)
-  flash_cache_attention_step  flash_cache_step + scheduled_attention (+ mass) in one launch
+  flash_cache_attention_step  flash_cache_step + scheduled_attention (+ mass) in one call
+  flash_cache_attention_step_single_launch  the same as one persistent launch (slower here)
 
 DecodeStep binds one step to fixed buffers; DecodeLoop chains steps with the
 planning on the device (no host round trip between steps).
@@ -39,7 +40,8 @@ __all__ = ["PagedKVCache", "flash_cache_step", "flash_cache_step_unfused", "sche
            "track_topb", "verify_accept", "attention_workspace_bytes",
            "flash_cache_workspace_bytes", "flash_cache_unfused_workspace_bytes", "DecodeStep",
            "decode_plan", "gather_hidden", "DecodeLoop", "lm_head_confidence",
-           "lm_head_workspace_bytes", "flash_cache_attention_step", "fused_step_workspace_bytes",
+           "lm_head_workspace_bytes", "flash_cache_attention_step",
+           "flash_cache_attention_step_single_launch", "fused_step_workspace_bytes",
            "fused_step_error", "attention_error", "attention_path", "scheduled_attention_static",
            "static_scratch_bytes", "FdlError", "load"]
 
@@ -379,7 +381,8 @@ class DecodeStep:
 
     def __init__(self, cache: PagedKVCache, x, w_qkv, cu_rows, positions, slots, kv_len,
                  rope_base, max_kv_len, max_rows_per_seq, views=None, topb=0,
-                 softmax_scale=0.0, verify=None, unfused=False, fused=False):
+                 softmax_scale=0.0, verify=None, unfused=False, fused=False,
+                 single_launch=False):
         self.lib = _lib.load()
         dev = x.device
         r = x.shape[0]
@@ -419,11 +422,16 @@ class DecodeStep:
                      self.workspace.data_ptr(), self.workspace.numel())
         self._top = ((self.mass.data_ptr(), self.mass_stride, kv_len.data_ptr(), self.batch,
                       self.topb, self.idx.data_ptr()) if self.topb else None)
-        # fused: flash_cache_attention_step in place of the two calls (needs the mass).
+        # fused: flash_cache_attention_step in place of the two calls (needs the
+        # mass); single_launch: its one-kernel form.
         self._fus = None
-        if fused:
+        self._fus_fn = (self.lib.flash_cache_attention_step_single_launch if single_launch
+                        else self.lib.flash_cache_attention_step)
+        self._fus_name = ("flash_cache_attention_step_single_launch" if single_launch
+                          else "flash_cache_attention_step")
+        if fused or single_launch:
             if not self.topb:
-                raise ValueError("the single-launch step forms the mass: topb must be > 0")
+                raise ValueError("the one-call step forms the mass: topb must be > 0")
             fus_need = fused_step_workspace_bytes(self.batch, r, h, d, int(max_kv_len),
                                                   int(max_rows_per_seq), self.mass_stride)
             self.fused_workspace = torch.zeros((max(fus_need, 256),), dtype=torch.uint8,
@@ -453,8 +461,7 @@ class DecodeStep:
         _lib.check(self._fc_name, self._fc_fn(*self._fcs, stream))
 
     def run_fused(self, stream: int):
-        _lib.check("flash_cache_attention_step",
-                   self.lib.flash_cache_attention_step(*self._fus, stream))
+        _lib.check(self._fus_name, self._fus_fn(*self._fus, stream))
 
     def fused_error(self) -> int:
         """The single-launch step's error word after the runs so far (waits
@@ -754,16 +761,9 @@ def fused_step_error(workspace: torch.Tensor, stream=None) -> int:
     return int(word)
 
 
-def flash_cache_attention_step(cache: PagedKVCache, x, w_qkv, cu_rows, positions, slots,
-                               rope_base, kv_len, max_kv_len, max_rows_per_seq, views=None,
-                               softmax_scale=0.0, mass_stride=None, q_out=None,
-                               slot_mapping_out=None, out=None, mass=None, workspace=None,
-                               stream=None, check=True):
-    """flash_cache_step then scheduled_attention with the mass, as one launch
-    (bitwise the same results).  ``workspace``, if given, must be zero-filled
-    before its first use, in the launch stream's order.  With ``check`` the
-    call waits for its stream and raises if the kernel reported a timed-out
-    wait.  Returns (q_out, slot_mapping, out, mass)."""
+def _one_call_step(single_launch, cache, x, w_qkv, cu_rows, positions, slots, rope_base, kv_len,
+                   max_kv_len, max_rows_per_seq, views, softmax_scale, mass_stride, q_out,
+                   slot_mapping_out, out, mass, workspace, stream, check):
     lib = _lib.load()
     _need(x, "x", torch.bfloat16, 2)
     _need(w_qkv, "w_qkv", torch.bfloat16, 2)
@@ -803,13 +803,45 @@ def flash_cache_attention_step(cache: PagedKVCache, x, w_qkv, cu_rows, positions
     if workspace is None:
         workspace = _fused_workspace(dev, sh, need)
     cs = cache.struct()
-    st = lib.flash_cache_attention_step(
-        ctypes.byref(cs), x.data_ptr(), hid, w_qkv.data_ptr(), batch, r, cu_rows.data_ptr(),
-        positions.data_ptr(), slots.data_ptr(), float(rope_base), q_out.data_ptr(),
-        slot_mapping_out.data_ptr(), kv_len.data_ptr(), int(max_kv_len), int(max_rows_per_seq),
-        _ptr(views), float(softmax_scale), out.data_ptr(), mass.data_ptr(), int(mass_stride),
-        workspace.data_ptr(), workspace.numel(), sh)
-    _lib.check("flash_cache_attention_step", st)
-    if check and fused_step_error(workspace, sh):
-        raise RuntimeError("flash_cache_attention_step: a phase wait timed out (results invalid)")
+    fn = lib.flash_cache_attention_step_single_launch if single_launch else \
+        lib.flash_cache_attention_step
+    name = "flash_cache_attention_step_single_launch" if single_launch else \
+        "flash_cache_attention_step"
+    st = fn(ctypes.byref(cs), x.data_ptr(), hid, w_qkv.data_ptr(), batch, r, cu_rows.data_ptr(),
+            positions.data_ptr(), slots.data_ptr(), float(rope_base), q_out.data_ptr(),
+            slot_mapping_out.data_ptr(), kv_len.data_ptr(), int(max_kv_len),
+            int(max_rows_per_seq), _ptr(views), float(softmax_scale), out.data_ptr(),
+            mass.data_ptr(), int(mass_stride), workspace.data_ptr(), workspace.numel(), sh)
+    _lib.check(name, st)
+    if single_launch and check and fused_step_error(workspace, sh):
+        raise RuntimeError(f"{name}: a phase wait timed out (results invalid)")
     return q_out, slot_mapping_out, out, mass
+
+
+def flash_cache_attention_step(cache: PagedKVCache, x, w_qkv, cu_rows, positions, slots,
+                               rope_base, kv_len, max_kv_len, max_rows_per_seq, views=None,
+                               softmax_scale=0.0, mass_stride=None, q_out=None,
+                               slot_mapping_out=None, out=None, mass=None, workspace=None,
+                               stream=None):
+    """flash_cache_step then scheduled_attention with the mass, in one call
+    (their kernels back to back; bitwise the same results).  Returns (q_out,
+    slot_mapping, out, mass)."""
+    return _one_call_step(False, cache, x, w_qkv, cu_rows, positions, slots, rope_base, kv_len,
+                          max_kv_len, max_rows_per_seq, views, softmax_scale, mass_stride, q_out,
+                          slot_mapping_out, out, mass, workspace, stream, False)
+
+
+def flash_cache_attention_step_single_launch(cache: PagedKVCache, x, w_qkv, cu_rows, positions,
+                                             slots, rope_base, kv_len, max_kv_len,
+                                             max_rows_per_seq, views=None, softmax_scale=0.0,
+                                             mass_stride=None, q_out=None, slot_mapping_out=None,
+                                             out=None, mass=None, workspace=None, stream=None,
+                                             check=True):
+    """The same step as one persistent launch (bitwise the same results;
+    row-group shapes only).  ``workspace``, if given, must be zero-filled
+    before its first use, in the launch stream's order.  With ``check`` the
+    call waits for its stream and raises if the kernel reported a timed-out
+    wait.  Returns (q_out, slot_mapping, out, mass)."""
+    return _one_call_step(True, cache, x, w_qkv, cu_rows, positions, slots, rope_base, kv_len,
+                          max_kv_len, max_rows_per_seq, views, softmax_scale, mass_stride, q_out,
+                          slot_mapping_out, out, mass, workspace, stream, check)

@@ -60,6 +60,10 @@ EXPORTS = {
                                                   c_i32, c_i32, c_vp, c_vp, c_vp, c_f32, c_vp,
                                                   c_vp, c_vp, c_i32, c_i32, c_vp, c_f32, c_vp,
                                                   c_vp, c_i32, c_vp, c_size, c_vp]),
+    "flash_cache_attention_step_single_launch": (
+        ctypes.c_int, [ctypes.POINTER(KVCacheStruct), c_vp, c_i32, c_vp, c_i32, c_i32, c_vp, c_vp,
+                       c_vp, c_f32, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_f32, c_vp, c_vp, c_i32,
+                       c_vp, c_size, c_vp]),
     "fdl_fused_step_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "fdl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fdl_last_hip_error": (ctypes.c_int, []),

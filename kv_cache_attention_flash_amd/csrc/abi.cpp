@@ -423,12 +423,60 @@ size_t fdl_fused_step_workspace_bytes(int32_t batch, int32_t num_rows, int32_t n
   if (batch < 0 || num_rows < 0 || num_heads <= 0 || head_dim <= 0 || max_kv_len < 0 ||
       max_rows_per_seq < 0 || mass_stride <= 0)
     return 0;
-  return kFusedSyncBytes + fdl::plan_attention(batch, num_rows, num_heads, head_dim, max_kv_len,
-                                               max_rows_per_seq, mass_stride)
-                               .bytes;
+  // [counters of the single launch][attention workspace][projection partials]
+  return kFusedSyncBytes +
+         fdl::plan_attention(batch, num_rows, num_heads, head_dim, max_kv_len, max_rows_per_seq,
+                             mass_stride)
+             .bytes +
+         fdl::flash_cache_workspace_max();
 }
 
 int flash_cache_attention_step(const fdl_kv_cache *cache, const void *x, int32_t hidden,
+                               const void *w_qkv, int32_t batch, int32_t num_rows,
+                               const int32_t *cu_rows, const int32_t *positions,
+                               const int32_t *slots, float rope_base, void *q_out,
+                               int64_t *slot_mapping_out, const int32_t *kv_len,
+                               int32_t max_kv_len, int32_t max_rows_per_seq,
+                               const fdl_two_view *views, float softmax_scale, float *out,
+                               float *mass, int32_t mass_stride, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  fdl::FlashCacheArgs fa;
+  fdl::AttnArgs aa;
+  fdl::AttnPlan plan;
+  bool empty_fc;
+  int empty_at;
+  int st = fc_args(cache, x, hidden, w_qkv, batch, num_rows, cu_rows, positions, slots,
+                   rope_base, q_out, slot_mapping_out, fa, empty_fc);
+  if (st) return st;
+  st = attn_args(cache, q_out, batch, num_rows, cu_rows, kv_len, max_kv_len, max_rows_per_seq,
+                 views, softmax_scale, out, mass, mass_stride, aa, plan, empty_at);
+  if (st || empty_at == 1) return st;
+  if (!mass) return FDL_EINVAL;
+  const size_t fc_need =
+      fdl::flash_cache_workspace_bytes(num_rows, hidden, cache->num_heads, cache->head_dim);
+  // the documented size (any hidden size), not only this projection's share
+  if (workspace_bytes < kFusedSyncBytes + plan.bytes + fdl::flash_cache_workspace_max() ||
+      !workspace)
+    return FDL_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_mode()) {
+    if (!empty_fc && (st = debug_check_rows(cache, batch, num_rows, cu_rows, positions, slots, s)))
+      return st;
+    if ((st = debug_check_attention(cache, batch, num_rows, cu_rows, kv_len, max_kv_len,
+                                    max_rows_per_seq, views, s)))
+      return st;
+  }
+  char *ws = static_cast<char *>(workspace);
+  if (!empty_fc) {
+    st = hip_status(fdl::launch_flash_cache(fa, fc_need ? ws + kFusedSyncBytes + plan.bytes : nullptr,
+                                            fc_need, s));
+    if (st) return st;
+  }
+  aa.ws = ws + kFusedSyncBytes;
+  return hip_status(fdl::launch_attention(aa, plan, s));
+}
+
+int flash_cache_attention_step_single_launch(const fdl_kv_cache *cache, const void *x, int32_t hidden,
                                const void *w_qkv, int32_t batch, int32_t num_rows,
                                const int32_t *cu_rows, const int32_t *positions,
                                const int32_t *slots, float rope_base, void *q_out,

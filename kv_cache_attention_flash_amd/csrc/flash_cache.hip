@@ -723,6 +723,12 @@ size_t flash_cache_workspace_bytes(int rows, int hidden, int H, int D) {
   return plan_fc(rows, hidden, H, D).bytes;
 }
 
+// An upper bound of flash_cache_workspace_bytes over every shape: a reduction
+// is split only while groups x splits stay within kSplitCap.
+size_t flash_cache_workspace_max() {
+  return (size_t)kSplitCap * 64 * kSplitCW * sizeof(float);
+}
+
 hipError_t launch_flash_cache(const FlashCacheArgs &a, void *ws, size_t ws_bytes, hipStream_t s) {
   const FcPlan fp = plan_fc(a.rows, a.hidden, a.c.H, a.c.D);
   if (fp.splitk) {

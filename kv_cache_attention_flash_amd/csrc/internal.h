@@ -26,6 +26,7 @@ struct FlashCacheArgs {
 };
 
 size_t flash_cache_workspace_bytes(int rows, int hidden, int H, int D);
+size_t flash_cache_workspace_max();
 hipError_t launch_flash_cache(const FlashCacheArgs &a, void *ws, size_t ws_bytes, hipStream_t s);
 size_t flash_cache_unfused_workspace_bytes(int rows, int hidden, int H, int D);
 hipError_t launch_flash_cache_unfused(const FlashCacheArgs &a, void *ws, size_t ws_bytes,

@@ -198,20 +198,22 @@ def test_lm_head_validation(lib):
 
 
 def test_fused_step_validation(lib):
-    """Host-side refusals of the single-launch step (nothing is launched)."""
+    """Host-side refusals of the one-call step and of its single-launch form
+    (nothing is launched)."""
     fake = 0x10000
     c = _cache(h=2, d=128, bs=32, nb=4, mb=4)
     ws = lib.fdl_fused_step_workspace_bytes(1, 40, 2, 128, 96, 40, 96)
     assert ws >= 256 and lib.fdl_fused_step_workspace_bytes(1, 40, 2, 128, 96, 40, 0) == 0
-    def call(hid=1024, mass=fake, wsb=ws, rows=40):
-        return lib.flash_cache_attention_step(ctypes.byref(c), fake, hid, fake, 1, rows, fake, fake,
-                                              fake, 1e4, fake, None, fake, 96, 40, None, 0.0,
-                                              fake, mass, 96, fake, wsb, None)
-    assert call(mass=None) == _lib.FDL_EINVAL          # the step always forms the mass
-    assert call(wsb=ws - 1) == _lib.FDL_EWORKSPACE
+    def call(fn, hid=1024, mass=fake, wsb=ws, rows=40):
+        return fn(ctypes.byref(c), fake, hid, fake, 1, rows, fake, fake, fake, 1e4, fake, None,
+                  fake, 96, 40, None, 0.0, fake, mass, 96, fake, wsb, None)
+    for fn in (lib.flash_cache_attention_step, lib.flash_cache_attention_step_single_launch):
+        assert call(fn, mass=None) == _lib.FDL_EINVAL      # the step always forms the mass
+        assert call(fn, wsb=16) == _lib.FDL_EWORKSPACE
+        assert call(fn, hid=200) == _lib.FDL_EUNSUPPORTED   # as flash_cache_step
+    assert call(lib.flash_cache_attention_step, wsb=ws - 1) == _lib.FDL_EWORKSPACE
     # a narrow layer at 40 rows splits its projection's reduction: not one launch
-    assert call() == _lib.FDL_EUNSUPPORTED
-    assert call(hid=200) == _lib.FDL_EUNSUPPORTED        # as flash_cache_step
+    assert call(lib.flash_cache_attention_step_single_launch) == _lib.FDL_EUNSUPPORTED
 
 
 def test_attention_path_selection(lib):
