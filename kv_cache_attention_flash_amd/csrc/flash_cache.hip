@@ -484,7 +484,8 @@ struct GemmLds {
   static constexpr int TR = BM + 64 * NWN, PIECES = BK / 8, NT = 128 * NWN;
   static constexpr int TRP = (TR * PIECES + NT - 1) / NT * NT / PIECES;
   u32x4 lds[2][TRP * PIECES];
-  int s_blk[BM], s_off[BM], s_pos[BM];
+  long long s_kvo[BM];  // element offset of the row's cache slot, (blk * H * bs + off) * D
+  int s_pos[BM];
 };
 
 template <int BM, int NWN, int NREG, int BK = 32>
@@ -500,8 +501,7 @@ __device__ __forceinline__ void qkv_gemm_body(const FlashCacheArgs &a, int nrow_
   constexpr int LD = (TR * PIECES + NT - 1) / NT;      // 16-byte loads per thread per step
   static_assert(NT % PIECES == 0, "whole rows per load round");
   auto &lds = L.lds;
-  auto &s_blk = L.s_blk;
-  auto &s_off = L.s_off;
+  auto &s_kvo = L.s_kvo;
   auto &s_pos = L.s_pos;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -520,8 +520,7 @@ __device__ __forceinline__ void qkv_gemm_body(const FlashCacheArgs &a, int nrow_
     if (r < act) {
       int blk, off, pos;
       row_meta(a, r, ct == 0, blk, off, pos);
-      s_blk[rl] = blk;
-      s_off[rl] = off;
+      s_kvo[rl] = ((long long)blk * H * a.c.bs + off) * D;
       s_pos[rl] = pos;
     }
   }
@@ -609,17 +608,37 @@ __device__ __forceinline__ void qkv_gemm_body(const FlashCacheArgs &a, int nrow_
   }
 
   // Epilogue: lane holds pair pair0 + 32 wn + l32 for 16 rows per M tile.
+  // The pair's section, head and destination column are formed once; each
+  // row then adds its own offset (Q row, or cache slot from s_kvo).
   const int p = pair0 + 32 * wn + l32;
   if (p >= total_pairs) return;
-  const double freq = rope_inv_freq(p % half, D, a.log2_base);
+  if (a.y_out) {  // unfused ablation: the raw fp32 pairs
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int rl = wm * (BM / 2) + 32 * mt + 8 * (e / 4) + 4 * hi + (e % 4);
+        if (row0 + rl < act) store_raw_pair(a, row0 + rl, p, acc[mt][0][e], acc[mt][1][e]);
+      }
+    return;
+  }
+  const int sh = p / half, i = p % half, sec = sh / H, h = sh % H;
+  const bool rot = sec < 2;
+  const double freq = rope_inv_freq(i, D, a.log2_base);
+  uint16_t *const base = sec == 0 ? a.q_out + (size_t)h * D + i
+                                  : (sec == 1 ? a.c.k : a.c.v) + (size_t)h * a.c.bs * D + i;
+  const size_t qstride = (size_t)H * D;
 #pragma unroll
   for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int rl = wm * (BM / 2) + 32 * mt + 8 * (e / 4) + 4 * hi + (e % 4);
-      if (row0 + rl >= act) continue;
-      store_pair(a, row0 + rl, p, acc[mt][0][e], acc[mt][1][e], s_blk[rl], s_off[rl], s_pos[rl],
-                 freq);
+      const int r = row0 + rl;
+      if (r >= act) continue;
+      const size_t ro = sec == 0 ? (size_t)r * qstride : (size_t)s_kvo[rl];
+      float c = 1.f, sn = 0.f;
+      if (rot) rope_cs(s_pos[rl], freq, c, sn);
+      store_word(base + ro, half, rotate_round_cs(acc[mt][0][e], acc[mt][1][e], rot, c, sn));
     }
 }
 
