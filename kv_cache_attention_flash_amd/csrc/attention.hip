@@ -35,7 +35,9 @@ namespace fdl {
 namespace {
 
 constexpr int KT = 32;   // keys per tile
-constexpr int kNpf = 2;  // split path: tiles in flight per key group (pass 1)
+constexpr int kNpf = 2;      // split path: tiles in flight per key group (pass 1)
+constexpr int kNpfFwdMass = 2;  // the same for pass 1 when the mass pass follows
+constexpr int kNpfMass = 2;     // K tiles in flight per key group in the mass pass
 constexpr float kNegInf = -__builtin_huge_valf();
 
 struct SeqInfo {
@@ -339,7 +341,7 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, int r, int h, bool ok,
 // them over heads and row tiles.
 template <int D, bool MASS>
 __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
-  constexpr int NPF = kNpf;  // tiles in flight per key group
+  constexpr int NPF = MASS ? kNpfFwdMass : kNpf;  // tiles in flight per key group
   // K tiles (swizzled chunks); 8 chunks more per tile make room for the
   // merge scratch that reuses them.
   __shared__ u32x4 klds[2][2][KT * D / 8 + 8];
@@ -462,12 +464,13 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
                 (((size_t)b * a.c.H + h) * p.row_tiles + rt) * a.mass_stride;
     // Pass 2: key group kg takes tiles te-1-kg, te-3-kg, ... (last first), K
     // only, the same uniform ring of loads as pass 1.
+    constexpr int NPF2 = kNpfMass;
     const int n2 = (te - tb + 1) / 2;
-    const int n2r = (n2 + NPF - 1) / NPF * NPF;
-    Tile<D> kf[NPF];
+    const int n2r = (n2 + NPF2 - 1) / NPF2 * NPF2;
+    Tile<D> kf[NPF2];
     if (te > tb) {
 #pragma unroll
-      for (int i = 0; i < NPF; ++i)
+      for (int i = 0; i < NPF2; ++i)
         load_tile<D>(kf[i], a, s_page, tb, h, max(te - 1 - kg - 2 * i, tb) * KT, false, gtid);
     }
     const int b3 = (j >> 3) & 1, b2 = (j >> 2) & 1, b1 = (j >> 1) & 1;
@@ -486,15 +489,15 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
         }
       }
     };
-    for (int it0 = 0; it0 < n2r; it0 += NPF) {
+    for (int it0 = 0; it0 < n2r; it0 += NPF2) {
 #pragma unroll
-      for (int ii = 0; ii < NPF; ++ii) {
+      for (int ii = 0; ii < NPF2; ++ii) {
         const int it = it0 + ii;
         const int tile = te - 1 - kg - 2 * it;
         const bool have = it < n2 && tile >= tb;
         const int buf = it & 1;
         store_tile<D>(kf[ii], klds[kg][buf], nullptr, false, gtid);
-        load_tile<D>(kf[ii], a, s_page, tb, h, max(tile - 2 * NPF, tb) * KT, false, gtid);
+        load_tile<D>(kf[ii], a, s_page, tb, h, max(tile - 2 * NPF2, tb) * KT, false, gtid);
         lds_barrier();
         if (it > 0) flush(it - 1);
         float pv[8];

@@ -627,19 +627,30 @@ __device__ __forceinline__ void qkv_gemm_body(const FlashCacheArgs &a, int nrow_
   const double freq = rope_inv_freq(i, D, a.log2_base);
   uint16_t *const base = sec == 0 ? a.q_out + (size_t)h * D + i
                                   : (sec == 1 ? a.c.k : a.c.v) + (size_t)h * a.c.bs * D + i;
-  const size_t qstride = (size_t)H * D;
+  // One loop per destination kind (the section is the same for the whole
+  // wave); rows past the active ones only occur in a grid's last row tile.
+  const bool full = row0 + BM <= act;
+  auto rows = [&](auto dst_off, auto rotate) {
 #pragma unroll
-  for (int mt = 0; mt < MTW; ++mt)
+    for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int rl = wm * (BM / 2) + 32 * mt + 8 * (e / 4) + 4 * hi + (e % 4);
-      const int r = row0 + rl;
-      if (r >= act) continue;
-      const size_t ro = sec == 0 ? (size_t)r * qstride : (size_t)s_kvo[rl];
-      float c = 1.f, sn = 0.f;
-      if (rot) rope_cs(s_pos[rl], freq, c, sn);
-      store_word(base + ro, half, rotate_round_cs(acc[mt][0][e], acc[mt][1][e], rot, c, sn));
-    }
+      for (int e = 0; e < 16; ++e) {
+        const int rl = wm * (BM / 2) + 32 * mt + 8 * (e / 4) + 4 * hi + (e % 4);
+        if (!full && row0 + rl >= act) continue;
+        float c = 1.f, sn = 0.f;
+        if (rotate.value) rope_cs(s_pos[rl], freq, c, sn);
+        store_word(base + dst_off(rl), half,
+                   rotate_round_cs(acc[mt][0][e], acc[mt][1][e], rotate.value, c, sn));
+      }
+  };
+  if (sec == 0) {
+    const size_t qstride = (size_t)H * D;
+    rows([&](int rl) { return (size_t)(row0 + rl) * qstride; }, std::true_type{});
+  } else if (rot) {
+    rows([&](int rl) { return (size_t)s_kvo[rl]; }, std::true_type{});
+  } else {
+    rows([&](int rl) { return (size_t)s_kvo[rl]; }, std::false_type{});
+  }
 }
 
 
