@@ -87,7 +87,7 @@ def test_deterministic_reruns():
     assert torch.equal(a.cache.k_cache, b.cache.k_cache)
 
 
-@pytest.mark.parametrize("name", ["small_long_l1500", "long_b4_l4096"])
+@pytest.mark.parametrize("name", ["small_long_l1500", "long_b4_l4096", "long_b5_h32_rounds"])
 def test_exchange_path_reruns_and_workspace(name):
     """The split path whose splits exchange row statistics (caches past 1024
     keys, mass asked for): bitwise the same results on three calls in a row
@@ -103,10 +103,24 @@ def test_exchange_path_reruns_and_workspace(name):
                          tracked=tuple(sorted(int(p) for p in g.choice(32, 32, replace=False))))
                  for b in range(4)]
         wl = synth.build(name, 25, 512, 8, 128, 32, 5.0e5, specs, topb=32)
+    elif name == "long_b5_h32_rounds":
+        # 5 x 32 heads = 160 units of up to four 1024-key splits: more
+        # workgroups than the GPU holds at once, so splits wait across rounds
+        g = np.random.default_rng(11)
+        specs = []
+        for _ in range(5):
+            L = int(g.integers(3073, 4097))
+            w0 = int(g.integers(32, L - 64))
+            specs.append(SeqSpec(kv_len=L, window=(w0, 32),
+                                 tracked=tuple(sorted(int(p) for p in g.choice(w0, 32,
+                                                                               replace=False)))))
+        wl = synth.build(name, 26, 512, 32, 64, 32, 5.0e5, specs, topb=32)
     else:
         wl = synth.WORKLOADS[name]()
     _banner(f"exchange path {name}: lengths {wl.kv_len.tolist()}")
     run = G.GpuRun(wl, dev)
+    assert fd.attention_path(wl.batch, wl.rows, wl.num_heads, wl.head_dim, wl.max_kv_len,
+                             run.max_rows, wl.max_kv_len) == "split_mass_exchange"
     q, sm = fd.flash_cache_step(run.cache, run.x, run.w, run.cu, run.pos, run.slots, wl.rope_base)
     need = fd.attention_workspace_bytes(wl.batch, wl.rows, wl.num_heads, wl.head_dim,
                                         wl.max_kv_len, run.max_rows, wl.max_kv_len)
