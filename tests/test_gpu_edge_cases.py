@@ -87,6 +87,43 @@ def test_deterministic_reruns():
     assert torch.equal(a.cache.k_cache, b.cache.k_cache)
 
 
+def _longest_cache_workload():
+    """One sequence at the page limit (1024 pages of 64 slots, 65535 keys
+    cached), 2 heads x 64, window in the middle and tracked rows spread over
+    the whole cache, top-16."""
+    g = np.random.default_rng(13)
+    L = 1024 * 64 - 1
+    w0 = 40000
+    tracked = tuple(sorted(int(p) for p in g.choice(w0, 24, replace=False)))
+    spec = SeqSpec(kv_len=L, window=(w0, 16), tracked=tracked)
+    return synth.build("longest_l65535", 27, 256, 2, 64, 64, 5.0e5, [spec], topb=16)
+
+
+@pytest.mark.parametrize("want_mass", [True, False])
+def test_cache_at_the_page_limit(want_mass):
+    """The longest cache the ABI takes (1024 pages): with the mass, 64
+    splits exchanging row statistics; without it, 64 splits merged in order.
+    Element-wise against the oracle (with the mass: top-B too)."""
+    import kv_cache_attention_flash_amd as fd
+    fd.load()
+    wl = _longest_cache_workload()
+    path = fd.attention_path(wl.batch, wl.rows, wl.num_heads, wl.head_dim, wl.max_kv_len,
+                             int(np.diff(wl.cu_rows).max()), wl.max_kv_len if want_mass else 0)
+    _banner(f"page limit: L {int(wl.kv_len[0])}, rows {wl.rows}, mass {want_mass}, path {path}")
+    assert path == ("split_mass_exchange" if want_mass else "split")
+    run = G.GpuRun(wl, "cuda:0")
+    if want_mass:
+        run.step()
+        full_check(wl, run=run)
+        return
+    q, sm = fd.flash_cache_step(run.cache, run.x, run.w, run.cu, run.pos, run.slots, wl.rope_base)
+    out, _ = fd.scheduled_attention(run.cache, q, run.cu, run.kv_len, wl.max_kv_len, run.max_rows,
+                                    views=run.views)
+    torch.cuda.synchronize()
+    ref = G.oracle_step(wl)
+    G.assert_close(out.cpu().numpy(), ref["out"], "attention output (no mass)")
+
+
 @pytest.mark.parametrize("name", ["small_long_l1500", "long_b4_l4096", "long_b5_h32_rounds"])
 def test_exchange_path_reruns_and_workspace(name):
     """The split path whose splits exchange row statistics (caches past 1024
