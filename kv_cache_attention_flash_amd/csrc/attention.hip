@@ -35,9 +35,7 @@ namespace fdl {
 namespace {
 
 constexpr int KT = 32;   // keys per tile
-constexpr int kNpf = 2;      // split path: tiles in flight per key group (pass 1)
-constexpr int kNpfFwdMass = 2;  // the same for pass 1 when the mass pass follows
-constexpr int kNpfMass = 2;     // K tiles in flight per key group in the mass pass
+constexpr int kNpf = 2;  // exchange-mass kernel: tiles in flight per key group
 constexpr float kNegInf = -__builtin_huge_valf();
 
 struct SeqInfo {
@@ -327,6 +325,137 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, int r, int h, bool ok,
                 : u32x4{0u, 0u, 0u, 0u};
 }
 
+// ---------------------------------------------------------------------------
+// LDS ring of the forward kernel.  A tile's K and V go from global memory
+// straight into LDS by buffer loads that write LDS (`buffer_load ... lds`):
+// no registers, no LDS store instructions.  Lane l of a load fills 16-byte
+// slot 64·piece + l of the tile, so the permuted layouts are made on the
+// source side: K slot s holds chunk (s % CH) ^ kswz(key) of key s / CH (the
+// kslot layout), V slot s chunk (s % CH) ^ vswz(key) (rows unpadded; the
+// permutation keeps the transposed reads free of bank conflicts).  Keys at or
+// past the cached length lie outside the buffer view and load as zeros.
+
+// f(integral_constant<int, I>) for I = B .. E-1 (compile-time ring indices).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+// The XOR term of kslot: kslot(key, ch) = key·CH + (ch ^ kswz(key)).
+template <int D>
+__device__ __forceinline__ int kswz(int key) {
+  return D == 128 ? (key & 3) | ((key >> 1) & 12) : ((key >> 1) & 1) | ((key >> 2) & 6);
+}
+// V rows: 16-byte chunk c of key row k sits at chunk c ^ vswz(k).
+template <int D>
+__device__ __forceinline__ int vswz(int key) {
+  return D == 128 ? (key & 3) << 1 : key & 2;
+}
+
+// An index the optimiser cannot split, so that an LDS read's address stays
+// one step off its ring buffer: the compiler then knows which buffer a read
+// touches and waits only for that buffer's loads.
+__device__ __forceinline__ int opaque_index(int x) {
+  asm("v_mov_b32 %0, %1" : "=v"(x) : "v"(x));
+  return x;
+}
+
+// Loads of one tile (K, and V when asked) into a ring buffer by the 4 waves
+// of a key group (wq = wave within the group, wave-uniform).  The tile is
+// the key run [key0, key0 + KT) of one page.
+template <int D>
+__device__ __forceinline__ void ring_issue(const AttnArgs &a, const int *s_page, int page0,
+                                           int h, int key0, int L, u32x4 *kdst,
+                                           u32x4 *vdst, bool want_v, int wq, int lane) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  constexpr int CH = D / 8, PERW = KT * CH / 64 / 4;  // 1 KB loads per wave per tile
+  const int sh = a.c.bs_shift;
+  const int page = __builtin_amdgcn_readfirstlane(s_page[(key0 >> sh) - page0]);
+  const size_t off = ((((size_t)page * a.c.H + h) << sh) + (key0 & (a.c.bs - 1))) * D;
+  // readfirstlane: a clamp may be selected as a vector instruction, and a
+  // descriptor word in a vector register costs a loop around each load.
+  const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(KT, L - key0)) * D * 2);
+  const auto rk = buffer_view(a.c.k + off, bytes);
+  const auto rv = buffer_view(a.c.v + off, bytes);
+#pragma unroll
+  for (int i = 0; i < PERW; ++i) {
+    const int piece = wq * PERW + i;
+    const int s = 64 * piece + lane, key = s / CH;
+    const int ko = (key * CH + ((s % CH) ^ kswz<D>(key))) * 16;
+    const int vo = (key * CH + ((s % CH) ^ vswz<D>(key))) * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(kdst + 64 * piece), 16, ko, 0, 0, 0);
+    if (want_v)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(vdst + 64 * piece), 16, vo, 0, 0,
+                                               0);
+  }
+}
+
+// S^T tile (32 keys x 16 rows) from a ring K tile (as scores()).
+template <int D>
+__device__ __forceinline__ void scores_ring(const u32x4 *kg_, const u32x4 *qf, int lane,
+                                            f32x4 s[2]) {
+  const lds_u32x4 *kb = (const lds_u32x4 *)kg_;
+  const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int key = 8 * (j >> 2) + 4 * mt + (j & 3);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      u32x4 kf = kb[opaque_index(kslot<D>(key, 4 * ks + g))];
+      acc = mfma16(kf, qf[ks], acc);
+    }
+    s[mt] = acc;
+  }
+}
+
+// V^T operand from a ring V tile (as vt_operand(), rows permuted by vswz).
+template <int D>
+__device__ __forceinline__ u32x4 vt_operand_ring(const u32x4 *vg, int dm, int lane) {
+  const lds_u32x4 *vb = (const lds_u32x4 *)vg;
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const lds_u16 *v16 = reinterpret_cast<const lds_u16 *>(vb);
+  const int g = lane >> 4, i = lane & 15;
+  const int c = 2 * dm + ((i >> 1) & 1), half = (i & 1) * 4;
+  const int k0 = 8 * g + (i >> 2), k1 = k0 + 4;
+  const int e0 = k0 * D + ((c ^ vswz<D>(k0)) << 3) + half;
+  const int e1 = k1 * D + ((c ^ vswz<D>(k1)) << 3) + half;
+  bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(v16 + opaque_index(e0)));
+  bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(v16 + opaque_index(e1)));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
+
+// Bare workgroup barrier after this wave's ring loads up to the awaited tile
+// are done (vmcnt encoding W): every wave's loads of that tile are then in
+// LDS, and every wave has finished with the buffer the next loads refill.
+// The compiler-only fences keep LDS accesses on their side of it.
+template <int W>
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(W);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+// Tiles a key group holds in LDS at once.  Depth 2 keeps a head-128
+// workgroup's LDS near 71 KB, so two workgroups (16 waves) share a CU; depth 3
+// (one more tile in flight per key group) needs 103 KB and fits one.  Two
+// workgroups at depth 2 stream the cache faster.
+#ifndef FDL_RING_DEPTH
+#define FDL_RING_DEPTH 2
+#endif
+constexpr int kRingDepth = FDL_RING_DEPTH;
+static_assert(kRingDepth == 2 || kRingDepth == 3, "ring depth");
+
 // Pass 1.  8 waves: key group kg = wave / 4 takes the unit's even or odd
 // tiles, row group wave % 4 owns 16 query rows; the two key groups keep their
 // own online-softmax state and are combined through LDS at the end (group 0
@@ -341,11 +470,15 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, int r, int h, bool ok,
 // them over heads and row tiles.
 template <int D, bool MASS>
 __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
-  constexpr int NPF = MASS ? kNpfFwdMass : kNpf;  // tiles in flight per key group
-  // K tiles (swizzled chunks); 8 chunks more per tile make room for the
-  // merge scratch that reuses them.
-  __shared__ u32x4 klds[2][2][KT * D / 8 + 8];
-  __shared__ uint16_t vlds[2][2][KT][kVPad<D>];
+  constexpr int T = KT * D / 8;                // 16-byte slots of a K (or V) tile
+  constexpr int PERW = KT * (D / 8) / 64 / 4;  // ring loads per wave per K (or V) tile
+  constexpr int NB = kRingDepth;
+  // NB ring buffers of [key group][K tile | V tile] (separate objects, so
+  // that reading one never waits for loads into another); ring0 has room
+  // after its tiles for the merge scratch (64 rows x D floats, 64 (m, l)).
+  __shared__ u32x4 ring0[4 * T + 32];
+  __shared__ u32x4 ring1[4 * T];
+  __shared__ u32x4 ring2[NB > 2 ? 4 * T : 1];
 
   int u = blockIdx.x;
   const int split = u % p.splits; u /= p.splits;
@@ -356,8 +489,10 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
   const int t0 = rt * 64;
   if (t0 >= si.nrows) return;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int kg = wave >> 2, wr = wave & 3, gtid = threadIdx.x & 255;
+  // The wave index in a scalar register: the ring loads' descriptors and LDS
+  // destinations are then wave-uniform to the compiler too.
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kg = wave >> 2, wr = wave & 3;
   const int g = lane >> 4, j = lane & 15;
   const int t = t0 + wr * 16 + j;  // local row of this lane
   const bool row_ok = t < si.nrows;
@@ -372,57 +507,72 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
   __shared__ int s_page[kMaxPages];
   stage_pages(a, b, tb, te, s_page);
   lds_barrier();
-  // Loads are unconditional (tile index clamped to the unit's last tile; the
-  // repeats hit L2) so the compiler keeps the other stage in flight.
+  const int page0 = (tb * KT) >> a.c.bs_shift;
   const int tlast = max(te - 1, tb);
-  Tile<D> pf[NPF];
-  if (te > tb) {
-#pragma unroll
-    for (int i = 0; i < NPF; ++i)
-      load_tile<D>(pf[i], a, s_page, tb, h, min(tb + kg + 2 * i, tlast) * KT, true, gtid);
-  }
+  auto ring = [&](auto b_c) -> u32x4 * {
+    constexpr int bi = decltype(b_c)::value;
+    if constexpr (bi == 0) return &ring0[0];
+    else if constexpr (bi == 1) return &ring1[0];
+    else return &ring2[0];
+  };
   u32x4 qf[D / 32];
   load_q<D>(a, r, h, row_ok, g, qf);
+  asm volatile("" ::: "memory");  // Q's loads ahead of the ring's (in-order load counts)
 
   f32x4 o[D / 16];
 #pragma unroll
   for (int dm = 0; dm < D / 16; ++dm) o[dm] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = kNegInf, l = 0.f;
 
-  // Every iteration has the same shape: one ring stage stored to LDS, the
-  // same stage reloaded, a barrier, then the tile's math only if the tile
-  // exists.  With no branch around a load, the compiler waits for exactly
-  // the stage it needs and keeps the other stages in flight.
-  const int niter_r = (niter + NPF - 1) / NPF * NPF;
-  for (int it0 = 0; it0 < niter_r; it0 += NPF) {
+  // Key group kg takes tiles tb + kg, tb + kg + 2, ...; iteration it uses ring
+  // buffer it % NB.  Iteration it waits for its tile (this wave's loads, then
+  // a barrier for every wave's), refills the buffer of iteration it - 1 with
+  // the tile of it + NB - 1, then does the tile's math if the tile exists.
+  // Every iteration issues the same number of loads (past the key group's
+  // last tile, loads of an empty view: zeros, no memory traffic), so the
+  // count of loads behind a tile is fixed.
+  auto issue1 = [&](auto b_c, int it) {
+    u32x4 *rb = ring(b_c) + kg * 2 * T;
+    const bool live = tb + kg + 2 * it < te;  // else an empty view: zeros, no traffic
+    const int tile = live ? tb + kg + 2 * it : tlast;
+    ring_issue<D>(a, s_page, page0, h, tile * KT, live ? si.L : 0, rb, rb + T, true, wr, lane);
+  };
+  if (te > tb) {
+    static_for<0, NB - 1>([&](auto s_c) { issue1(s_c, decltype(s_c)::value); });
+    const int niter_r = (niter + NB - 1) / NB * NB;
+    for (int it0 = 0; it0 < niter_r; it0 += NB) {
+      static_for<0, NB>([&](auto s_c) {
+        constexpr int sb = decltype(s_c)::value;
+        const int it = it0 + sb;
+        ring_barrier<vmcnt_only((NB - 2) * 2 * PERW)>();
+        issue1(std::integral_constant<int, (sb + NB - 1) % NB>{}, it + NB - 1);
+        asm volatile("" ::: "memory");
+        const int tile = tb + kg + 2 * it;
+        const bool have = it < niter && tile < te;
+        const int key0 = tile * KT;
+        const int tv = have ? tile_vis(vis, key0) : 0;
+        if (tv != 0) {
+          const u32x4 *rb = ring(s_c) + kg * 2 * T;
+          f32x4 sv[2];
+          scores_ring<D>(rb, qf, lane, sv);
+          float xs[8];
+          const u32x4 pb = tile_softmax<D / 16>(sv, vis, tv, key0, g, a.scale_log2, m, l, o, xs);
 #pragma unroll
-    for (int ii = 0; ii < NPF; ++ii) {
-      const int it = it0 + ii;
-      const int tile = tb + kg + 2 * it;
-      const bool have = it < niter && tile < te;
-      const int buf = it & 1;  // alternates across iterations for any NPF
-      store_tile<D>(pf[ii], klds[kg][buf], vlds[kg][buf], true, gtid, si.L - tile * KT);
-      load_tile<D>(pf[ii], a, s_page, tb, h, min(tile + 2 * NPF, tlast) * KT, true, gtid);
-      lds_barrier();
-      const int key0 = tile * KT;
-      const int tv = have ? tile_vis(vis, key0) : 0;
-      if (tv != 0) {
-        f32x4 s[2];
-        scores<D>(klds[kg][buf], qf, lane, s);
-        float xs[8];
-        const u32x4 pb = tile_softmax<D / 16>(s, vis, tv, key0, g, a.scale_log2, m, l, o, xs);
-#pragma unroll
-        for (int dm = 0; dm < D / 16; ++dm)
-          o[dm] = mfma16(vt_operand<D>(vlds[kg][buf], dm, lane), pb, o[dm]);
-      }
+          for (int dm = 0; dm < D / 16; ++dm)
+            o[dm] = mfma16(vt_operand_ring<D>(rb + T, dm, lane), pb, o[dm]);
+        }
+      });
     }
   }
+  // Ring loads past the last tile still write LDS: complete before ring0 holds
+  // the merge scratch.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // Combine the two key groups (group 1's state through LDS, reusing the tiles).
   lds_barrier();
-  float *mo = reinterpret_cast<float *>(&klds[0][0][0]);  // [4 row groups][16 rows][D]
-  float *mml = mo + 64 * D;                                   // [64 rows][2]
-  static_assert((64 * D + 128) * 4 <= (int)sizeof(klds), "merge scratch");
+  float *mo = reinterpret_cast<float *>(&ring0[0]);  // [4 row groups][16 rows][D]
+  float *mml = mo + 64 * D;                            // [64 rows][2]
+  static_assert((64 * D + 128) * 4 <= (int)sizeof(ring0), "merge scratch");
   const int rl = wr * 16 + j;
   if (kg == 1) {
 #pragma unroll
@@ -463,16 +613,15 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
     float *mp = reinterpret_cast<float *>(a.ws + p.off_mass_part) +
                 (((size_t)b * a.c.H + h) * p.row_tiles + rt) * a.mass_stride;
     // Pass 2: key group kg takes tiles te-1-kg, te-3-kg, ... (last first), K
-    // only, the same uniform ring of loads as pass 1.
-    constexpr int NPF2 = kNpfMass;
+    // only, through the same ring (the merge scratch is no longer read).
     const int n2 = (te - tb + 1) / 2;
-    const int n2r = (n2 + NPF2 - 1) / NPF2 * NPF2;
-    Tile<D> kf[NPF2];
-    if (te > tb) {
-#pragma unroll
-      for (int i = 0; i < NPF2; ++i)
-        load_tile<D>(kf[i], a, s_page, tb, h, max(te - 1 - kg - 2 * i, tb) * KT, false, gtid);
-    }
+    const int n2r = te > tb ? (n2 + NB - 1) / NB * NB : 0;
+    auto issue2 = [&](auto b_c, int it) {
+      u32x4 *rb = ring(b_c) + kg * 2 * T;
+      const bool live = te - 1 - kg - 2 * it >= tb;
+      const int tile = live ? te - 1 - kg - 2 * it : tb;
+      ring_issue<D>(a, s_page, page0, h, tile * KT, live ? si.L : 0, rb, rb, false, wr, lane);
+    };
     const int b3 = (j >> 3) & 1, b2 = (j >> 2) & 1, b1 = (j >> 1) & 1;
     // The sums of the previous iteration's tile (buffer pb_) are added over
     // the row groups after the next barrier, by 64 threads (key group
@@ -482,24 +631,26 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
         const int fk = threadIdx.x / KT, key = threadIdx.x % KT, pb_ = it_prev & 1;
         const int tile = te - 1 - fk - 2 * it_prev;
         if (it_prev < n2 && tile >= tb) {
-          const float v = ((wsum[pb_][fk][0][key] + wsum[pb_][fk][1][key]) + wsum[pb_][fk][2][key]) +
-                          wsum[pb_][fk][3][key];
+          const float *ws4 = &wsum[0][0][0][0];
+          const int w0 = opaque_index((pb_ * 2 + fk) * 4 * KT + key);
+          const float v = ((ws4[w0] + ws4[w0 + KT]) + ws4[w0 + 2 * KT]) + ws4[w0 + 3 * KT];
           const int jj = tile * KT + key;
           if (jj < si.L) mp[jj] = v;
         }
       }
     };
-    for (int it0 = 0; it0 < n2r; it0 += NPF2) {
-#pragma unroll
-      for (int ii = 0; ii < NPF2; ++ii) {
-        const int it = it0 + ii;
+    if (n2r > 0) static_for<0, NB - 1>([&](auto s_c) { issue2(s_c, decltype(s_c)::value); });
+    for (int it0 = 0; it0 < n2r; it0 += NB) {
+      static_for<0, NB>([&](auto s_c) {
+        constexpr int sb = decltype(s_c)::value;
+        const int it = it0 + sb;
         const int tile = te - 1 - kg - 2 * it;
         const bool have = it < n2 && tile >= tb;
         const int buf = it & 1;
-        store_tile<D>(kf[ii], klds[kg][buf], nullptr, false, gtid);
-        load_tile<D>(kf[ii], a, s_page, tb, h, max(tile - 2 * NPF2, tb) * KT, false, gtid);
-        lds_barrier();
+        ring_barrier<vmcnt_only((NB - 2) * PERW)>();
         if (it > 0) flush(it - 1);
+        issue2(std::integral_constant<int, (sb + NB - 1) % NB>{}, it + NB - 1);
+        asm volatile("" ::: "memory");
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) pv[e] = 0.f;
@@ -507,7 +658,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
         const int tv = have ? tile_vis(vis, key0) : 0;
         if (tv != 0) {
           f32x4 sv[2];
-          scores<D>(klds[kg][buf], qf, lane, sv);
+          scores_ring<D>(ring(s_c) + kg * 2 * T, qf, lane, sv);
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -536,9 +687,14 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
         const float q1 = keep + lane_xor2(give);
         const float other = lane_xor1(q1);
         const float tot = (j & 1) ? other + q1 : q1 + other;
-        if ((j & 1) == 0) wsum[buf][kg][wr][8 * g + 4 * b3 + 2 * b2 + b1] = tot;
-      }
+        // Opaque index: the write stays visibly inside wsum, so it need not
+        // wait for the ring loads in flight.
+        if ((j & 1) == 0)
+          (&wsum[0][0][0][0])[opaque_index(((buf * 2 + kg) * 4 + wr) * KT + 8 * g + 4 * b3 +
+                                           2 * b2 + b1)] = tot;
+      });
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     lds_barrier();
     if (n2r > 0) flush(n2r - 1);
     return;
