@@ -433,10 +433,13 @@ __device__ __forceinline__ u32x4 vt_operand_ring(const u32x4 *vg, int dm, int la
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
 
-// Bare workgroup barrier after this wave's ring loads up to the awaited tile
-// are done (vmcnt encoding W): every wave's loads of that tile are then in
-// LDS, and every wave has finished with the buffer the next loads refill.
-// The compiler-only fences keep LDS accesses on their side of it.
+// Workgroup barrier after this wave's ring loads up to the awaited tile are
+// done and its LDS accesses have completed (s_waitcnt encoding W): every
+// wave's loads of that tile are then in LDS, every wave has finished with the
+// buffer the next loads refill, and LDS written before the barrier (the mass
+// pass's row-group sums) is visible after it.  The barrier instruction alone
+// orders none of this; the compiler-only fences keep LDS accesses on their
+// side of it.
 template <int W>
 __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_s_waitcnt(W);
@@ -444,7 +447,8 @@ __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
-constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+// s_waitcnt operand: vector memory count <= n, LDS count 0, export count free.
+constexpr int vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
 
 // Tiles a key group holds in LDS at once.  Depth 2 keeps a head-128
 // workgroup's LDS near 71 KB, so two workgroups (16 waves) share a CU; depth 3
@@ -544,7 +548,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
       static_for<0, NB>([&](auto s_c) {
         constexpr int sb = decltype(s_c)::value;
         const int it = it0 + sb;
-        ring_barrier<vmcnt_only((NB - 2) * 2 * PERW)>();
+        ring_barrier<vm_lgkm0((NB - 2) * 2 * PERW)>();
         issue1(std::integral_constant<int, (sb + NB - 1) % NB>{}, it + NB - 1);
         asm volatile("" ::: "memory");
         const int tile = tb + kg + 2 * it;
@@ -647,7 +651,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
         const int tile = te - 1 - kg - 2 * it;
         const bool have = it < n2 && tile >= tb;
         const int buf = it & 1;
-        ring_barrier<vmcnt_only((NB - 2) * PERW)>();
+        ring_barrier<vm_lgkm0((NB - 2) * PERW)>();
         if (it > 0) flush(it - 1);
         issue2(std::integral_constant<int, (sb + NB - 1) % NB>{}, it + NB - 1);
         asm volatile("" ::: "memory");

@@ -377,7 +377,7 @@ def test_second_pass_mass_path(case):
     per unit: the mass comes from a second, last-first pass over K in the same
     workgroup.  Ragged lengths (not multiples of the block size), two row tiles
     in some sequences, two-view sequences; element-wise against the oracle,
-    and bitwise equal on a rerun."""
+    and bitwise equal on eight reruns."""
     import kv_cache_attention_flash_amd as fd
     fd.load()
     g = np.random.default_rng(31 if case.startswith("d64") else 32)
@@ -412,7 +412,8 @@ def test_second_pass_mass_path(case):
     run.step()
     a_out, a_mass = run.out.clone(), run.mass.clone()
     full_check(wl, run=run)
-    o2, m2 = fd.scheduled_attention(run.cache, run.q, run.cu, run.kv_len, wl.max_kv_len,
-                                    run.max_rows, views=run.views, want_mass=True)
-    torch.cuda.synchronize()
-    assert torch.equal(o2, a_out) and torch.equal(m2, a_mass)
+    for rep in range(8):  # the mass pass's row-group sums cross a barrier every tile
+        o2, m2 = fd.scheduled_attention(run.cache, run.q, run.cu, run.kv_len, wl.max_kv_len,
+                                        run.max_rows, views=run.views, want_mass=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, a_out) and torch.equal(m2, a_mass), rep
