@@ -335,15 +335,6 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, int r, int h, bool ok,
 // permutation keeps the transposed reads free of bank conflicts).  Keys at or
 // past the cached length lie outside the buffer view and load as zeros.
 
-// f(integral_constant<int, I>) for I = B .. E-1 (compile-time ring indices).
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F &&f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
@@ -356,14 +347,6 @@ __device__ __forceinline__ int kswz(int key) {
 template <int D>
 __device__ __forceinline__ int vswz(int key) {
   return D == 128 ? (key & 3) << 1 : key & 2;
-}
-
-// An index the optimiser cannot split, so that an LDS read's address stays
-// one step off its ring buffer: the compiler then knows which buffer a read
-// touches and waits only for that buffer's loads.
-__device__ __forceinline__ int opaque_index(int x) {
-  asm("v_mov_b32 %0, %1" : "=v"(x) : "v"(x));
-  return x;
 }
 
 // Loads of one tile (K, and V when asked) into a ring buffer by the 4 waves
@@ -432,23 +415,6 @@ __device__ __forceinline__ u32x4 vt_operand_ring(const u32x4 *vg, int dm, int la
   const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
-
-// Workgroup barrier after this wave's ring loads up to the awaited tile are
-// done and its LDS accesses have completed (s_waitcnt encoding W): every
-// wave's loads of that tile are then in LDS, every wave has finished with the
-// buffer the next loads refill, and LDS written before the barrier (the mass
-// pass's row-group sums) is visible after it.  The barrier instruction alone
-// orders none of this; the compiler-only fences keep LDS accesses on their
-// side of it.
-template <int W>
-__device__ __forceinline__ void ring_barrier() {
-  __builtin_amdgcn_s_waitcnt(W);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-// s_waitcnt operand: vector memory count <= n, LDS count 0, export count free.
-constexpr int vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
 
 // Tiles a key group holds in LDS at once.  Depth 2 keeps a head-128
 // workgroup's LDS near 71 KB, so two workgroups (16 waves) share a CU; depth 3

@@ -1,6 +1,7 @@
 // Device helpers shared by the gfx950 kernels: vector types, MFMA wrappers,
 // bf16 rounding and wave-level reductions.  Wavefronts are 64 lanes wide.
 #pragma once
+#include <type_traits>
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -119,6 +120,45 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void *base, 
 __device__ __forceinline__ u32x4 buffer_ld16(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+
+// Rings of LDS buffers filled by buffer loads that write LDS directly
+// (buffer_load ... lds: lane l of a 16-byte load fills 16 bytes at the
+// wave-uniform LDS address + 16 l).  Each buffer is its own __shared__ object
+// and the rings are unrolled over compile-time buffer indices, so the
+// compiler knows which buffer an LDS read touches and waits only for loads
+// into that one.
+
+// f(integral_constant<int, I>) for I = B .. E-1 (compile-time ring indices).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// An index the optimiser cannot split, so that an LDS read's address stays
+// one step off its buffer (the alias information the waits rely on).
+__device__ __forceinline__ int opaque_index(int x) {
+  asm("v_mov_b32 %0, %1" : "=v"(x) : "v"(x));
+  return x;
+}
+
+// Workgroup barrier once this wave's ring loads up to the awaited buffer are
+// done and its LDS accesses have completed (s_waitcnt encoding W): every
+// wave's loads of that buffer are then in LDS, every wave has finished with
+// the buffer the next loads refill, and LDS written before the barrier is
+// visible after it.  The barrier instruction alone orders none of this; the
+// compiler-only fences keep LDS accesses on their side of it.
+template <int W>
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(W);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// s_waitcnt operand: vector memory count <= n, LDS count 0, export count free.
+constexpr int vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
 
 __device__ __forceinline__ void st16(void *p, const u32x4 &v) {
   *reinterpret_cast<u32x4 *>(p) = v;
