@@ -416,15 +416,11 @@ __device__ __forceinline__ u32x4 vt_operand_ring(const u32x4 *vg, int dm, int la
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
 
-// Tiles a key group holds in LDS at once.  Depth 2 keeps a head-128
-// workgroup's LDS near 71 KB, so two workgroups (16 waves) share a CU; depth 3
-// (one more tile in flight per key group) needs 103 KB and fits one.  Two
-// workgroups at depth 2 stream the cache faster.
-#ifndef FDL_RING_DEPTH
-#define FDL_RING_DEPTH 2
-#endif
-constexpr int kRingDepth = FDL_RING_DEPTH;
-static_assert(kRingDepth == 2 || kRingDepth == 3, "ring depth");
+// Tiles a key group holds in LDS at once.  Two keep a head-128 workgroup's LDS
+// near 71 KB, so two workgroups (16 waves) share a CU; a third (one more tile
+// in flight per key group) needs 103 KB and fits one workgroup per CU, which
+// streams the cache more slowly.
+constexpr int kRingDepth = 2;
 
 // Pass 1.  8 waves: key group kg = wave / 4 takes the unit's even or odd
 // tiles, row group wave % 4 owns 16 query rows; the two key groups keep their
@@ -443,12 +439,12 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
   constexpr int T = KT * D / 8;                // 16-byte slots of a K (or V) tile
   constexpr int PERW = KT * (D / 8) / 64 / 4;  // ring loads per wave per K (or V) tile
   constexpr int NB = kRingDepth;
-  // NB ring buffers of [key group][K tile | V tile] (separate objects, so
+  static_assert(NB == 2, "two ring buffers");
+  // The ring buffers of [key group][K tile | V tile] (separate objects, so
   // that reading one never waits for loads into another); ring0 has room
   // after its tiles for the merge scratch (64 rows x D floats, 64 (m, l)).
   __shared__ u32x4 ring0[4 * T + 32];
   __shared__ u32x4 ring1[4 * T];
-  __shared__ u32x4 ring2[NB > 2 ? 4 * T : 1];
 
   int u = blockIdx.x;
   const int split = u % p.splits; u /= p.splits;
@@ -480,11 +476,10 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a, AttnPlan p) {
   const int page0 = (tb * KT) >> a.c.bs_shift;
   const int tlast = max(te - 1, tb);
   auto ring = [&](auto b_c) -> u32x4 * {
-    constexpr int bi = decltype(b_c)::value;
-    if constexpr (bi == 0) return &ring0[0];
-    else if constexpr (bi == 1) return &ring1[0];
-    else return &ring2[0];
+    if constexpr (decltype(b_c)::value == 0) return &ring0[0];
+    else return &ring1[0];
   };
+
   u32x4 qf[D / 32];
   load_q<D>(a, r, h, row_ok, g, qf);
   asm volatile("" ::: "memory");  // Q's loads ahead of the ring's (in-order load counts)
