@@ -35,7 +35,6 @@ namespace fdl {
 namespace {
 
 constexpr int KT = 32;   // keys per tile
-constexpr int kNpf = 2;  // exchange-mass kernel: tiles in flight per key group
 constexpr float kNegInf = -__builtin_huge_valf();
 
 struct SeqInfo {
@@ -210,15 +209,6 @@ __device__ __forceinline__ Vis row_vis(const SeqInfo &si, int t, bool row_ok) {
   return v;
 }
 
-// One 32-key tile of head h moves global -> registers -> LDS, K and V both
-// row-major ([key][D + pad]), by one group of 256 threads (NCH 16-byte chunks
-// of K and of V per thread).
-template <int D>
-struct Tile {
-  static constexpr int CH = D / 8;                  // 16-byte chunks per key
-  static constexpr int NCH = KT * CH / 256;         // chunks per thread
-  u32x4 k[NCH], v[NCH];
-};
 template <int D> constexpr int kVPad = D + 16;  // V row stride: conflict-free transposed reads
 
 // Slot (in 16-byte chunks) of chunk ch of key row key in a K tile held in LDS.
@@ -247,38 +237,6 @@ __device__ __forceinline__ void stage_pages(const AttnArgs &a, int b, int tb, in
     s_page[i] = a.c.block_table[(size_t)b * a.c.max_blocks + p0 + i];
 }
 
-template <int D>
-__device__ __forceinline__ void load_tile(Tile<D> &t, const AttnArgs &a, const int *s_page, int tb,
-                                          int h, int key0, bool want_v, int gtid) {
-  const int sh = a.c.bs_shift;
-  const int page = s_page[(key0 >> sh) - ((tb * KT) >> sh)];
-  const size_t base = ((((size_t)page * a.c.H + h) << sh) + (key0 & (a.c.bs - 1))) * D;
-#pragma unroll
-  for (int i = 0; i < Tile<D>::NCH; ++i) {
-    const int c = gtid + 256 * i;
-    t.k[i] = ld16(a.c.k + base + (size_t)c * 8);
-    if (want_v) t.v[i] = ld16(a.c.v + base + (size_t)c * 8);
-  }
-}
-
-// V rows at or past the cached length (vkeys valid keys in the tile) are
-// stored as zeros: those slots' contents are unspecified, and a zero weight
-// times a NaN would still poison the product.
-template <int D>
-__device__ __forceinline__ void store_tile(const Tile<D> &t, u32x4 *klds,
-                                           uint16_t (*vlds)[kVPad<D>], bool want_v, int gtid,
-                                           int vkeys = KT) {
-  const bool part = vkeys < KT;
-#pragma unroll
-  for (int i = 0; i < Tile<D>::NCH; ++i) {
-    const int c = gtid + 256 * i;
-    const int key = c / Tile<D>::CH, dc = c % Tile<D>::CH;
-    klds[kslot<D>(key, dc)] = t.k[i];
-    if (want_v)
-      st16(&vlds[key][dc * 8], part && key >= vkeys ? u32x4{0u, 0u, 0u, 0u} : t.v[i]);
-  }
-}
-
 // V^T operand of O^T += V^T P^T for features 16*dm .. 16*dm+15: lane l needs
 // keys 8g .. 8g+7 (g = l / 16) of feature 16*dm + l % 16.  ds_read_tr16_b64
 // gives lane i of a 16-lane group element k = position i % 4 of the 8-byte
@@ -295,25 +253,6 @@ __device__ __forceinline__ u32x4 vt_operand(uint16_t (*vlds)[kVPad<D>], int dm, 
   bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p1));
   const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
-}
-
-// S^T tile (32 keys x 16 rows) for one wave: s[mt][e] is key 8g + 4mt + e for
-// query row (lane & 15).
-template <int D>
-__device__ __forceinline__ void scores(const u32x4 *klds, const u32x4 *qf,
-                                       int lane, f32x4 s[2]) {
-  const int g = lane >> 4, j = lane & 15;
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int key = 8 * (j >> 2) + 4 * mt + (j & 3);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      u32x4 kf = klds[kslot<D>(key, 4 * ks + g)];
-      acc = mfma16(kf, qf[ks], acc);
-    }
-    s[mt] = acc;
-  }
 }
 
 template <int D>
@@ -379,7 +318,8 @@ __device__ __forceinline__ void ring_issue(const AttnArgs &a, const int *s_page,
   }
 }
 
-// S^T tile (32 keys x 16 rows) from a ring K tile (as scores()).
+// S^T tile (32 keys x 16 rows) for one wave from a ring K tile: s[mt][e] is
+// key 8g + 4mt + e for query row (lane & 15).
 template <int D>
 __device__ __forceinline__ void scores_ring(const u32x4 *kg_, const u32x4 *qf, int lane,
                                             f32x4 s[2]) {
@@ -398,7 +338,8 @@ __device__ __forceinline__ void scores_ring(const u32x4 *kg_, const u32x4 *qf, i
   }
 }
 
-// V^T operand from a ring V tile (as vt_operand(), rows permuted by vswz).
+// V^T operand from a ring V tile (as vt_operand() from a padded tile, with
+// the rows' chunks permuted by vswz).
 template <int D>
 __device__ __forceinline__ u32x4 vt_operand_ring(const u32x4 *vg, int dm, int lane) {
   const lds_u32x4 *vb = (const lds_u32x4 *)vg;
@@ -767,7 +708,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, AttnPlan p)
 // the error word is set and the results of the call are invalid.
 constexpr int kXSplitTiles = 32;  // tiles (of KT keys) per split: 1024 keys
 constexpr int kXWaveTiles = kXSplitTiles / 2;
-constexpr int kXRegTiles = 11;    // of a wave's tiles, the scores held in registers
+constexpr int kXRegTiles = 13;    // of a wave's tiles, the scores held in registers
+constexpr int kXRingDepth = 3;    // ring buffers (tiles a key group holds in LDS)
 constexpr int kXLdsTiles = kXWaveTiles - kXRegTiles;
 constexpr int kXSpinLimit = 1 << 16;  // polls: ~0.1 s, far beyond any pass
 constexpr int kXSyncHead = 4;     // ticket, error word, 2 spare; then one count per group
@@ -795,9 +737,15 @@ __global__ __launch_bounds__(256) void attn_xclear_kernel(int *sync, int n) {
 
 template <int D>
 __global__ __launch_bounds__(512) void attn_xmass_kernel(AttnArgs a, AttnPlan p) {
-  constexpr int NPF = kNpf;
-  __shared__ u32x4 klds[2][2][KT * D / 8 + 8];
-  __shared__ uint16_t vlds[2][2][KT][kVPad<D>];
+  constexpr int T = KT * D / 8;                // 16-byte slots of a K (or V) tile
+  constexpr int PERW = KT * (D / 8) / 64 / 4;  // ring loads per wave per K (or V) tile
+  constexpr int NB = kXRingDepth;
+  // NB ring buffers of [key group][K tile | V tile], as in attn_fwd; ring0
+  // then holds the key-group merge and the mass sums.
+  __shared__ u32x4 ring0[4 * T + 32];
+  __shared__ u32x4 ring1[4 * T];
+  __shared__ u32x4 ring2[4 * T];
+  static_assert(NB == 3, "three ring buffers");
   __shared__ float sc_lds[8][kXLdsTiles][8][64];  // [wave][tile][element][lane]
   __shared__ float s_tmax[2][kXWaveTiles][64];     // [key group][tile][row]
   __shared__ int s_page[kXSplitTiles * KT / 32];   // block size >= 32
@@ -828,8 +776,8 @@ __global__ __launch_bounds__(512) void attn_xmass_kernel(AttnArgs a, AttnPlan p)
   const int Sb = max(1, (tiles + kXSplitTiles - 1) / kXSplitTiles);
   if (t0 >= si.nrows || split >= Sb) return;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int kg = wave >> 2, wr = wave & 3, gtid = threadIdx.x & 255;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kg = wave >> 2, wr = wave & 3;
   const int g = lane >> 4, j = lane & 15;
   const int t = t0 + wr * 16 + j;  // local row of this lane
   const bool row_ok = t < si.nrows;
@@ -854,55 +802,70 @@ __global__ __launch_bounds__(512) void attn_xmass_kernel(AttnArgs a, AttnPlan p)
   // maximum (kept in s_tmax)
   float sc[kXRegTiles][8];
 
-  // The same uniform ring as attn_fwd, unrolled over the wave's tiles so that
-  // every probability lands in a fixed register (or LDS slot).  An empty
-  // cache (no tile, no staged page) issues no load at all.
+  // The LDS ring of attn_fwd (NB buffers per key group, loads of an empty view
+  // past the key group's last tile), unrolled over the wave's tiles so that
+  // every probability lands in a fixed register (or LDS slot) and every ring
+  // buffer index is a constant.  An empty cache (no tile, no staged page)
+  // issues no load at all.
+  const int page0 = (tb * KT) >> a.c.bs_shift;
+  auto ring = [&](auto b_c) -> u32x4 * {
+    if constexpr (decltype(b_c)::value == 0) return &ring0[0];
+    else if constexpr (decltype(b_c)::value == 1) return &ring1[0];
+    else return &ring2[0];
+  };
+  auto issue = [&](auto b_c, int it) {
+    u32x4 *rb = ring(b_c) + kg * 2 * T;
+    const bool live = tb + kg + 2 * it < te;
+    const int tile = live ? tb + kg + 2 * it : tlast;
+    ring_issue<D>(a, s_page, page0, h, tile * KT, live ? si.L : 0, rb, rb + T, true, wr, lane);
+  };
   if (te > tb) {
-  Tile<D> pf[NPF];
+    asm volatile("" ::: "memory");  // Q's loads ahead of the ring's
+    static_for<0, NB - 1>([&](auto b_c) { issue(b_c, decltype(b_c)::value); });
+    static_for<0, kXWaveTiles>([&](auto it_c) {
+      constexpr int it = decltype(it_c)::value;
+      const int tile = tb + kg + 2 * it;
+      const bool have = it < niter && tile < te;
+      ring_barrier<vm_lgkm0((NB - 2) * 2 * PERW)>();
+      issue(std::integral_constant<int, (it + NB - 1) % NB>{}, it + NB - 1);
+      asm volatile("" ::: "memory");
+      const u32x4 *rb = ring(std::integral_constant<int, it % NB>{}) + kg * 2 * T;
+      const int key0 = tile * KT;
+      const int tv = have ? tile_vis(vis, key0) : 0;
+      float pv[8], mt = 0.f;
+      if (tv != 0) {
+        f32x4 sv[2];
+        scores_ring<D>(rb, qf, lane, sv);
+        const u32x4 pb =
+            tile_softmax_pv<D / 16>(sv, vis, tv, key0, g, a.scale_log2, m, l, o, pv, mt);
 #pragma unroll
-  for (int i = 0; i < NPF; ++i)
-    load_tile<D>(pf[i], a, s_page, tb, h, min(tb + kg + 2 * i, tlast) * KT, true, gtid);
+        for (int dm = 0; dm < D / 16; ++dm)
+          o[dm] = mfma16(vt_operand_ring<D>(rb + T, dm, lane), pb, o[dm]);
+      } else {
 #pragma unroll
-  for (int it = 0; it < kXWaveTiles; ++it) {
-    const int ii = it % NPF;
-    const int tile = tb + kg + 2 * it;
-    const bool have = it < niter && tile < te;
-    const int buf = it & 1;
-    store_tile<D>(pf[ii], klds[kg][buf], vlds[kg][buf], true, gtid, si.L - tile * KT);
-    load_tile<D>(pf[ii], a, s_page, tb, h, min(tile + 2 * NPF, tlast) * KT, true, gtid);
-    lds_barrier();
-    const int key0 = tile * KT;
-    const int tv = have ? tile_vis(vis, key0) : 0;
-    float pv[8], mt = 0.f;
-    if (tv != 0) {
-      f32x4 sv[2];
-      scores<D>(klds[kg][buf], qf, lane, sv);
-      const u32x4 pb = tile_softmax_pv<D / 16>(sv, vis, tv, key0, g, a.scale_log2, m, l, o, pv, mt);
+        for (int e = 0; e < 8; ++e) pv[e] = 0.f;
+      }
+      if (g == 0) s_tmax[kg][it][rl] = mt;
+      if constexpr (it < kXRegTiles) {
 #pragma unroll
-      for (int dm = 0; dm < D / 16; ++dm)
-        o[dm] = mfma16(vt_operand<D>(vlds[kg][buf], dm, lane), pb, o[dm]);
-    } else {
+        for (int e = 0; e < 8; ++e) sc[it][e] = pv[e];
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = 0.f;
-    }
-    if (g == 0) s_tmax[kg][it][rl] = mt;
-    if (it < kXRegTiles) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sc[it < kXRegTiles ? it : 0][e] = pv[e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sc_lds[wave][it - kXRegTiles][e][lane] = pv[e];
-    }
+        for (int e = 0; e < 8; ++e) sc_lds[wave][it - kXRegTiles][e][lane] = pv[e];
+      }
+    });
   }
-  }
+  // Ring loads past the last tile still write LDS: complete before ring0
+  // holds the merge.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // Combine the two key groups: group 1's state through LDS (reusing the
   // tiles), the maxima and normalisers first so that they can be published
   // before the outputs are merged.
   lds_barrier();
-  float *mo = reinterpret_cast<float *>(&klds[0][0][0]);  // [64 rows][D]
-  float *mml = mo + 64 * D;                                   // [64 rows][2]
-  static_assert((64 * D + 128) * 4 <= (int)sizeof(klds), "merge scratch");
+  float *mo = reinterpret_cast<float *>(&ring0[0]);  // [64 rows][D]
+  float *mml = mo + 64 * D;                            // [64 rows][2]
+  static_assert((64 * D + 128) * 4 <= (int)sizeof(ring0), "merge scratch");
   if (kg == 1) {
 #pragma unroll
     for (int dm = 0; dm < D / 16; ++dm)
@@ -1009,8 +972,8 @@ __global__ __launch_bounds__(512) void attn_xmass_kernel(AttnArgs a, AttnPlan p)
   // Mass of the wave's keys over its 16 rows: each probability rescaled by
   // its tile's factor exp2(mt - LSE), a reduce-scatter over the row lanes,
   // then the 4 row groups added in order through LDS.
-  float *wsum = reinterpret_cast<float *>(&klds[0][0][0]);  // [4 row groups][kXSplitTiles * KT]
-  static_assert(4 * kXSplitTiles * KT * 4 <= (int)sizeof(klds), "mass scratch");
+  float *wsum = reinterpret_cast<float *>(&ring0[0]);  // [4 row groups][kXSplitTiles * KT]
+  static_assert(4 * kXSplitTiles * KT * 4 <= (int)sizeof(ring0), "mass scratch");
   const int b3 = (j >> 3) & 1, b2 = (j >> 2) & 1, b1 = (j >> 1) & 1;
 #pragma unroll
   for (int it = 0; it < kXWaveTiles; ++it) {
