@@ -124,3 +124,52 @@ def test_random_long_cache(seed):
           f"lengths {wl.kv_len.tolist()}, topb {wl.topb}, views {wl.views is not None}",
           flush=True)
     full_check(wl)
+
+
+REREAD_CASES = 6
+
+
+def random_reread_workload(seed):
+    """Enough sequences x heads for one workgroup per (sequence, row tile,
+    head) unit (>= 256) and caches past 1024 keys: attention takes the split
+    path whose workgroups read K a second time for the mass.  Block sizes 32
+    to 256, both head sizes, ragged lengths (some on a tile boundary), one or
+    two row tiles per sequence, some two-view sequences."""
+    g = np.random.default_rng(7000 + seed)
+    dim = int(g.choice([64, 128]))
+    heads = int(g.choice([16, 32]))
+    batch = 256 // heads + int(g.integers(0, 3))
+    bs = int(g.choice([32, 64, 128, 256]))
+    specs = []
+    for _ in range(batch):
+        length = int(g.choice([1056, 2048])) if g.random() < 0.25 else int(g.integers(1030, 2300))
+        if g.random() < 0.25:
+            w = int(g.integers(1, 33))
+            ctx = length - w
+            w0 = int(g.integers(0, ctx - w + 1))
+            specs.append(synth.SeqSpec(kv_len=length, window=(w0, w), tracked=(), draft_start=ctx))
+        else:
+            w = int(g.integers(1, 49))
+            w0 = int(g.integers(0, length - w + 1))
+            pool = [p for p in range(length) if not (w0 <= p < w0 + w)]
+            nt = int(g.integers(0, 41))
+            tr = tuple(sorted(int(p) for p in g.choice(pool, size=nt, replace=False))) if nt else ()
+            specs.append(synth.SeqSpec(kv_len=length, window=(w0, w), tracked=tr))
+    topb = int(g.choice([8, 16, 32]))
+    return synth.build(f"random_reread_{seed}", 300 + seed, 256, heads, dim, bs, 1.0e4, specs,
+                       topb=topb)
+
+
+@pytest.mark.parametrize("seed", range(REREAD_CASES))
+def test_random_second_pass_mass(seed):
+    import kv_cache_attention_flash_amd as fd
+    fd.load()
+    wl = random_reread_workload(seed)
+    path = fd.attention_path(wl.batch, wl.rows, wl.num_heads, wl.head_dim, wl.max_kv_len,
+                             int(np.diff(wl.cu_rows).max()), wl.max_kv_len)
+    print(f"[random-reread] seed {seed}: rows {wl.rows}, batch {wl.batch}, "
+          f"{wl.num_heads}x{wl.head_dim}, block {wl.block_size}, "
+          f"lengths {wl.kv_len.min()}..{wl.kv_len.max()}, topb {wl.topb}, path {path}",
+          flush=True)
+    assert path == "split_mass_reread"
+    full_check(wl)
