@@ -265,14 +265,15 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, int r, int h, bool ok,
 }
 
 // ---------------------------------------------------------------------------
-// LDS ring of the forward kernel.  A tile's K and V go from global memory
-// straight into LDS by buffer loads that write LDS (`buffer_load ... lds`):
-// no registers, no LDS store instructions.  Lane l of a load fills 16-byte
-// slot 64·piece + l of the tile, so the permuted layouts are made on the
-// source side: K slot s holds chunk (s % CH) ^ kswz(key) of key s / CH (the
-// kslot layout), V slot s chunk (s % CH) ^ vswz(key) (rows unpadded; the
-// permutation keeps the transposed reads free of bank conflicts).  Keys at or
-// past the cached length lie outside the buffer view and load as zeros.
+// LDS ring of the split-path kernels (attn_fwd, attn_xmass).  A tile's K and
+// V go from global memory straight into LDS by buffer loads that write LDS
+// (`buffer_load ... lds`): no registers, no LDS store instructions.  Lane l
+// of a load fills 16-byte slot 64·piece + l of the tile, so the permuted
+// layouts are made on the source side: K slot s holds chunk (s % CH) ^
+// kswz(key) of key s / CH (the kslot layout), V slot s chunk (s % CH) ^
+// vswz(key) (rows unpadded; the permutation keeps the transposed reads free
+// of bank conflicts).  Keys at or past the cached length lie outside the
+// buffer view and load as zeros.
 
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
@@ -321,9 +322,9 @@ __device__ __forceinline__ void ring_issue(const AttnArgs &a, const int *s_page,
 // S^T tile (32 keys x 16 rows) for one wave from a ring K tile: s[mt][e] is
 // key 8g + 4mt + e for query row (lane & 15).
 template <int D>
-__device__ __forceinline__ void scores_ring(const u32x4 *kg_, const u32x4 *qf, int lane,
+__device__ __forceinline__ void scores_ring(const u32x4 *ktile, const u32x4 *qf, int lane,
                                             f32x4 s[2]) {
-  const lds_u32x4 *kb = (const lds_u32x4 *)kg_;
+  const lds_u32x4 *kb = (const lds_u32x4 *)ktile;
   const int g = lane >> 4, j = lane & 15;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
@@ -341,8 +342,8 @@ __device__ __forceinline__ void scores_ring(const u32x4 *kg_, const u32x4 *qf, i
 // V^T operand from a ring V tile (as vt_operand() from a padded tile, with
 // the rows' chunks permuted by vswz).
 template <int D>
-__device__ __forceinline__ u32x4 vt_operand_ring(const u32x4 *vg, int dm, int lane) {
-  const lds_u32x4 *vb = (const lds_u32x4 *)vg;
+__device__ __forceinline__ u32x4 vt_operand_ring(const u32x4 *vtile, int dm, int lane) {
+  const lds_u32x4 *vb = (const lds_u32x4 *)vtile;
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
   const lds_u16 *v16 = reinterpret_cast<const lds_u16 *>(vb);
