@@ -182,6 +182,32 @@ def test_exchange_path_reruns_and_workspace(name):
     full_check(wl, run=run)
 
 
+@pytest.mark.parametrize("name", ["llada8b_ragged_b32", "llada8b_verify_b8"])
+def test_split_attention_reruns_bitwise(name):
+    """Both split-path attention kernels at full layer size (batch 32: one
+    1024-key split per unit, scores on chip; two-view batch 8: the forward
+    kernel): eight calls on the same inputs give the same bits."""
+    import kv_cache_attention_flash_amd as fd
+    fd.load()
+    wl = synth.WORKLOADS[name]()
+    run = G.GpuRun(wl, "cuda:0")
+    mass = name == "llada8b_ragged_b32"
+    path = fd.attention_path(wl.batch, wl.rows, wl.num_heads, wl.head_dim, wl.max_kv_len,
+                             run.max_rows, wl.max_kv_len if mass else 0)
+    _banner(f"split attention reruns {name}: path {path}")
+    q, _ = fd.flash_cache_step(run.cache, run.x, run.w, run.cu, run.pos, run.slots, wl.rope_base)
+    ref = None
+    for rep in range(8):
+        res = fd.scheduled_attention(run.cache, q, run.cu, run.kv_len, wl.max_kv_len, run.max_rows,
+                                     views=run.views, want_mass=mass)
+        torch.cuda.synchronize()
+        res = tuple(t.clone() for t in res if t is not None)
+        if ref is None:
+            ref = res
+        else:
+            assert all(torch.equal(x, y) for x, y in zip(res, ref)), rep
+
+
 def test_block_permutation_invariance():
     _banner("block-table permutation invariance")
     wl = synth.small_ragged()
