@@ -736,290 +736,408 @@ __global__ __launch_bounds__(256) void attn_xclear_kernel(int *sync, int n) {
     if (i != 1) sync[i] = 0;  // the error word stays as it is
 }
 
-template <int D>
+template <int D, bool LOOP>
 __global__ __launch_bounds__(512) void attn_xmass_kernel(AttnArgs a, AttnPlan p) {
   constexpr int T = KT * D / 8;                // 16-byte slots of a K (or V) tile
   constexpr int PERW = KT * (D / 8) / 64 / 4;  // ring loads per wave per K (or V) tile
   constexpr int NB = kXRingDepth;
-  // NB ring buffers of [key group][K tile | V tile], as in attn_fwd; ring0
-  // then holds the key-group merge and the mass sums.
+  // NB ring buffers of [key group][K tile | V tile], as in attn_fwd.  Tile
+  // iteration it of a key group uses buffer (it + 1) % NB, so that ring0 is
+  // free after a unit's pass: it then holds the key-group merge and the mass
+  // sums while ring1 and ring2 take the next unit's first tiles.
   __shared__ u32x4 ring0[4 * T + 32];
   __shared__ u32x4 ring1[4 * T];
   __shared__ u32x4 ring2[4 * T];
   static_assert(NB == 3, "three ring buffers");
   __shared__ float sc_lds[8][kXLdsTiles][8][64];  // [wave][tile][element][lane]
   __shared__ float s_tmax[2][kXWaveTiles][64];     // [key group][tile][row]
-  __shared__ int s_page[kXSplitTiles * KT / 32];   // block size >= 32
+  constexpr int kSplitPages = kXSplitTiles * KT / 32;  // block size >= 32
+  __shared__ int s_page[kSplitPages];
   __shared__ float s_lse[64];
   __shared__ int s_unit;
-
-  int *sync = reinterpret_cast<int *>(a.ws + p.off_sync);
-  if (p.splits > 1) {
-    if (threadIdx.x == 0)
-      s_unit = __hip_atomic_fetch_add(sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-  } else if (threadIdx.x == 0) {
-    s_unit = blockIdx.x;  // no waits: the launch order is enough
-  }
-  __syncthreads();
-  int u = s_unit;
-  const int S = p.splits;
-  const int split = u % S;
-  const int grp = u / S;  // (sequence, row tile, head)
-  u = grp;
-  const int h = u % a.c.H;
-  u /= a.c.H;
-  const int rt = u % p.row_tiles;
-  const int b = u / p.row_tiles;
-  const SeqInfo si = seq_info(a, b);
-  const int t0 = rt * 64;
-  const int tiles = (si.L + KT - 1) / KT;
-  const int Sb = max(1, (tiles + kXSplitTiles - 1) / kXSplitTiles);
-  if (t0 >= si.nrows || split >= Sb) return;
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kg = wave >> 2, wr = wave & 3;
   const int g = lane >> 4, j = lane & 15;
-  const int t = t0 + wr * 16 + j;  // local row of this lane
-  const bool row_ok = t < si.nrows;
-  const int r = si.r0 + (row_ok ? t : 0);
-  const int rl = wr * 16 + j;      // row of the lane inside the tile
-  const Vis vis = row_vis(si, t, row_ok);
-
-  const int tb = split * kXSplitTiles, te = min(tiles, tb + kXSplitTiles);
-  const int niter = (te - tb + 1) / 2;  // iterations per key group
-
-  stage_pages(a, b, tb, te, s_page);
-  lds_barrier();
-  const int tlast = max(te - 1, tb);
-  u32x4 qf[D / 32];
-  load_q<D>(a, r, h, row_ok, g, qf);
-
-  f32x4 o[D / 16];
-#pragma unroll
-  for (int dm = 0; dm < D / 16; ++dm) o[dm] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = kNegInf, l = 0.f;
-  // fp32 probabilities of the wave's tiles, each against its tile's running
-  // maximum (kept in s_tmax)
-  float sc[kXRegTiles][8];
-
-  // The LDS ring of attn_fwd (NB buffers per key group, loads of an empty view
-  // past the key group's last tile), unrolled over the wave's tiles so that
-  // every probability lands in a fixed register (or LDS slot) and every ring
-  // buffer index is a constant.  An empty cache (no tile, no staged page)
-  // issues no load at all.
-  const int page0 = (tb * KT) >> a.c.bs_shift;
+  const int rl = wr * 16 + j;  // row of the lane inside the tile
+  const int S = p.splits;
+  int *sync = reinterpret_cast<int *>(a.ws + p.off_sync);
   auto ring = [&](auto b_c) -> u32x4 * {
     if constexpr (decltype(b_c)::value == 0) return &ring0[0];
     else if constexpr (decltype(b_c)::value == 1) return &ring1[0];
     else return &ring2[0];
   };
-  auto issue = [&](auto b_c, int it) {
-    u32x4 *rb = ring(b_c) + kg * 2 * T;
-    const bool live = tb + kg + 2 * it < te;
-    const int tile = live ? tb + kg + 2 * it : tlast;
-    ring_issue<D>(a, s_page, page0, h, tile * KT, live ? si.L : 0, rb, rb + T, true, wr, lane);
+
+  // LOOP (every cache fits one split: no unit waits for another): a grid of
+  // at most one workgroup per CU walks the units u = blockIdx.x, + gridDim.x,
+  // ..., skipping empty row tiles, and starts each next unit's pages, Q and
+  // first two tiles while it finishes the current one.  Otherwise one unit
+  // per workgroup, taken from the ticket counter when the splits exchange.
+  const int units = a.batch * p.row_tiles * a.c.H * S;
+  // LOOP: the units in order of decreasing cache length (sequences ranked in
+  // LDS, ties by index; a batch above kXRankMax keeps index order), dealt to
+  // the workgroups in snake order (round k: workgroup w takes position
+  // k G + w for even k, k G + G - 1 - w for odd k), so that every workgroup's
+  // total is close to the mean.
+  constexpr int kXRankMax = 128;
+  __shared__ int s_order[kXRankMax];
+  const bool ranked = LOOP && a.batch <= kXRankMax;
+  if (ranked) {
+    if ((int)threadIdx.x < a.batch) {
+      const int L = min(a.kv_len[threadIdx.x], a.max_kv_len);
+      int rank = 0;
+      for (int i = 0; i < a.batch; ++i) {
+        const int Li = min(a.kv_len[i], a.max_kv_len);
+        rank += (Li > L || (Li == L && i < (int)threadIdx.x)) ? 1 : 0;
+      }
+      s_order[rank] = threadIdx.x;
+    }
+    __syncthreads();
+  }
+  const int per_seq = p.row_tiles * a.c.H;  // units of a sequence (LOOP: one split)
+  auto unit_at = [&](int k) -> int {        // k-th position of this workgroup, or units
+    const int G = gridDim.x;
+    const int pos = k * G + ((k & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    if (pos >= units) return units;
+    const int rb = pos / per_seq;
+    return (ranked ? s_order[rb] : rb) * per_seq + pos % per_seq;
   };
-  if (te > tb) {
-    asm volatile("" ::: "memory");  // Q's loads ahead of the ring's
-    static_for<0, NB - 1>([&](auto b_c) { issue(b_c, decltype(b_c)::value); });
-    static_for<0, kXWaveTiles>([&](auto it_c) {
-      constexpr int it = decltype(it_c)::value;
-      const int tile = tb + kg + 2 * it;
-      const bool have = it < niter && tile < te;
-      ring_barrier<vm_lgkm0((NB - 2) * 2 * PERW)>();
-      issue(std::integral_constant<int, (it + NB - 1) % NB>{}, it + NB - 1);
-      asm volatile("" ::: "memory");
-      const u32x4 *rb = ring(std::integral_constant<int, it % NB>{}) + kg * 2 * T;
-      const int key0 = tile * KT;
-      const int tv = have ? tile_vis(vis, key0) : 0;
-      float pv[8], mt = 0.f;
-      if (tv != 0) {
-        f32x4 sv[2];
-        scores_ring<D>(rb, qf, lane, sv);
-        const u32x4 pb =
-            tile_softmax_pv<D / 16>(sv, vis, tv, key0, g, a.scale_log2, m, l, o, pv, mt);
+  auto live_k = [&](int k) -> int {  // first position at or after k whose row tile has rows
+    for (;; ++k) {
+      const int v = unit_at(k);
+      if (v >= units) return k;
+      const int b = v / per_seq, rt = v / a.c.H % p.row_tiles;
+      if (rt * 64 < a.cu_rows[b + 1] - a.cu_rows[b]) return k;
+    }
+  };
+  int u, kpos = 0;
+  if constexpr (LOOP) {
+    // (unit numbers in scalar registers: the per-unit loads are then scalar
+    // loads, which do not wait behind the next unit's tiles in flight)
+    kpos = __builtin_amdgcn_readfirstlane(live_k(0));
+    u = __builtin_amdgcn_readfirstlane(unit_at(kpos));
+  } else {
+    if (S > 1) {
+      if (threadIdx.x == 0)
+        s_unit = __hip_atomic_fetch_add(sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+    } else if (threadIdx.x == 0) {
+      s_unit = blockIdx.x;  // no waits: the launch order is enough
+    }
+    __syncthreads();
+    u = s_unit;
+  }
+  bool pref = false;  // this unit's pages, Q and first two tiles are on their way
+  u32x4 qf[D / 32];
+  int next_page = 0;  // LOOP: this thread's block-table entry of the next unit
+  // LOOP: the next unit's sequence, read before its tiles were issued (a
+  // vector load at the loop top would wait behind those tiles)
+  SeqInfo nsi{};
+
+  while (!LOOP || u < units) {
+    const int split = u % S;
+    const int grp = u / S;  // (sequence, row tile, head)
+    const int h = grp % a.c.H;
+    const int rt = grp / a.c.H % p.row_tiles;
+    const int b = grp / a.c.H / p.row_tiles;
+    const SeqInfo si = pref ? nsi : seq_info(a, b);
+    const int t0 = rt * 64;
+    const int tiles = (si.L + KT - 1) / KT;
+    const int Sb = max(1, (tiles + kXSplitTiles - 1) / kXSplitTiles);
+    if (!LOOP && (t0 >= si.nrows || split >= Sb)) return;
+
+    const int t = t0 + wr * 16 + j;  // local row of this lane
+    const bool row_ok = t < si.nrows;
+    const int r = si.r0 + (row_ok ? t : 0);
+    const Vis vis = row_vis(si, t, row_ok);
+
+    const int tb = split * kXSplitTiles, te = min(tiles, tb + kXSplitTiles);
+    const int niter = (te - tb + 1) / 2;  // iterations per key group
+    const int tlast = max(te - 1, tb);
+    const int page0 = (tb * KT) >> a.c.bs_shift;
+    auto issue = [&](auto b_c, int it) {
+      u32x4 *rb = ring(b_c) + kg * 2 * T;
+      const bool live = tb + kg + 2 * it < te;
+      const int tile = live ? tb + kg + 2 * it : tlast;
+      ring_issue<D>(a, s_page, page0, h, tile * KT, live ? si.L : 0, rb, rb + T, true, wr, lane);
+    };
+    if (!pref) {
+      stage_pages(a, b, tb, te, s_page);
+      lds_barrier();
+      load_q<D>(a, r, h, row_ok, g, qf);
+      if (te > tb) {
+        asm volatile("" ::: "memory");  // Q's loads ahead of the ring's
+        static_for<0, NB - 1>([&](auto c_) {
+          issue(std::integral_constant<int, decltype(c_)::value + 1>{}, decltype(c_)::value);
+        });
+      }
+    }
+
+    f32x4 o[D / 16];
+#pragma unroll
+    for (int dm = 0; dm < D / 16; ++dm) o[dm] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = kNegInf, l = 0.f;
+    // fp32 probabilities of the wave's tiles, each against its tile's running
+    // maximum (kept in s_tmax)
+    float sc[kXRegTiles][8];
+
+    // The wave's tiles, unrolled so that every probability lands in a fixed
+    // register (or LDS slot) and every ring buffer index is a constant.  An
+    // empty cache (no tile, no staged page) issues no load at all.
+    if (te > tb) {
+      static_for<0, kXWaveTiles>([&](auto it_c) {
+        constexpr int it = decltype(it_c)::value;
+        // Past the split's last iteration (the same for the whole workgroup)
+        // there is nothing to wait for or compute; the loads already issued
+        // for those iterations are drained after the loop.
+        if (it >= niter) return;
+        const int tile = tb + kg + 2 * it;
+        const bool have = tile < te;
+        ring_barrier<vm_lgkm0((NB - 2) * 2 * PERW)>();
+        issue(std::integral_constant<int, (it + NB) % NB>{}, it + NB - 1);
+        asm volatile("" ::: "memory");
+        const u32x4 *rb = ring(std::integral_constant<int, (it + 1) % NB>{}) + kg * 2 * T;
+        const int key0 = tile * KT;
+        const int tv = have ? tile_vis(vis, key0) : 0;
+        float pv[8], mt = 0.f;
+        if (tv != 0) {
+          f32x4 sv[2];
+          scores_ring<D>(rb, qf, lane, sv);
+          const u32x4 pb =
+              tile_softmax_pv<D / 16>(sv, vis, tv, key0, g, a.scale_log2, m, l, o, pv, mt);
+#pragma unroll
+          for (int dm = 0; dm < D / 16; ++dm)
+            o[dm] = mfma16(vt_operand_ring<D>(rb + T, dm, lane), pb, o[dm]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[e] = 0.f;
+        }
+        if (g == 0) s_tmax[kg][it][rl] = mt;
+        if constexpr (it < kXRegTiles) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sc[it][e] = pv[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sc_lds[wave][it - kXRegTiles][e][lane] = pv[e];
+        }
+      });
+    }
+    // Ring loads past the last tile still write LDS: complete before ring0
+    // holds the merge (and before ring1 / ring2 take the next unit's tiles).
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+
+    // LOOP: the next unit, and its block-table entries on their way (written
+    // to s_page once this unit's outputs are out; the pass no longer reads it).
+    int nu = units, nb_ = 0, nh = 0, nrt = 0;
+    int nte = 0;
+    if constexpr (LOOP) {
+      kpos = __builtin_amdgcn_readfirstlane(live_k(kpos + 1));
+      nu = __builtin_amdgcn_readfirstlane(unit_at(kpos));
+      if (nu < units) {
+        nh = nu / S % a.c.H;
+        nrt = nu / S / a.c.H % p.row_tiles;
+        nb_ = nu / S / a.c.H / p.row_tiles;
+        nsi = seq_info(a, nb_);
+        nte = min((nsi.L + KT - 1) / KT, kXSplitTiles);
+        const int np = nte > 0 ? ((nte * KT - 1) >> a.c.bs_shift) + 1 : 0;
+        if ((int)threadIdx.x < np)
+          next_page = a.c.block_table[(size_t)nb_ * a.c.max_blocks + threadIdx.x];
+      }
+    }
+
+    // Combine the two key groups: group 1's state through LDS (reusing the
+    // tiles), the maxima and normalisers first so that they can be published
+    // before the outputs are merged.
+    lds_barrier();
+    float *mo = reinterpret_cast<float *>(&ring0[0]);  // [64 rows][D]
+    float *mml = mo + 64 * D;                            // [64 rows][2]
+    static_assert((64 * D + 128) * 4 <= (int)sizeof(ring0), "merge scratch");
+    if (kg == 1) {
+#pragma unroll
+      for (int dm = 0; dm < D / 16; ++dm)
+        *reinterpret_cast<f32x4 *>(&mo[rl * D + 16 * dm + 4 * g]) = o[dm];
+      if (g == 0) {
+        mml[2 * rl] = m;
+        mml[2 * rl + 1] = l;
+      }
+    }
+    lds_barrier();
+    float f0 = 0.f, f1 = 0.f;
+    if (kg == 0) {
+      const float m1 = mml[2 * rl], l1 = mml[2 * rl + 1];
+      const float mx = fmaxf(m, m1);
+      f0 = m == kNegInf ? 0.f : exp2f(m - mx);
+      f1 = m1 == kNegInf ? 0.f : exp2f(m1 - mx);
+      l = l * f0 + l1 * f1;
+      m = mx;
+    }
+    float *po = reinterpret_cast<float *>(a.ws + p.off_part_o);
+    float *pml = reinterpret_cast<float *>(a.ws + p.off_part_ml);
+    const size_t stride = (size_t)a.rows * a.c.H;
+    const size_t rh0 = (size_t)r * a.c.H + h;
+    int *count = sync + kXSyncHead + grp;
+    if (!LOOP && Sb > 1) {
+      // Publish this split's (m, l) with device-coherent stores, complete them,
+      // then count the split in.
+      if (kg == 0 && row_ok && g == 0) {
+        store_agent(&pml[2 * (split * stride + rh0)], m);
+        store_agent(&pml[2 * (split * stride + rh0) + 1], l);
+      }
+      wait_mem();
+      __syncthreads();
+      if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(count, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // The outputs, while the other splits arrive: the final (normalised) rows
+    // when the cache fits one split, else this split's unnormalised partial.
+    if (kg == 0 && row_ok) {
+#pragma unroll
+      for (int dm = 0; dm < D / 16; ++dm)
+        o[dm] = o[dm] * f0 + *reinterpret_cast<const f32x4 *>(&mo[rl * D + 16 * dm + 4 * g]) * f1;
+      if (Sb == 1) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        float *dst = a.out + rh0 * D + 4 * g;
 #pragma unroll
         for (int dm = 0; dm < D / 16; ++dm)
-          o[dm] = mfma16(vt_operand_ring<D>(rb + T, dm, lane), pb, o[dm]);
+          *reinterpret_cast<f32x4 *>(dst + 16 * dm) = o[dm] * inv;
       } else {
+        float *dst = po + (split * stride + rh0) * D + 4 * g;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = 0.f;
+        for (int dm = 0; dm < D / 16; ++dm) *reinterpret_cast<f32x4 *>(dst + 16 * dm) = o[dm];
       }
-      if (g == 0) s_tmax[kg][it][rl] = mt;
-      if constexpr (it < kXRegTiles) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sc[it][e] = pv[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sc_lds[wave][it - kXRegTiles][e][lane] = pv[e];
-      }
-    });
-  }
-  // Ring loads past the last tile still write LDS: complete before ring0
-  // holds the merge.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
 
-  // Combine the two key groups: group 1's state through LDS (reusing the
-  // tiles), the maxima and normalisers first so that they can be published
-  // before the outputs are merged.
-  lds_barrier();
-  float *mo = reinterpret_cast<float *>(&ring0[0]);  // [64 rows][D]
-  float *mml = mo + 64 * D;                            // [64 rows][2]
-  static_assert((64 * D + 128) * 4 <= (int)sizeof(ring0), "merge scratch");
-  if (kg == 1) {
-#pragma unroll
-    for (int dm = 0; dm < D / 16; ++dm)
-      *reinterpret_cast<f32x4 *>(&mo[rl * D + 16 * dm + 4 * g]) = o[dm];
-    if (g == 0) {
-      mml[2 * rl] = m;
-      mml[2 * rl + 1] = l;
-    }
-  }
-  lds_barrier();
-  float f0 = 0.f, f1 = 0.f;
-  if (kg == 0) {
-    const float m1 = mml[2 * rl], l1 = mml[2 * rl + 1];
-    const float mx = fmaxf(m, m1);
-    f0 = m == kNegInf ? 0.f : exp2f(m - mx);
-    f1 = m1 == kNegInf ? 0.f : exp2f(m1 - mx);
-    l = l * f0 + l1 * f1;
-    m = mx;
-  }
-  float *po = reinterpret_cast<float *>(a.ws + p.off_part_o);
-  float *pml = reinterpret_cast<float *>(a.ws + p.off_part_ml);
-  const size_t stride = (size_t)a.rows * a.c.H;
-  const size_t rh0 = (size_t)r * a.c.H + h;
-  int *count = sync + kXSyncHead + grp;
-  if (Sb > 1) {
-    // Publish this split's (m, l) with device-coherent stores, complete them,
-    // then count the split in.
-    if (kg == 0 && row_ok && g == 0) {
-      store_agent(&pml[2 * (split * stride + rh0)], m);
-      store_agent(&pml[2 * (split * stride + rh0) + 1], l);
-    }
-    wait_mem();
-    __syncthreads();
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_add(count, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  // The outputs, while the other splits arrive: the final (normalised) rows
-  // when the cache fits one split, else this split's unnormalised partial.
-  if (kg == 0 && row_ok) {
-#pragma unroll
-    for (int dm = 0; dm < D / 16; ++dm)
-      o[dm] = o[dm] * f0 + *reinterpret_cast<const f32x4 *>(&mo[rl * D + 16 * dm + 4 * g]) * f1;
-    if (Sb == 1) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      float *dst = a.out + rh0 * D + 4 * g;
-#pragma unroll
-      for (int dm = 0; dm < D / 16; ++dm) *reinterpret_cast<f32x4 *>(dst + 16 * dm) = o[dm] * inv;
+    // The row's log-sum-exp over the whole cache.
+    float lse = kNegInf;
+    if (LOOP || Sb == 1) {
+      if (kg == 0 && row_ok) lse = l > 0.f ? m + log2f(l) : kNegInf;
     } else {
-      float *dst = po + (split * stride + rh0) * D + 4 * g;
+      if (threadIdx.x == 0) {
+        int spins = 0;
+        while (__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < Sb) {
+          if (++spins > kXSpinLimit) {
+            __hip_atomic_store(sync + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      __syncthreads();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (kg == 0 && row_ok) {
+        // Eight splits' pairs at a time, all loads in flight together; the
+        // chunks are combined in split order.
+        float mx = kNegInf, lsum = 0.f;
+        for (int s0 = 0; s0 < Sb; s0 += 8) {
+          float mv[8], lv[8];
 #pragma unroll
-      for (int dm = 0; dm < D / 16; ++dm) *reinterpret_cast<f32x4 *>(dst + 16 * dm) = o[dm];
+          for (int i = 0; i < 8; ++i) {
+            const size_t k = (size_t)min(s0 + i, Sb - 1) * stride + rh0;
+            mv[i] = load_agent(&pml[2 * k]);
+            lv[i] = load_agent(&pml[2 * k + 1]);
+          }
+          float cm = kNegInf;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) cm = s0 + i < Sb ? fmaxf(cm, mv[i]) : cm;
+          const float nm = fmaxf(mx, cm);
+          if (nm != kNegInf) {
+            float cs = mx == kNegInf ? 0.f : lsum * exp2f(mx - nm);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              cs += (s0 + i < Sb && mv[i] != kNegInf) ? lv[i] * exp2f(mv[i] - nm) : 0.f;
+            lsum = cs;
+          }
+          mx = nm;
+        }
+        lse = lsum > 0.f ? mx + log2f(lsum) : kNegInf;
+      }
     }
-  }
+    if (kg == 0 && g == 0) s_lse[rl] = lse;
+    if constexpr (LOOP) {
+      if (nu < units && (int)threadIdx.x < kSplitPages) s_page[threadIdx.x] = next_page;
+    }
+    lds_barrier();
+    const float lr = s_lse[rl];
 
-  // The row's log-sum-exp over the whole cache.
-  float lse = kNegInf;
-  if (Sb == 1) {
-    if (kg == 0 && row_ok) lse = l > 0.f ? m + log2f(l) : kNegInf;
-  } else {
-    if (threadIdx.x == 0) {
-      int spins = 0;
-      while (__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < Sb) {
-        if (++spins > kXSpinLimit) {
-          __hip_atomic_store(sync + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
+    if constexpr (LOOP) {
+      // The next unit's Q and first two tiles (into ring1 and ring2) go out
+      // now and arrive while this unit's mass is formed.
+      if (nu < units) {
+        const int nt = nrt * 64 + wr * 16 + j;
+        const bool nrow_ok = nt < nsi.nrows;
+        load_q<D>(a, nsi.r0 + (nrow_ok ? nt : 0), nh, nrow_ok, g, qf);
+        if (nte > 0) {
+          asm volatile("" ::: "memory");
+          const int ntlast = nte - 1;
+          static_for<0, NB - 1>([&](auto c_) {
+            constexpr int it = decltype(c_)::value;
+            u32x4 *rb = ring(std::integral_constant<int, it + 1>{}) + kg * 2 * T;
+            const bool live = kg + 2 * it < nte;
+            const int tile = live ? kg + 2 * it : ntlast;
+            ring_issue<D>(a, s_page, 0, nh, tile * KT, live ? nsi.L : 0, rb, rb + T, true, wr,
+                          lane);
+          });
         }
-        __builtin_amdgcn_s_sleep(2);
       }
     }
-    __syncthreads();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (kg == 0 && row_ok) {
-      // Eight splits' pairs at a time, all loads in flight together; the
-      // chunks are combined in split order.
-      float mx = kNegInf, lsum = 0.f;
-      for (int s0 = 0; s0 < Sb; s0 += 8) {
-        float mv[8], lv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const size_t k = (size_t)min(s0 + i, Sb - 1) * stride + rh0;
-          mv[i] = load_agent(&pml[2 * k]);
-          lv[i] = load_agent(&pml[2 * k + 1]);
-        }
-        float cm = kNegInf;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) cm = s0 + i < Sb ? fmaxf(cm, mv[i]) : cm;
-        const float nm = fmaxf(mx, cm);
-        if (nm != kNegInf) {
-          float cs = mx == kNegInf ? 0.f : lsum * exp2f(mx - nm);
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            cs += (s0 + i < Sb && mv[i] != kNegInf) ? lv[i] * exp2f(mv[i] - nm) : 0.f;
-          lsum = cs;
-        }
-        mx = nm;
-      }
-      lse = lsum > 0.f ? mx + log2f(lsum) : kNegInf;
-    }
-  }
-  if (kg == 0 && g == 0) s_lse[rl] = lse;
-  lds_barrier();
-  const float lr = s_lse[rl];
 
-  // Mass of the wave's keys over its 16 rows: each probability rescaled by
-  // its tile's factor exp2(mt - LSE), a reduce-scatter over the row lanes,
-  // then the 4 row groups added in order through LDS.
-  float *wsum = reinterpret_cast<float *>(&ring0[0]);  // [4 row groups][kXSplitTiles * KT]
-  static_assert(4 * kXSplitTiles * KT * 4 <= (int)sizeof(ring0), "mass scratch");
-  const int b3 = (j >> 3) & 1, b2 = (j >> 2) & 1, b1 = (j >> 1) & 1;
+    // Mass of the wave's keys over its 16 rows: each probability rescaled by
+    // its tile's factor exp2(mt - LSE), a reduce-scatter over the row lanes,
+    // then the 4 row groups added in order through LDS.
+    float *wsum = reinterpret_cast<float *>(&ring0[0]);  // [4 row groups][kXSplitTiles * KT]
+    static_assert(4 * kXSplitTiles * KT * 4 <= (int)sizeof(ring0), "mass scratch");
+    const int b3 = (j >> 3) & 1, b2 = (j >> 2) & 1, b1 = (j >> 1) & 1;
 #pragma unroll
-  for (int it = 0; it < kXWaveTiles; ++it) {
-    const int tile = tb + kg + 2 * it;
-    if (it < niter && tile < te) {
-      const float f = lr == kNegInf ? 0.f : fast_exp2(s_tmax[kg][it][rl] - lr);
-      float pv[8];
+    for (int it = 0; it < kXWaveTiles; ++it) {
+      const int tile = tb + kg + 2 * it;
+      if (it < niter && tile < te) {
+        const float f = lr == kNegInf ? 0.f : fast_exp2(s_tmax[kg][it][rl] - lr);
+        float pv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = it < kXRegTiles ? sc[it < kXRegTiles ? it : 0][e]
-                                        : sc_lds[wave][it < kXRegTiles ? 0 : it - kXRegTiles][e][lane];
-        pv[e] = x * f;
+        for (int e = 0; e < 8; ++e) {
+          const float x = it < kXRegTiles
+                              ? sc[it < kXRegTiles ? it : 0][e]
+                              : sc_lds[wave][it < kXRegTiles ? 0 : it - kXRegTiles][e][lane];
+          pv[e] = x * f;
+        }
+        float q4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float give = b3 ? pv[i] : pv[i + 4];
+          const float keep = b3 ? pv[i + 4] : pv[i];
+          q4[i] = keep + lane_xor8(give);
+        }
+        float q2[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const float give = b2 ? q4[i] : q4[i + 2];
+          const float keep = b2 ? q4[i + 2] : q4[i];
+          q2[i] = keep + lane_xor4(give);
+        }
+        const float give = b1 ? q2[0] : q2[1];
+        const float keep = b1 ? q2[1] : q2[0];
+        const float q1 = keep + lane_xor2(give);
+        const float other = lane_xor1(q1);
+        const float tot = (j & 1) ? other + q1 : q1 + other;
+        if ((j & 1) == 0)
+          wsum[wr * (kXSplitTiles * KT) + (tile - tb) * KT + 8 * g + 4 * b3 + 2 * b2 + b1] = tot;
       }
-      float q4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float give = b3 ? pv[i] : pv[i + 4];
-        const float keep = b3 ? pv[i + 4] : pv[i];
-        q4[i] = keep + lane_xor8(give);
-      }
-      float q2[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const float give = b2 ? q4[i] : q4[i + 2];
-        const float keep = b2 ? q4[i + 2] : q4[i];
-        q2[i] = keep + lane_xor4(give);
-      }
-      const float give = b1 ? q2[0] : q2[1];
-      const float keep = b1 ? q2[1] : q2[0];
-      const float q1 = keep + lane_xor2(give);
-      const float other = lane_xor1(q1);
-      const float tot = (j & 1) ? other + q1 : q1 + other;
-      if ((j & 1) == 0)
-        wsum[wr * (kXSplitTiles * KT) + (tile - tb) * KT + 8 * g + 4 * b3 + 2 * b2 + b1] = tot;
     }
-  }
-  lds_barrier();
-  float *mp = reinterpret_cast<float *>(a.ws + p.off_mass_part) +
-              (((size_t)b * a.c.H + h) * p.row_tiles + rt) * a.mass_stride;
-  const int nk = (te - tb) * KT;
-  for (int k = threadIdx.x; k < nk; k += blockDim.x) {
-    const int jj = tb * KT + k;
-    constexpr int W = kXSplitTiles * KT;
-    const float v = ((wsum[k] + wsum[W + k]) + wsum[2 * W + k]) + wsum[3 * W + k];
-    if (jj < si.L) mp[jj] = v;
+    // The LDS sums complete and visible; no wait for the next unit's tiles in
+    // flight (a fence would wait for those loads into LDS too).
+    ring_barrier<vm_lgkm0(63)>();
+    float *mp = reinterpret_cast<float *>(a.ws + p.off_mass_part) +
+                (((size_t)b * a.c.H + h) * p.row_tiles + rt) * a.mass_stride;
+    const int nk = (te - tb) * KT;
+    for (int k = threadIdx.x; k < nk; k += blockDim.x) {
+      const int jj = tb * KT + k;
+      constexpr int W = kXSplitTiles * KT;
+      const float v = ((wsum[k] + wsum[W + k]) + wsum[2 * W + k]) + wsum[3 * W + k];
+      if (jj < si.L) mp[jj] = v;
+    }
+    if constexpr (!LOOP) return;
+    u = nu;
+    pref = true;
   }
 }
 
@@ -1523,7 +1641,11 @@ hipError_t launch_xmass(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int units = a.batch * p.row_tiles * a.c.H * p.splits;
-  hipLaunchKernelGGL(attn_xmass_kernel<D>, dim3(units), dim3(512), 0, s, a, p);
+  if (p.splits == 1)  // no unit waits for another: at most one workgroup per CU, looping
+    hipLaunchKernelGGL((attn_xmass_kernel<D, true>), dim3(std::min(units, device_cus())),
+                       dim3(512), 0, s, a, p);
+  else
+    hipLaunchKernelGGL((attn_xmass_kernel<D, false>), dim3(units), dim3(512), 0, s, a, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nb_mass = a.batch * ((a.mass_stride + 255) / 256);

@@ -702,14 +702,7 @@ __global__ __launch_bounds__(256) void scatter_kv_kernel(FlashCacheArgs a, const
 
 }  // namespace
 
-// Tile shape of the split-K projection: kSplitNTW 16-feature tiles per wave,
-// kSplitNGW wave groups across features, kSplitNST register stages,
-// kSplitWaves waves, kSplitKC reduction elements per staged chunk; at most
-// kSplitCap workgroups before the reduction is split.
-namespace {
-constexpr int kSplitNTW = 3, kSplitNGW = 1, kSplitNST = 2, kSplitWaves = 8, kSplitKC = 256;
-constexpr int kSplitCap = 320;
-
+#ifndef FDL_DEVICE_ONLY
 // Compute units of the current device (cached per device; 256 if the query
 // fails, the part's count).
 int device_cus() {
@@ -725,6 +718,15 @@ int device_cus() {
   }
   return cus[dev];
 }
+#endif
+
+// Tile shape of the split-K projection: kSplitNTW 16-feature tiles per wave,
+// kSplitNGW wave groups across features, kSplitNST register stages,
+// kSplitWaves waves, kSplitKC reduction elements per staged chunk; at most
+// kSplitCap workgroups before the reduction is split.
+namespace {
+constexpr int kSplitNTW = 3, kSplitNGW = 1, kSplitNST = 2, kSplitWaves = 8, kSplitKC = 256;
+constexpr int kSplitCap = 320;
 constexpr int kSplitCW = 16 * kSplitNTW * kSplitNGW;  // features per column group
 
 struct FcPlan {

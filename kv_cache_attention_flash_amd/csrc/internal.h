@@ -61,6 +61,9 @@ struct AttnArgs {
 
 hipError_t launch_attention(const AttnArgs &a, const AttnPlan &p, hipStream_t s);
 
+// Compute units of the current device (cached per device).
+int device_cus();
+
 // Single-launch step (fused.hip): the projection then row-group attention with
 // the mass, for shapes whose separate calls take a one-launch projection (no
 // split reduction) and the row-group attention path.  sync: 5 ints of device

@@ -182,6 +182,42 @@ def test_exchange_path_reruns_and_workspace(name):
     full_check(wl, run=run)
 
 
+def test_scores_on_chip_loop_with_empty_row_tiles():
+    """Caches up to 1024 keys with the mass and more units than CUs: the
+    scores-on-chip kernel loops over units per workgroup, dealt longest cache
+    first.  Some sequences have two row tiles and some one, so the second row
+    tile of the short ones is an empty unit that the loop skips; one sequence
+    has a 40-key cache and one a cache on a tile boundary.  Element-wise
+    against the oracle, and bitwise equal on a rerun."""
+    import kv_cache_attention_flash_amd as fd
+    fd.load()
+    g = np.random.default_rng(41)
+    specs = []
+    for i in range(10):
+        L = [40, 1024][i] if i < 2 else int(g.integers(300, 1025))
+        w = int(min(L, 48 if i % 3 == 0 else 16))
+        w0 = int(g.integers(0, L - w + 1))
+        pool = [q for q in range(L) if not (w0 <= q < w0 + w)]
+        nt = int(min(len(pool), 40 if i % 3 == 0 else 8))
+        tr = tuple(sorted(int(q) for q in g.choice(pool, size=nt, replace=False))) if nt else ()
+        specs.append(SeqSpec(kv_len=L, window=(w0, w), tracked=tr))
+    wl = synth.build("xmass_loop", 29, 256, 32, 128, 32, 5.0e5, specs, topb=16)
+    run = G.GpuRun(wl, "cuda:0")
+    rows = np.diff(wl.cu_rows)
+    path = fd.attention_path(wl.batch, wl.rows, wl.num_heads, wl.head_dim, wl.max_kv_len,
+                             run.max_rows, wl.max_kv_len)
+    _banner(f"scores-on-chip loop: rows per sequence {rows.tolist()}, "
+            f"lengths {wl.kv_len.tolist()}, path {path}")
+    assert path == "split_mass_exchange" and rows.max() > 64 and rows.min() <= 64
+    run.step()
+    o1, m1 = run.out.clone(), run.mass.clone()
+    full_check(wl, run=run)
+    o2, m2 = fd.scheduled_attention(run.cache, run.q, run.cu, run.kv_len, wl.max_kv_len,
+                                    run.max_rows, want_mass=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o1) and torch.equal(m2, m1)
+
+
 @pytest.mark.parametrize("name", ["llada8b_ragged_b32", "llada8b_verify_b8"])
 def test_split_attention_reruns_bitwise(name):
     """Both split-path attention kernels at full layer size (batch 32: one
