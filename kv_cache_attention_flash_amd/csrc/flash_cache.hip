@@ -509,9 +509,21 @@ __device__ __forceinline__ void qkv_gemm_body(const FlashCacheArgs &a, int nrow_
   const int total_pairs = 3 * H * half;
   const int hidden = a.hidden;
   const int nb = nrow_tiles * ncol_tiles;
-  int idx = bid;
-  if (nb % 8 == 0) idx = (bid % 8) * (nb / 8) + bid / 8;
-  const int ct = idx / nrow_tiles, rtile = idx % nrow_tiles;
+  // Workgroup bid runs on XCD bid % 8 (workgroups are dealt to the XCDs
+  // round-robin).  Each XCD owns a contiguous slice of the column tiles, so
+  // its share of W is fetched once, and walks it row tile by row tile: the
+  // column tiles that read one X row tile run side by side and share it
+  // through that XCD's L2.
+  int ct = bid / nrow_tiles, rtile = bid % nrow_tiles;
+  if (nb % 8 == 0 && ncol_tiles % 8 == 0) {
+    const int cpx = ncol_tiles / 8, l = bid / 8;
+    ct = (bid % 8) * cpx + l % cpx;
+    rtile = l / cpx;
+  } else if (nb % 8 == 0) {
+    const int idx = (bid % 8) * (nb / 8) + bid / 8;
+    ct = idx / nrow_tiles;
+    rtile = idx % nrow_tiles;
+  }
   const int row0 = rtile * BM, pair0 = ct * BP;
 
   const int act = active_rows(a);
