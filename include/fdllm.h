@@ -280,8 +280,8 @@ int verify_accept(const int32_t *draft_tok, const int32_t *mask_tok,
  *   workspace  fdl_fused_step_workspace_bytes(...) bytes (the same workspace
  *              also serves flash_cache_attention_step_single_launch); contents
  *              need no initialisation.  The attention's workspace starts at
- *              byte 256, so its error word (see scheduled_attention) is the
- *              int32 at byte 260. */
+ *              byte 4096, so its error word (see scheduled_attention) is the
+ *              int32 at byte 4100. */
 int flash_cache_attention_step(const fdl_kv_cache *cache, const void *x, int32_t hidden,
                                const void *w_qkv, int32_t batch, int32_t num_rows,
                                const int32_t *cu_rows, const int32_t *positions,
@@ -297,26 +297,36 @@ int flash_cache_attention_step(const fdl_kv_cache *cache, const void *x, int32_t
  * flash_cache_step followed by scheduled_attention with the mass, as one
  * persistent launch (an alternative form of flash_cache_attention_step, kept
  * for comparison: on this part it is slower than the back-to-back kernels).
- * Arguments as for flash_cache_attention_step.  Results are bitwise those of
- * the two separate calls: each phase runs the same workgroup code.
- * Workgroups take items from a ticket counter in phase order (projection,
- * attention, mass); an attention item starts once every projection item has
- * finished, a mass item once every attention item has.  An item only waits
- * for items with lower tickets, held by running workgroups, so the ordinary
- * launch needs no co-residency guarantee.  Hand-offs between workgroups use
- * device-scope release/acquire on counters in the workspace.
- *   workspace  fdl_fused_step_workspace_bytes(...) bytes.  Its first 256
- *              bytes hold the counters, the ticket and an error word: they
+ * Arguments as for flash_cache_attention_step.
+ * Items are dealt to the XCDs by head (XCD x owns heads x, x + 8, ...): each
+ * XCD's queue holds the projection items of its heads' Q, K and V features,
+ * then the row-group attention items of those heads.  A workgroup takes items
+ * from the queue of the XCD it runs on (read from the hardware), so a head's
+ * projection hands Q and the written K/V to its attention through that XCD's
+ * L2: a per-head count, no L2 write-back.  An attention item starts once its
+ * own head is projected; the mass items (a sum over every head) start after
+ * each XCD has written its L2 back once.  An item only waits for items with
+ * lower tickets, held by running workgroups, so the ordinary launch needs no
+ * co-residency guarantee.  Results agree with the two separate calls' (each
+ * item runs their workgroup code): bitwise with the tiled projection (more
+ * than 64 rows); with the split-K projection the column groups are formed per
+ * XCD, so Q, K and V may differ in the last bit (another order of the fp32
+ * sums).  Every call gives bitwise the same results as the last.
+ *   workspace  fdl_fused_step_workspace_bytes(...) bytes.  Its first 4096
+ *              bytes hold the counters, the tickets and an error word: they
  *              must be zero before the first call (for example a zero-filled
  *              allocation, made in stream order before the call); each call
  *              leaves the counters zero.  The error word (int32 at byte 12)
- *              becomes 1 if a phase wait ever timed out (it never should: every
+ *              becomes 1 if a wait ever timed out (it never should: every
  *              wait is for a running workgroup); results are then invalid,
  *              and the word stays set until the caller clears it.  Calls
  *              sharing a workspace must not run at the same time.
  * Supported: the shapes whose separate calls take a one-launch projection (no
  * split reduction) and the row-group attention path (few sequences x heads,
- * caches up to 1024 keys); otherwise FDL_EUNSUPPORTED and nothing launched. */
+ * caches up to 1024 keys), with at most 1004 heads; otherwise
+ * FDL_EUNSUPPORTED and nothing launched.  The part is taken to have 8 XCDs
+ * (XCC_ID 0..7); a device with fewer runs no item of the missing XCDs' queues,
+ * and the mass wait then times out and sets the error word. */
 int flash_cache_attention_step_single_launch(
     const fdl_kv_cache *cache, const void *x, int32_t hidden, const void *w_qkv, int32_t batch,
     int32_t num_rows, const int32_t *cu_rows, const int32_t *positions, const int32_t *slots,

@@ -738,8 +738,8 @@ _FUSED_WS = {}
 def _fused_workspace(device, stream_handle: int, nbytes: int):
     """Zero-filled workspace per (device, stream), allocated and filled in the
     stream's order (so the fill is done before the call's kernel starts): its
-    first 256 bytes are the single-launch step's counters, which every call
-    leaves at zero."""
+    first FUSED_SYNC_BYTES bytes are the single-launch step's counters, which
+    every call leaves at zero."""
     key = (device.index if device.index is not None else torch.cuda.current_device(), stream_handle)
     ws = _FUSED_WS.get(key)
     if ws is None or ws.numel() < nbytes:
@@ -750,6 +750,7 @@ def _fused_workspace(device, stream_handle: int, nbytes: int):
 
 
 FUSED_ERROR_OFFSET = 12  # byte offset of the single-launch step's error word
+FUSED_SYNC_BYTES = 4096  # the one-call steps' leading counter bytes (attention workspace after)
 
 
 def fused_step_error(workspace: torch.Tensor, stream=None) -> int:
@@ -837,8 +838,10 @@ def flash_cache_attention_step_single_launch(cache: PagedKVCache, x, w_qkv, cu_r
                                              mass_stride=None, q_out=None, slot_mapping_out=None,
                                              out=None, mass=None, workspace=None, stream=None,
                                              check=True):
-    """The same step as one persistent launch (bitwise the same results;
-    row-group shapes only).  ``workspace``, if given, must be zero-filled
+    """The same step as one persistent launch, items dealt to the XCDs by
+    head (row-group shapes only; the results agree with the two calls', up to
+    the order of the split-K projection's fp32 sums, and every call repeats
+    the last bitwise).  ``workspace``, if given, must be zero-filled
     before its first use, in the launch stream's order.  With ``check`` the
     call waits for its stream and raises if the kernel reported a timed-out
     wait.  Returns (q_out, slot_mapping, out, mass)."""

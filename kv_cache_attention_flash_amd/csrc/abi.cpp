@@ -265,7 +265,7 @@ int attn_args(const fdl_kv_cache *cache, const void *q, int32_t batch, int32_t n
   return FDL_OK;
 }
 
-constexpr size_t kFusedSyncBytes = 256;  // counters, ticket and error word, padded
+using fdl::kFusedSyncBytes;
 
 }  // namespace
 

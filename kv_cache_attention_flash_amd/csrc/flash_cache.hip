@@ -155,6 +155,16 @@ __device__ __forceinline__ void row_meta(const FlashCacheArgs &a, int r, bool wr
 // reduction inside this kernel would need device-scope release/acquire fences,
 // which on a multi-XCD part write back and invalidate the L2 that the weight
 // stream is using.)
+// Maps a projection item's pair index to the rotary pair it computes.  The
+// separate kernels use the identity (and deal their items to the XCDs
+// themselves); the single-launch step, which assigns items to XCDs by head,
+// passes its own map (an index past the last pair marks a pair that does not
+// exist).
+struct PairIdentity {
+  static constexpr bool kIdentity = true;
+  __device__ int operator()(int p) const { return p; }
+};
+
 struct SplitPlan {
   int G, S, ks;     // column groups, splits, reduction elements per split
   float *partials;  // [G][S][64][CW]
@@ -171,9 +181,10 @@ struct SplitLds {
 
 // The workgroup body (item bid of the grid; LDS from the caller, so a fused
 // kernel can share one buffer across phases).
-template <int NTW, int NGW, int NST, int NCH, int NW, int KC>
+template <int NTW, int NGW, int NST, int NCH, int NW, int KC, class PM = PairIdentity>
 __device__ __forceinline__ void qkv_splitk_body(const FlashCacheArgs &a, const SplitPlan &sp,
-                                                int bid, SplitLds<NTW, NGW, KC> &L) {
+                                                int bid, SplitLds<NTW, NGW, KC> &L,
+                                                PM pmap = PM{}) {
   constexpr int NKQ = NW / NGW;
   constexpr int CW = 16 * NTW * NGW;
   constexpr int PW = CW / 2;
@@ -199,9 +210,12 @@ __device__ __forceinline__ void qkv_splitk_body(const FlashCacheArgs &a, const S
   // (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
   const int nb = sp.G * sp.S;
   int idx = bid;
-  if (nb % 8 == 0) idx = (bid % 8) * (nb / 8) + bid / 8;
+  if (PM::kIdentity && nb % 8 == 0) idx = (bid % 8) * (nb / 8) + bid / 8;
   const int grp = idx / sp.S, split = idx % sp.S;
   const int pair0 = grp * PW;
+  // A mapped group whose first pair does not exist has none to compute.
+  if constexpr (!PM::kIdentity)
+    if (pmap(pair0) >= total_pairs) return;
   const int k_begin = split * sp.ks;
 
   // Row metadata for the epilogue (S == 1), in three steps.  Every wave
@@ -250,7 +264,7 @@ __device__ __forceinline__ void qkv_splitk_body(const FlashCacheArgs &a, const S
       src[i] = a.x + (size_t)r * hidden + k_begin + piece * 8;
     } else {
       const int c = tr - ROWS;  // column in the group: tile c/16, lane col c%16
-      int p = pair0 + 8 * (c / 16) + (c & 7);
+      int p = pmap(pair0 + 8 * (c / 16) + (c & 7));
       p = p < total_pairs ? p : total_pairs - 1;
       const int lh = D == 128 ? 6 : 5;  // log2(D / 2): D is 64 or 128
       const int feat = (p >> lh) * D + (p & (half - 1)) + ((c & 8) ? half : 0);
@@ -313,7 +327,7 @@ __device__ __forceinline__ void qkv_splitk_body(const FlashCacheArgs &a, const S
 #pragma unroll
     for (int k = 0; k < NIT; ++k) {
       const int item = tid + NW * 64 * k;
-      const int rl = max(0, min(item / PW, act - 1)), p = pair0 + item % PW;
+      const int rl = max(0, min(item / PW, act - 1)), p = pmap(pair0 + item % PW);
       rope_cs(s_pos[rl], s_freq[p % half], ec[k], es[k]);
       edst[k] = pair_dst(a, rl, min(p, total_pairs - 1), s_blk[rl], s_off[rl]);
       if (item / PW < act && p < total_pairs) eflags |= 1u << k;
@@ -414,7 +428,7 @@ __device__ __forceinline__ void qkv_splitk_body(const FlashCacheArgs &a, const S
     const int clo = 16 * (pl >> 3) + (pl & 7);
     const float lo = ysum(rl * YS + clo), hi = ysum(rl * YS + clo + 8);
     if (a.y_out)
-      store_raw_pair(a, rl, pair0 + pl, lo, hi);
+      store_raw_pair(a, rl, pmap(pair0 + pl), lo, hi);
     else
       store_word(edst[k], half, rotate_round_cs(lo, hi, eflags >> (NIT + k) & 1u, ec[k], es[k]));
   }
@@ -488,9 +502,10 @@ struct GemmLds {
   int s_pos[BM];
 };
 
-template <int BM, int NWN, int NREG, int BK = 32>
+template <int BM, int NWN, int NREG, int BK = 32, class PM = PairIdentity>
 __device__ __forceinline__ void qkv_gemm_body(const FlashCacheArgs &a, int nrow_tiles,
-                                              int ncol_tiles, int bid, GemmLds<BM, NWN, BK> &L) {
+                                              int ncol_tiles, int bid, GemmLds<BM, NWN, BK> &L,
+                                              PM pmap = PM{}) {
   constexpr int NT = 128 * NWN;                        // threads
   constexpr int BP = 32 * NWN;                         // pairs per tile
   constexpr int BN = 2 * BP;                           // output features per tile
@@ -515,11 +530,11 @@ __device__ __forceinline__ void qkv_gemm_body(const FlashCacheArgs &a, int nrow_
   // column tiles that read one X row tile run side by side and share it
   // through that XCD's L2.
   int ct = bid / nrow_tiles, rtile = bid % nrow_tiles;
-  if (nb % 8 == 0 && ncol_tiles % 8 == 0) {
+  if (PM::kIdentity && nb % 8 == 0 && ncol_tiles % 8 == 0) {
     const int cpx = ncol_tiles / 8, l = bid / 8;
     ct = (bid % 8) * cpx + l % cpx;
     rtile = l / cpx;
-  } else if (nb % 8 == 0) {
+  } else if (PM::kIdentity && nb % 8 == 0) {
     const int idx = (bid % 8) * (nb / 8) + bid / 8;
     ct = idx / nrow_tiles;
     rtile = idx % nrow_tiles;
@@ -549,7 +564,7 @@ __device__ __forceinline__ void qkv_gemm_body(const FlashCacheArgs &a, int nrow_
       src[i] = a.x + (size_t)r * hidden + piece * 8;
     } else {
       const int c = tr - BM;  // 0..BN-1: first elements, then partners
-      int p = pair0 + (c % BP);
+      int p = pmap(pair0 + (c % BP));
       p = p < total_pairs ? p : total_pairs - 1;
       const int feat = (p / half) * D + (p % half) + (c >= BP ? half : 0);
       src[i] = a.w + (size_t)feat * hidden + piece * 8;
@@ -622,7 +637,7 @@ __device__ __forceinline__ void qkv_gemm_body(const FlashCacheArgs &a, int nrow_
   // Epilogue: lane holds pair pair0 + 32 wn + l32 for 16 rows per M tile.
   // The pair's section, head and destination column are formed once; each
   // row then adds its own offset (Q row, or cache slot from s_kvo).
-  const int p = pair0 + 32 * wn + l32;
+  const int p = pmap(pair0 + 32 * wn + l32);
   if (p >= total_pairs) return;
   if (a.y_out) {  // unfused ablation: the raw fp32 pairs
 #pragma unroll

@@ -68,6 +68,9 @@ int device_cus();
 // the mass, for shapes whose separate calls take a one-launch projection (no
 // split reduction) and the row-group attention path.  sync: 5 ints of device
 // memory, zero before the first call (each call leaves them zero).
+// Leading bytes of the one-call steps' workspace: the single launch's
+// counters (tickets, per-XCD and per-head counts) and its error word (byte 12).
+constexpr size_t kFusedSyncBytes = 4096;
 bool fused_step_supported(const FlashCacheArgs &fa, const AttnPlan &ap, bool mass);
 hipError_t launch_fused_step(const FlashCacheArgs &fa, const AttnArgs &aa, const AttnPlan &ap,
                              int *sync, hipStream_t s);
