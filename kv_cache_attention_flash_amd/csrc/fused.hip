@@ -108,6 +108,12 @@ __device__ __forceinline__ void stores_done() {
   __syncthreads();
 }
 
+// Consumer side: the invalidate completes (it counts as a vector memory
+// operation) before the barrier that lets the workgroup's loads go.
+__device__ __forceinline__ void invalidate_l1() {
+  asm volatile("buffer_inv sc0\n\ts_waitcnt vmcnt(0)" ::: "memory");
+}
+
 __device__ __forceinline__ bool poll_until(int *counter, int target, int *error) {
   int spins = 0;
   while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
@@ -180,7 +186,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_step_kernel(FlashCacheArg
         poll_until(sync + kHeadReady0 + h, xq.head_items(j) * xq.nru, error);
         // Q and the written K/V are in this XCD's L2; drop any copy in the
         // CU's L1 before reading them.
-        asm volatile("buffer_inv sc0" ::: "memory");
+        invalidate_l1();
       }
       __syncthreads();
       attn_rows_body<D, MAXT, true>(aa, ap, (b * xq.H + h) * xq.rgroups + rg, 1, lds.rows);
@@ -216,6 +222,9 @@ __global__ __launch_bounds__(kFusedThreads) void fused_step_kernel(FlashCacheArg
       if (threadIdx.x == 0) {
         poll_until(sync + kXcdsDone, xcds_att, error);
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // the invalidate done before the barrier
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
       }
       __syncthreads();
       waited = true;
