@@ -119,6 +119,8 @@ typedef struct fdl_two_view {
  *   slot_mapping_out  device int64 [num_rows] physical slot of each row, or NULL.
  *   workspace  device scratch of fdl_flash_cache_workspace_bytes(...) bytes
  *              (no initialisation needed); NULL when that is 0.
+ * x, w_qkv, q_out and both cache pools must be 16-byte aligned (they are read
+ * and written in 16-byte pieces); otherwise FDL_EINVAL, nothing launched.
  * num_rows == 0 or batch == 0 is a no-op.  Output bits do not depend on the
  * order in which workgroups finish: partial sums are added in a fixed order. */
 int flash_cache_step(const fdl_kv_cache *cache, const void *x, int32_t hidden,

@@ -177,6 +177,11 @@ int fc_args(const fdl_kv_cache *cache, const void *x, int32_t hidden, const void
     return FDL_OK;
   }
   if (!x || !w_qkv || !cu_rows || !positions || !slots || !q_out) return FDL_EINVAL;
+  // the projection reads X and W and writes Q and the pools in 16-byte pieces
+  auto misaligned = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
+  if (misaligned(x) || misaligned(w_qkv) || misaligned(q_out) || misaligned(cache->k_cache) ||
+      misaligned(cache->v_cache))
+    return FDL_EINVAL;
   a.c = view_of(cache);
   a.x = static_cast<const uint16_t *>(x);
   a.w = static_cast<const uint16_t *>(w_qkv);

@@ -69,6 +69,14 @@ def test_flash_cache_step_validation(lib):
     assert args(_cache(bt=0)) == _lib.FDL_EINVAL
     assert args(_cache(k=0)) == _lib.FDL_EINVAL
     assert args(_cache(), rows=-1) == _lib.FDL_EINVAL
+    # X, W, Q and the pools are read and written in 16-byte pieces
+    for at in range(3):
+        ptrs = [fake, fake, fake]
+        ptrs[at] = fake + 8
+        assert lib.flash_cache_step(ctypes.byref(_cache()), ptrs[0], 256, ptrs[1], 1, 4, fake,
+                                    fake, fake, 1e4, ptrs[2], None, fake, ws,
+                                    None) == _lib.FDL_EINVAL
+    assert args(_cache(k=fake + 2)) == _lib.FDL_EINVAL
     # empty calls are no-ops and touch nothing
     assert args(_cache(), rows=0) == _lib.FDL_OK
     assert args(_cache(), batch=0) == _lib.FDL_OK
