@@ -318,7 +318,7 @@ def test_topb_crafted_masses():
             rng.random(4096, dtype=np.float32),
             np.zeros(4096, np.float32)]
     lens = [7, 4096, 3000, 10]
-    # stride 4096 (the 1024-thread workgroup) and 2000 (the 256-thread one)
+    # stride 4096 (the 1024-thread workgroup) and 2000 (the 512-thread one)
     for width in (4096, 2000):
         mass = torch.from_numpy(np.ascontiguousarray(np.stack(rows)[:, :width])).to(dev)
         wl = [min(L, width) for L in lens]
@@ -352,7 +352,7 @@ def test_topb_uncached_rows_and_low_digits():
         for i, L in enumerate(lens):
             want = O.top_b(rows[i].astype(np.float64), L, b_)
             assert np.array_equal(got[i], want), (b_, i)
-    # the same rows cut to 2048 keys (the 256-thread workgroup, LDS-cached)
+    # the same rows cut to 2048 keys (the 512-thread workgroup, LDS-cached)
     mass2 = torch.from_numpy(np.ascontiguousarray(np.stack(rows)[:, :2048])).to(dev)
     kv2 = G.i32([2048, 2047, 2048, 1500], dev)
     for b_ in (32, 150):
